@@ -1,0 +1,175 @@
+"""CPU oracle for the heterogeneous-adapter LoRA delta -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never calls it and has
+no fallback to it.  It shares no code with ``adapter_gemv_amd``; the two meet
+only at the seeded inputs from ``workloads`` and at the comparison.
+
+The arithmetic lives in ``lora_oracle.c`` (plain C, fp64, one thread); this
+module builds it with gcc and marshals numpy arrays through ctypes.  The
+pages' analytic byte and FLOP accounting lives in ``oracle.costmodel``.
+
+Functions and the passages they follow:
+
+* ``build_segments`` -- group rows by adapter ("6. Deep Dive A: Batching
+  Heterogeneous Adapters" on "m07 -- Multi-Adapter (LoRA) Serving": an index
+  vector maps each sequence to an adapter slot; "One weight read, many
+  adapters" on "LoRA, quotas and noisy neighbours": tag each row with its
+  adapter and group).
+* ``lora_module`` -- v = A.x, delta = scale * B.v, y = y0 + delta for one
+  projection ("2. Scale Numbers" for the shapes of A and B; "6. Deep Dive A"
+  for y = Wx + (B.A)x(alpha/r)).
+* ``lora_layer`` -- the same for every projection in a module mask.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lora_oracle.c")
+_LIB = os.path.join(_HERE, "liblora_oracle.so")
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_vpp = ctypes.POINTER(ctypes.c_void_p)
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with the host C compiler (no fast-math, -O2)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(
+            ["gcc", "-std=c99", "-O2", "-fno-fast-math", "-ffp-contract=off",
+             "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC],
+            check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = _configure(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _configure(lib):
+    """Declare the C signatures on a loaded oracle library."""
+    lib.oracle_build_segments.restype = ctypes.c_int32
+    lib.oracle_build_segments.argtypes = [
+        _i32p, ctypes.c_int32, ctypes.c_int32, _i32p, _i32p, _i32p, _i32p]
+    lib.oracle_lora_module.restype = ctypes.c_int32
+    lib.oracle_lora_module.argtypes = [
+        _u16p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+        _u16p, ctypes.c_int64, ctypes.c_int32,
+        _i32p, ctypes.c_int32, _vpp, _vpp, _i32p, _f32p, ctypes.c_int32,
+        _i32p, ctypes.c_int32, _f64p, _f64p, _f64p, _f64p]
+    return lib
+
+
+def _ptr(a: np.ndarray, typ):
+    return a.ctypes.data_as(typ)
+
+
+@dataclass
+class Segments:
+    perm: np.ndarray          # int32 [n_valid]  original row of each sorted position
+    seg_offsets: np.ndarray   # int32 [nseg + 1]
+    seg_adapter: np.ndarray   # int32 [nseg]
+    num_segments: int
+    num_bad_ids: int          # rows with id >= num_slots
+
+
+def build_segments(ids: np.ndarray, num_slots: int) -> Segments:
+    """Stable grouping of rows by adapter id (ids < 0: base-only, skipped)."""
+    lib = _load()
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    n = ids.shape[0]
+    perm = np.full(max(n, 1), -1, np.int32)
+    offs = np.zeros(max(n, 1) + 1, np.int32)
+    adap = np.full(max(n, 1), -1, np.int32)
+    nseg = np.zeros(1, np.int32)
+    bad = lib.oracle_build_segments(_ptr(ids, _i32p), n, num_slots, _ptr(perm, _i32p),
+                                    _ptr(offs, _i32p), _ptr(adap, _i32p), _ptr(nseg, _i32p))
+    ns = int(nseg[0])
+    nvalid = int(offs[ns])
+    return Segments(perm[:nvalid].copy(), offs[:ns + 1].copy(), adap[:ns].copy(), ns, int(bad))
+
+
+@dataclass
+class ModuleResult:
+    v: np.ndarray       # float64 [n_sel, max_rank]
+    delta: np.ndarray   # float64 [n_sel, d_out]
+    y: np.ndarray       # float64 [n_sel, d_out]
+    num_bad_rank: int
+
+
+def lora_module(x: np.ndarray, y0: np.ndarray, ids: np.ndarray,
+                A_ptrs: np.ndarray, B_ptrs: np.ndarray, ranks: np.ndarray,
+                scales: np.ndarray, max_rank: int, rows=None,
+                keep_alive=()) -> ModuleResult:
+    """The delta of one projection for the selected rows.
+
+    x   uint16 (bf16 bits) [num_rows, >= d_in]; y0 uint16 [num_rows, >= d_out]
+    A_ptrs / B_ptrs: uint64 host addresses, one per slot, of bf16 arrays
+    A [rank, d_in] and B [d_out, rank] (row-major, compact); ranks int32,
+    scales float32, one per slot.  ``keep_alive`` holds the arrays those
+    addresses point into.  ``rows``: row indices to compute (default: all).
+    """
+    lib = _load()
+    assert x.dtype == np.uint16 and y0.dtype == np.uint16
+    assert x.ndim == 2 and y0.ndim == 2 and x.strides[1] == 2 and y0.strides[1] == 2
+    num_rows = x.shape[0]
+    assert y0.shape[0] == num_rows
+    d_in, d_out = x.shape[1], y0.shape[1]
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    assert ids.shape[0] == num_rows
+    if rows is None:
+        rows = np.arange(num_rows, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    assert rows.size == 0 or (rows.min() >= 0 and rows.max() < num_rows)
+    num_slots = ranks.shape[0]
+    A_ptrs = np.ascontiguousarray(A_ptrs, dtype=np.uint64)
+    B_ptrs = np.ascontiguousarray(B_ptrs, dtype=np.uint64)
+    ranks = np.ascontiguousarray(ranks, dtype=np.int32)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    n_sel = rows.shape[0]
+    v = np.zeros((n_sel, max_rank), np.float64)
+    delta = np.zeros((n_sel, d_out), np.float64)
+    y = np.zeros((n_sel, d_out), np.float64)
+    scratch = np.zeros(max_rank + d_out, np.float64)
+    bad = lib.oracle_lora_module(
+        _ptr(x, _u16p), x.strides[0] // 2, num_rows, d_in,
+        _ptr(y0, _u16p), y0.strides[0] // 2, d_out,
+        _ptr(ids, _i32p), num_slots,
+        A_ptrs.ctypes.data_as(_vpp), B_ptrs.ctypes.data_as(_vpp),
+        _ptr(ranks, _i32p), _ptr(scales, _f32p), max_rank,
+        _ptr(rows, _i32p), n_sel, _ptr(v, _f64p), _ptr(delta, _f64p), _ptr(y, _f64p),
+        _ptr(scratch, _f64p))
+    return ModuleResult(v, delta, y, int(bad))
+
+
+def lora_layer(workload, rows=None, modules=None) -> dict:
+    """Every projection of a layer-shaped workload (see ``workloads``).
+
+    Returns {module_name: ModuleResult}.  ``modules`` restricts the set.
+    """
+    out = {}
+    for m in workload.modules:
+        if modules is not None and m.name not in modules:
+            continue
+        A_ptrs, B_ptrs, ranks, scales = workload.host_table(m.index)
+        out[m.name] = lora_module(workload.x[m.x_name], workload.y0[m.name], workload.ids,
+                                  A_ptrs, B_ptrs, ranks, scales, workload.max_rank, rows=rows)
+    return out

@@ -1,0 +1,168 @@
+/*
+ * lora_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, single-threaded CPU statement of the heterogeneous-adapter
+ * LoRA delta, used to check the HIP library.  Only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg may load it.  It shares no source
+ * with the GPU library and must never be used as a fallback for it.
+ *
+ * Everything is the plain definition: bf16 inputs are decoded exactly to
+ * double, every product of two bf16 values is exact in double, and sums run in
+ * ascending index order in double.  No blocking, no fusion, no reordering.
+ *
+ * Sources (the pages this library's method comes from):
+ *  - "m07 -- Multi-Adapter (LoRA) Serving", section "2. Scale Numbers": a
+ *    weight W of shape (d_out, d_in) gains B.A with A (r, d_in) and
+ *    B (d_out, r).
+ *  - same page, "6. Deep Dive A: Batching Heterogeneous Adapters": the forward
+ *    is y = Wx + (B.A)x.(alpha/r); the adapter term is per row; the batched
+ *    kernel takes the batch, an index vector mapping each sequence to an
+ *    adapter slot, and the adapter buffer, and gathers inside the kernel.
+ *  - "12. Adapter Serving and Multi-Tenant Customization", section
+ *    "Scheduling with adapter awareness": requests are grouped by adapter,
+ *    base-only requests form their own group, and the adapter products are a
+ *    second, indexed operation after the shared base product.
+ *  - "LoRA, quotas and noisy neighbours", section "One weight read, many
+ *    adapters": rows are tagged with their adapter and grouped (segmented
+ *    gather matrix-vector).
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *  - rows whose id is negative are base-only: no segment, y unchanged;
+ *  - ids >= num_slots are errors: the row is skipped and counted;
+ *  - segments are in ascending adapter id, rows ascending inside a segment;
+ *  - rank 0 means the module is not targeted: zero delta;
+ *  - a table rank outside [0, max_rank] is an error: skipped and counted;
+ *  - scale (alpha/r) multiplies the delta, 1.0 when unspecified;
+ *  - the oracle keeps y in double with no output rounding.
+ */
+#include <stdint.h>
+#include <string.h>
+
+/* bf16 is the upper half of an IEEE-754 binary32; decoding is exact. */
+static double bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/*
+ * Segment build: group rows by adapter.  For each adapter a in ascending
+ * order, the rows b with ids[b] == a are appended to perm in ascending b; a
+ * segment opens for every adapter with at least one row.
+ *   perm[n_valid], seg_offsets[nseg + 1], seg_adapter[nseg], *num_segments.
+ * Returns the number of rows whose id is >= num_slots (errors).
+ */
+int32_t oracle_build_segments(const int32_t *ids, int32_t num_rows,
+                              int32_t num_slots, int32_t *perm,
+                              int32_t *seg_offsets, int32_t *seg_adapter,
+                              int32_t *num_segments)
+{
+    int32_t bad = 0, pos = 0, nseg = 0;
+    for (int32_t b = 0; b < num_rows; ++b)
+        if (ids[b] >= num_slots)
+            ++bad;
+    for (int32_t a = 0; a < num_slots; ++a) {
+        int32_t start = pos;
+        for (int32_t b = 0; b < num_rows; ++b)
+            if (ids[b] == a)
+                perm[pos++] = b;
+        if (pos > start) {
+            seg_offsets[nseg] = start;
+            seg_adapter[nseg] = a;
+            ++nseg;
+        }
+    }
+    seg_offsets[nseg] = pos;
+    *num_segments = nseg;
+    return bad;
+}
+
+/* v[j] = sum_k A[j][k] * x[k] for j < rank  (A row-major, leading dim d_in). */
+void oracle_shrink_row(const uint16_t *x, int32_t d_in, const uint16_t *A,
+                       int32_t rank, double *v)
+{
+    for (int32_t j = 0; j < rank; ++j) {
+        double s = 0.0;
+        const uint16_t *a = A + (int64_t)j * d_in;
+        for (int32_t k = 0; k < d_in; ++k)
+            s += bf16_value(a[k]) * bf16_value(x[k]);
+        v[j] = s;
+    }
+}
+
+/* delta[n] = scale * sum_j B[n][j] * v[j]  (B row-major, leading dim rank). */
+void oracle_expand_row(const double *v, int32_t rank, const uint16_t *B,
+                       int32_t d_out, double scale, double *delta)
+{
+    for (int32_t n = 0; n < d_out; ++n) {
+        double s = 0.0;
+        const uint16_t *b = B + (int64_t)n * rank;
+        for (int32_t j = 0; j < rank; ++j)
+            s += bf16_value(b[j]) * v[j];
+        delta[n] = scale * s;
+    }
+}
+
+/*
+ * One projection (module) over a set of rows.
+ *
+ *   x      bf16 [num_rows][ldx]        input rows
+ *   y0     bf16 [num_rows][ldy]        base output W.x
+ *   ids    int32 [num_rows]            row -> adapter slot (-1 = base only)
+ *   A_ptr, B_ptr, rank, scale  [num_slots]   the adapter table for this module
+ *   rows   int32 [n_sel]               which rows to compute (any order)
+ * Outputs, one line per selected row (in the order of `rows`):
+ *   v      double [n_sel][max_rank]    shrink result, 0 beyond the rank
+ *   delta  double [n_sel][d_out]       scale * B.v   (0 for skipped rows)
+ *   y      double [n_sel][d_out]       y0 + delta    (y0 for skipped rows)
+ * Any of v, delta, y may be NULL.  Returns the number of selected rows
+ * skipped because the table rank is outside [0, max_rank].
+ */
+int32_t oracle_lora_module(const uint16_t *x, int64_t ldx, int32_t num_rows,
+                           int32_t d_in, const uint16_t *y0, int64_t ldy,
+                           int32_t d_out, const int32_t *ids, int32_t num_slots,
+                           const uint16_t *const *A_ptr,
+                           const uint16_t *const *B_ptr, const int32_t *rank,
+                           const float *scale, int32_t max_rank,
+                           const int32_t *rows, int32_t n_sel, double *v,
+                           double *delta, double *y, double *scratch)
+{
+    int32_t bad = 0;
+    /* scratch holds max_rank + d_out doubles */
+    double *vr = scratch;
+    double *dr = scratch + max_rank;
+    for (int32_t i = 0; i < n_sel; ++i) {
+        int32_t b = rows[i];
+        int32_t a = (b >= 0 && b < num_rows) ? ids[b] : -1;
+        int32_t r = 0;
+        int ok = 0;
+        if (a >= 0 && a < num_slots) {
+            r = rank[a];
+            if (r < 0 || r > max_rank)
+                ++bad;
+            else if (r > 0)
+                ok = 1;
+        }
+        for (int32_t j = 0; j < max_rank; ++j)
+            vr[j] = 0.0;
+        for (int32_t n = 0; n < d_out; ++n)
+            dr[n] = 0.0;
+        if (ok) {
+            oracle_shrink_row(x + (int64_t)b * ldx, d_in, A_ptr[a], r, vr);
+            oracle_expand_row(vr, r, B_ptr[a], d_out, (double)scale[a], dr);
+        }
+        if (v)
+            for (int32_t j = 0; j < max_rank; ++j)
+                v[(int64_t)i * max_rank + j] = vr[j];
+        if (delta)
+            for (int32_t n = 0; n < d_out; ++n)
+                delta[(int64_t)i * d_out + n] = dr[n];
+        if (y)
+            for (int32_t n = 0; n < d_out; ++n)
+                y[(int64_t)i * d_out + n] =
+                    bf16_value(y0[(int64_t)b * ldy + n]) + dr[n];
+    }
+    return bad;
+}

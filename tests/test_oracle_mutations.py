@@ -1,0 +1,59 @@
+"""The oracle's pins are sensitive: each plausible mistake planted in a copy of
+the oracle's C source (on the CPU, in a temporary library) fails at least one
+pin from ``test_oracle_pins``.  The real oracle is untouched.
+"""
+import ctypes
+import subprocess
+
+import pytest
+
+import oracle
+import tests.test_oracle_pins as pins
+
+SRC = open(oracle._SRC).read()
+
+MUTATIONS = {
+    "drop_last_k": ("for (int32_t k = 0; k < d_in; ++k)", "for (int32_t k = 0; k < d_in - 1; ++k)"),
+    "wrong_sign": ("s += bf16_value(a[k]) * bf16_value(x[k]);", "s -= bf16_value(a[k]) * bf16_value(x[k]);"),
+    "A_transposed": ("s += bf16_value(a[k]) * bf16_value(x[k]);",
+                     "s += bf16_value(A[(int64_t)k * rank + j]) * bf16_value(x[k]); (void)a;"),
+    "B_transposed": ("s += bf16_value(b[j]) * v[j];", "s += bf16_value(B[(int64_t)j * d_out + n]) * v[j]; (void)b;"),
+    "drop_last_rank_term": ("for (int32_t j = 0; j < rank; ++j)\n            s += bf16_value(b[j])",
+                            "for (int32_t j = 0; j < rank - 1; ++j)\n            s += bf16_value(b[j])"),
+    "no_scale": ("delta[n] = scale * s;", "delta[n] = s; (void)scale;"),
+    "wrong_row_adapter": ("int32_t a = (b >= 0 && b < num_rows) ? ids[b] : -1;",
+                          "int32_t a = (b >= 0 && b < num_rows) ? ids[(b + 1) % num_rows] : -1;"),
+    "no_base_output": ("bf16_value(y0[(int64_t)b * ldy + n]) + dr[n];", "dr[n]; (void)y0;"),
+    "unstable_segments": ("for (int32_t b = 0; b < num_rows; ++b)\n            if (ids[b] == a)",
+                          "for (int32_t b = num_rows - 1; b >= 0; --b)\n            if (ids[b] == a)"),
+    "keeps_bad_ids": ("if (ids[b] >= num_slots)\n            ++bad;", "if (ids[b] >= num_slots)\n            bad += 0;"),
+}
+
+CHECKS = [
+    (pins.test_exact_rational, dict(d_in=8, d_out=16, rank=8, rows=6, slots=3)),
+    (pins.test_exact_rational, dict(d_in=24, d_out=8, rank=3, rows=5, slots=4)),
+    (pins.test_against_blas_medium, {}),
+    (pins.test_one_hot_gather_closed_form, {}),
+    (pins.test_identity_adapter, {}),
+    (pins.test_merged_weight_identity, {}),
+    (pins.test_zero_cases_leave_y_exactly, {}),
+    (pins.test_segments_vs_stable_sort, dict(n=257, slots=9, seed=3)),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, tmp_path, monkeypatch):
+    old, new = MUTATIONS[name]
+    assert SRC.count(old) >= 1, name
+    src = tmp_path / "mutant.c"
+    src.write_text(SRC.replace(old, new, 1))
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-std=c99", "-O2", "-fPIC", "-shared", "-o", str(so), str(src)], check=True)
+    monkeypatch.setattr(oracle, "_lib", oracle._configure(ctypes.CDLL(str(so))))
+    caught = []
+    for fn, kw in CHECKS:
+        try:
+            fn(**kw)
+        except AssertionError:
+            caught.append(fn.__name__)
+    assert caught, f"no pin catches the planted mistake {name}"
