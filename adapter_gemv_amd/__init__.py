@@ -1,0 +1,232 @@
+"""Python binding of ``liblora_gemv.so``, the gfx950 heterogeneous-adapter LoRA delta.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+declared in ``include/lora_gemv.h``.  PyTorch provides device memory and the
+stream (the current torch stream unless one is given).  There is no CPU path:
+if the library is not built, importing the binding's functions raises.
+
+The calls follow "m07 -- Multi-Adapter (LoRA) Serving", "6. Deep Dive A:
+Batching Heterogeneous Adapters": the batch, an index vector mapping each row
+to an adapter slot, and an adapter table read on the device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "LoraError", "Segments", "ModuleIO", "MODULES", "TABLE_ENTRY_DTYPE", "lib", "workspace_bytes",
+    "build_segments", "shrink", "expand", "apply_layer", "layer_shrink", "layer_expand", "pack_table",
+    "status_string", "MAX_RANK",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblora_gemv.so")
+MAX_RANK = 64
+MODULES = ("q", "k", "v", "o", "gate", "up", "down")
+
+# lora_adapter_entry_t, 32 bytes
+TABLE_ENTRY_DTYPE = np.dtype([("A", "<u8"), ("B", "<u8"), ("rank", "<i4"), ("scale", "<f4"), ("reserved", "<i8")])
+assert TABLE_ENTRY_DTYPE.itemsize == 32
+
+
+class LoraError(RuntimeError):
+    pass
+
+
+class _Seg(ctypes.Structure):
+    _fields_ = [("perm", ctypes.c_void_p), ("seg_offsets", ctypes.c_void_p), ("seg_adapter", ctypes.c_void_p),
+                ("num_segments", ctypes.c_void_p), ("status", ctypes.c_void_p)]
+
+
+class _IO(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("ldx", ctypes.c_int64), ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64),
+                ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LoraError(f"{LIB_PATH} is missing: build it with `python -m adapter_gemv_amd.build` "
+                            "(there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        st, i32, i64, u32, vp, sz = (ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
+                                     ctypes.c_void_p, ctypes.c_size_t)
+        L.lora_workspace_bytes.restype = sz
+        L.lora_workspace_bytes.argtypes = [i32, i32, i32, i64]
+        L.lora_status_string.restype = ctypes.c_char_p
+        L.lora_status_string.argtypes = [st]
+        L.lora_build_segments.restype = st
+        L.lora_build_segments.argtypes = [vp, i32, i32, _Seg, vp, sz, vp]
+        L.lora_shrink.restype = st
+        L.lora_shrink.argtypes = [vp, i64, i32, i32, vp, i32, i32, i32, _Seg, i32, vp, i64, vp, sz, vp]
+        L.lora_expand.restype = st
+        L.lora_expand.argtypes = [vp, i64, i32, i32, vp, i32, i32, i32, _Seg, i32, vp, i64, vp, sz, vp]
+        for name in ("lora_apply_layer", "lora_layer_shrink", "lora_layer_expand"):
+            f = getattr(L, name)
+            f.restype = st
+            f.argtypes = [ctypes.POINTER(_IO), u32, i32, vp, i32, _Seg, i32, vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().lora_status_string(code).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise LoraError(f"{what}: {status_string(code)}")
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, dtype, what, ndim=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be on the GPU")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{what} must have {ndim} dims")
+    if t.dim() >= 1 and t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{what} must have unit stride in its last dim")
+
+
+class Segments:
+    """Device buffers of lora_segments_t for batches of up to ``num_rows`` rows."""
+
+    def __init__(self, num_rows: int, device="cuda"):
+        import torch
+        n = max(int(num_rows), 1)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.num_rows = int(num_rows)
+        self.perm = torch.zeros(n, **i32)
+        self.seg_offsets = torch.zeros(n + 1, **i32)
+        self.seg_adapter = torch.zeros(n, **i32)
+        self.num_segments = torch.zeros(1, **i32)
+        self.status = torch.zeros(1, **i32)
+
+    def c(self) -> _Seg:
+        return _Seg(self.perm.data_ptr(), self.seg_offsets.data_ptr(), self.seg_adapter.data_ptr(),
+                    self.num_segments.data_ptr(), self.status.data_ptr())
+
+    def host(self):
+        """(perm, seg_offsets, seg_adapter, status) copied to the host (synchronises)."""
+        ns = int(self.num_segments.item())
+        offs = self.seg_offsets[:ns + 1].cpu().numpy()
+        return (self.perm[:int(offs[-1])].cpu().numpy(), offs, self.seg_adapter[:ns].cpu().numpy(),
+                int(self.status.item()))
+
+
+class ModuleIO:
+    """One projection for the layer calls: x [rows, >= d_in], y [rows, >= d_out], bf16."""
+
+    def __init__(self, x, y, d_in=None, d_out=None):
+        self.x, self.y = x, y
+        self.d_in = int(x.shape[1] if d_in is None else d_in)
+        self.d_out = int(y.shape[1] if d_out is None else d_out)
+
+
+def workspace_bytes(num_rows: int, num_slots: int, max_rank: int, sum_d_in: int) -> int:
+    return int(lib().lora_workspace_bytes(num_rows, num_slots, max_rank, sum_d_in))
+
+
+def pack_table(A_ptrs, B_ptrs, ranks, scales) -> np.ndarray:
+    """Host bytes of a table of lora_adapter_entry_t; arrays of shape [num_slots, n_mod]."""
+    ranks = np.asarray(ranks)
+    t = np.zeros(ranks.shape, TABLE_ENTRY_DTYPE)
+    t["A"] = np.asarray(A_ptrs, np.uint64)
+    t["B"] = np.asarray(B_ptrs, np.uint64)
+    t["rank"] = ranks.astype(np.int32)
+    t["scale"] = np.asarray(scales, np.float32)
+    return t
+
+
+def build_segments(row_adapter, num_slots: int, seg: Segments, ws, stream=None):
+    """Group rows by adapter slot (stable); see lora_build_segments."""
+    import torch
+    _need(row_adapter, torch.int32, "row_adapter", 1)
+    n = row_adapter.shape[0]
+    if n > seg.num_rows:
+        raise ValueError("Segments buffers too small for this batch")
+    _check(lib().lora_build_segments(_ptr(row_adapter), n, num_slots, seg.c(), _ptr(ws), ws.numel() * ws.element_size(),
+                                     _stream(stream)), "lora_build_segments")
+
+
+def shrink(x, table, num_slots: int, n_mod: int, module: int, seg: Segments, max_rank: int, v, ws, stream=None):
+    """v[b, :rank] = A . x[b] for rows in a segment; see lora_shrink."""
+    import torch
+    _need(x, torch.bfloat16, "x", 2)
+    _need(v, torch.float32, "v", 2)
+    _check(lib().lora_shrink(_ptr(x), x.stride(0), x.shape[0], x.shape[1], _ptr(table), num_slots, n_mod, module,
+                             seg.c(), max_rank, _ptr(v), v.stride(0), _ptr(ws), ws.numel() * ws.element_size(),
+                             _stream(stream)), "lora_shrink")
+
+
+def expand(v, table, num_slots: int, n_mod: int, module: int, seg: Segments, max_rank: int, y, ws, stream=None):
+    """y[b] = bf16(y[b] + scale * B . v[b]) for rows in a segment; see lora_expand."""
+    import torch
+    _need(v, torch.float32, "v", 2)
+    _need(y, torch.bfloat16, "y", 2)
+    _check(lib().lora_expand(_ptr(v), v.stride(0), y.shape[0], y.shape[1], _ptr(table), num_slots, n_mod, module,
+                             seg.c(), max_rank, _ptr(y), y.stride(0), _ptr(ws), ws.numel() * ws.element_size(),
+                             _stream(stream)), "lora_expand")
+
+
+def _ios(ios, num_rows):
+    import torch
+    arr = (_IO * 7)()
+    mask = 0
+    for i, name in enumerate(MODULES):
+        io = ios.get(name) if isinstance(ios, dict) else (ios[i] if i < len(ios) else None)
+        if io is None:
+            continue
+        _need(io.x, torch.bfloat16, f"{name}.x", 2)
+        _need(io.y, torch.bfloat16, f"{name}.y", 2)
+        if io.x.shape[0] < num_rows or io.y.shape[0] < num_rows:
+            raise ValueError(f"{name}: fewer rows than num_rows")
+        arr[i] = _IO(io.x.data_ptr(), io.x.stride(0), io.y.data_ptr(), io.y.stride(0), io.d_in, io.d_out)
+        mask |= 1 << i
+    return arr, mask
+
+
+def _layer(fn, what, ios, num_rows, table, num_slots, seg, max_rank, ws, stream, module_mask):
+    arr, mask = _ios(ios, num_rows)
+    if module_mask is None:
+        module_mask = mask
+    _check(fn(arr, module_mask, num_rows, _ptr(table), num_slots, seg.c(), max_rank, _ptr(ws),
+              ws.numel() * ws.element_size(), _stream(stream)), what)
+
+
+def apply_layer(ios, num_rows, table, num_slots, seg, max_rank, ws, stream=None, module_mask=None):
+    """Delta of every projection given in ``ios`` ({name: ModuleIO}); see lora_apply_layer."""
+    _layer(lib().lora_apply_layer, "lora_apply_layer", ios, num_rows, table, num_slots, seg, max_rank, ws, stream,
+           module_mask)
+
+
+def layer_shrink(ios, num_rows, table, num_slots, seg, max_rank, ws, stream=None, module_mask=None):
+    _layer(lib().lora_layer_shrink, "lora_layer_shrink", ios, num_rows, table, num_slots, seg, max_rank, ws, stream,
+           module_mask)
+
+
+def layer_expand(ios, num_rows, table, num_slots, seg, max_rank, ws, stream=None, module_mask=None):
+    _layer(lib().lora_layer_expand, "lora_layer_expand", ios, num_rows, table, num_slots, seg, max_rank, ws, stream,
+           module_mask)

@@ -1,0 +1,251 @@
+// C ABI of the LoRA-delta library: argument checks, work decomposition and
+// launches.  Every check runs before the first HIP call, so a rejected call
+// touches neither the device nor the stream.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lora_internal.h"
+
+using namespace lora;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+lora_status_t check_segments(const lora_segments_t &seg) {
+  if (!seg.perm || !seg.seg_offsets || !seg.seg_adapter || !seg.num_segments || !seg.status) return LORA_ERR_NULL;
+  return LORA_OK;
+}
+
+size_t ws_need(int num_rows, int num_slots, int max_rank, int64_t sum_d_in) {
+  const size_t a = segments_ws_bytes(num_rows, num_slots);
+  const size_t b = partials_ws_bytes(num_rows, max_rank, sum_d_in);
+  return a > b ? a : b;
+}
+
+// Work decomposition: the n-tile of the expand (the shrink k-chunk is
+// kKChunkMin).
+int pick_nt(int max_rank) {
+  // One expand item streams 16 loads of 16 bytes per lane; an n-tile of
+  // that many outputs at the table's largest rank, at least 1024.
+  int cls = max_rank <= 8 ? 8 : max_rank <= 16 ? 16 : max_rank <= 32 ? 32 : 64;
+  int lpr = cls / 8;
+  int sub = 16 * kDecodeThreads / lpr;
+  return sub < 1024 ? 1024 : sub;
+}
+
+struct ModuleArgs {
+  const void *x;
+  int64_t ldx;
+  void *y;
+  int64_t ldy;
+  int32_t d_in;
+  int32_t d_out;
+  int32_t col;
+};
+
+// Fill the descriptor for a set of modules; items are k-chunks (shrink) or
+// n-tiles (expand).
+void fill_desc(LayerDesc &d, const ModuleArgs *ms, int n, bool shrink_items, int num_rows, int num_slots,
+               int max_rank, int table_cols, const lora_adapter_entry_t *table, const lora_segments_t &seg,
+               void *ws) {
+  d = LayerDesc{};
+  d.kc = kKChunkMin;
+  d.nt = pick_nt(max_rank);
+  int item = 0, chunk = 0;
+  for (int i = 0; i < n; ++i) {
+    ModuleDesc &m = d.mod[i];
+    m.x = static_cast<const uint16_t *>(ms[i].x);
+    m.ldx = ms[i].ldx;
+    m.y = static_cast<uint16_t *>(ms[i].y);
+    m.ldy = ms[i].ldy;
+    m.d_in = ms[i].d_in;
+    m.d_out = ms[i].d_out;
+    m.col = ms[i].col;
+    m.n_chunks = m.d_in > 0 ? (m.d_in + d.kc - 1) / d.kc : 0;
+    m.part_base = chunk;
+    chunk += m.n_chunks;
+    m.n_items = shrink_items ? m.n_chunks : (m.d_out + d.nt - 1) / d.nt;
+    m.item_base = item;
+    item += m.n_items;
+  }
+  d.n_active = n;
+  d.items_per_seg = item;
+  d.table_cols = table_cols;
+  d.rs = partial_row_stride(max_rank);
+  d.num_rows = num_rows;
+  d.num_slots = num_slots;
+  d.max_rank = max_rank;
+  d.perm = seg.perm;
+  d.seg_offsets = seg.seg_offsets;
+  d.seg_adapter = seg.seg_adapter;
+  d.num_segments = seg.num_segments;
+  d.status = seg.status;
+  d.table = table;
+  d.part = static_cast<float *>(ws);
+}
+
+int grid_for(const LayerDesc &d, int num_rows, int num_slots) {
+  const int64_t max_seg = num_rows < num_slots ? num_rows : num_slots;
+  const int64_t g = max_seg * d.items_per_seg;
+  return g > 0x7fffffff ? -1 : (int)g;
+}
+
+lora_status_t launched(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_ERR_LAUNCH; }
+
+// Common checks of the layer calls; fills the module list.
+lora_status_t check_layer(const lora_module_io_t *io, uint32_t module_mask, int32_t num_rows,
+                          const lora_adapter_entry_t *table, int32_t num_slots, const lora_segments_t &seg,
+                          int32_t max_rank, void *ws, size_t ws_bytes, ModuleArgs *ms, int *n_out) {
+  if (!io || !table || !ws) return LORA_ERR_NULL;
+  lora_status_t st = check_segments(seg);
+  if (st != LORA_OK) return st;
+  if (module_mask == 0 || module_mask >= (1u << LORA_NUM_MODULES)) return LORA_ERR_MODULE;
+  if (num_rows < 0 || num_slots < 1) return LORA_ERR_SHAPE;
+  if (max_rank < 1 || max_rank > LORA_MAX_RANK) return LORA_ERR_RANK;
+  int n = 0;
+  int64_t sum_d_in = 0;
+  for (int c = 0; c < LORA_NUM_MODULES; ++c) {
+    if (!(module_mask & (1u << c))) continue;
+    const lora_module_io_t &m = io[c];
+    if (!m.x || !m.y) return LORA_ERR_NULL;
+    if (m.d_in <= 0 || m.d_out <= 0 || m.ldx < m.d_in || m.ldy < m.d_out) return LORA_ERR_SHAPE;
+    if ((m.d_in & 7) || (m.d_out & 7) || (m.ldx & 7) || (m.ldy & 7) || !aligned16(m.x) || !aligned16(m.y))
+      return LORA_ERR_ALIGN;
+    ms[n] = ModuleArgs{m.x, m.ldx, m.y, m.ldy, m.d_in, m.d_out, c};
+    sum_d_in += m.d_in;
+    ++n;
+  }
+  if (ws_bytes < ws_need(num_rows, num_slots, max_rank, sum_d_in)) return LORA_ERR_WORKSPACE;
+  *n_out = n;
+  return LORA_OK;
+}
+
+lora_status_t layer_phase(bool do_shrink, bool do_expand, const lora_module_io_t *io, uint32_t module_mask,
+                          int32_t num_rows, const lora_adapter_entry_t *table, int32_t num_slots,
+                          lora_segments_t seg, int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
+  ModuleArgs ms[LORA_NUM_MODULES];
+  int n = 0;
+  lora_status_t st = check_layer(io, module_mask, num_rows, table, num_slots, seg, max_rank, ws, ws_bytes, ms, &n);
+  if (st != LORA_OK) return st;
+  if (num_rows == 0) return LORA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  LayerDesc d;
+  if (do_shrink) {
+    fill_desc(d, ms, n, true, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws);
+    const int g = grid_for(d, num_rows, num_slots);
+    if (g < 0) return LORA_ERR_SHAPE;
+    st = launched(launch_decode_shrink(d, g, s));
+    if (st != LORA_OK) return st;
+  }
+  if (do_expand) {
+    fill_desc(d, ms, n, false, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws);
+    const int g = grid_for(d, num_rows, num_slots);
+    if (g < 0) return LORA_ERR_SHAPE;
+    st = launched(launch_decode_expand(d, g, s));
+  }
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lora_workspace_bytes(int32_t num_rows, int32_t num_slots, int32_t max_rank, int64_t sum_d_in) {
+  if (num_rows < 0 || num_slots < 1 || max_rank < 1 || max_rank > LORA_MAX_RANK || sum_d_in < 0) return 0;
+  return ws_need(num_rows, num_slots, max_rank, sum_d_in);
+}
+
+const char *lora_status_string(lora_status_t status) {
+  switch (status) {
+    case LORA_OK: return "LORA_OK";
+    case LORA_ERR_NULL: return "LORA_ERR_NULL: a required pointer is NULL";
+    case LORA_ERR_SHAPE: return "LORA_ERR_SHAPE: a size or leading dimension is out of range";
+    case LORA_ERR_RANK: return "LORA_ERR_RANK: max_rank outside [1, LORA_MAX_RANK]";
+    case LORA_ERR_ALIGN: return "LORA_ERR_ALIGN: pointer or dimension not 16-byte / 8-element aligned";
+    case LORA_ERR_WORKSPACE: return "LORA_ERR_WORKSPACE: workspace too small";
+    case LORA_ERR_MODULE: return "LORA_ERR_MODULE: bad module index, n_mod or module mask";
+    case LORA_ERR_LAUNCH: return "LORA_ERR_LAUNCH: kernel launch failed";
+  }
+  return "unknown lora_status_t";
+}
+
+lora_status_t lora_build_segments(const int32_t *row_adapter, int32_t num_rows, int32_t num_slots,
+                                  lora_segments_t seg, void *ws, size_t ws_bytes, void *stream) {
+  lora_status_t st = check_segments(seg);
+  if (st != LORA_OK) return st;
+  if (num_rows < 0 || num_slots < 1) return LORA_ERR_SHAPE;
+  if (num_rows > 0 && !row_adapter) return LORA_ERR_NULL;
+  if (!ws) return LORA_ERR_NULL;
+  if (ws_bytes < segments_ws_bytes(num_rows, num_slots)) return LORA_ERR_WORKSPACE;
+  return launched(launch_build_segments(row_adapter, num_rows, num_slots, seg, ws, static_cast<hipStream_t>(stream)));
+}
+
+lora_status_t lora_shrink(const void *x, int64_t ldx, int32_t num_rows, int32_t d_in,
+                          const lora_adapter_entry_t *table, int32_t num_slots, int32_t n_mod, int32_t module,
+                          lora_segments_t seg, int32_t max_rank, float *v, int64_t ldv, void *ws, size_t ws_bytes,
+                          void *stream) {
+  if (!x || !table || !v || !ws) return LORA_ERR_NULL;
+  lora_status_t st = check_segments(seg);
+  if (st != LORA_OK) return st;
+  if (n_mod < 1 || n_mod > LORA_NUM_MODULES || module < 0 || module >= n_mod) return LORA_ERR_MODULE;
+  if (max_rank < 1 || max_rank > LORA_MAX_RANK) return LORA_ERR_RANK;
+  if (num_rows < 0 || num_slots < 1 || d_in <= 0 || ldx < d_in || ldv < max_rank) return LORA_ERR_SHAPE;
+  if ((d_in & 7) || (ldx & 7) || (ldv & 3) || !aligned16(x) || !aligned16(v)) return LORA_ERR_ALIGN;
+  if (ws_bytes < ws_need(num_rows, num_slots, max_rank, d_in)) return LORA_ERR_WORKSPACE;
+  if (num_rows == 0) return LORA_OK;
+  ModuleArgs m{x, ldx, nullptr, 0, d_in, 0, module};
+  LayerDesc d;
+  fill_desc(d, &m, 1, true, num_rows, num_slots, max_rank, n_mod, table, seg, ws);
+  d.v_out = v;
+  d.ldv = ldv;
+  const int g = grid_for(d, num_rows, num_slots);
+  if (g < 0) return LORA_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launched(launch_decode_shrink(d, g, s));
+  if (st != LORA_OK) return st;
+  return launched(launch_shrink_reduce(d, s));
+}
+
+lora_status_t lora_expand(const float *v, int64_t ldv, int32_t num_rows, int32_t d_out,
+                          const lora_adapter_entry_t *table, int32_t num_slots, int32_t n_mod, int32_t module,
+                          lora_segments_t seg, int32_t max_rank, void *y, int64_t ldy, void *ws, size_t ws_bytes,
+                          void *stream) {
+  if (!v || !table || !y || !ws) return LORA_ERR_NULL;
+  lora_status_t st = check_segments(seg);
+  if (st != LORA_OK) return st;
+  if (n_mod < 1 || n_mod > LORA_NUM_MODULES || module < 0 || module >= n_mod) return LORA_ERR_MODULE;
+  if (max_rank < 1 || max_rank > LORA_MAX_RANK) return LORA_ERR_RANK;
+  if (num_rows < 0 || num_slots < 1 || d_out <= 0 || ldy < d_out || ldv < max_rank) return LORA_ERR_SHAPE;
+  if ((d_out & 7) || (ldy & 7) || (ldv & 3) || !aligned16(y) || !aligned16(v)) return LORA_ERR_ALIGN;
+  if (ws_bytes < ws_need(num_rows, num_slots, max_rank, 0)) return LORA_ERR_WORKSPACE;
+  if (num_rows == 0) return LORA_OK;
+  ModuleArgs m{nullptr, 0, y, ldy, 0, d_out, module};
+  LayerDesc d;
+  fill_desc(d, &m, 1, false, num_rows, num_slots, max_rank, n_mod, table, seg, ws);
+  d.v = v;
+  d.ldv = ldv;
+  const int g = grid_for(d, num_rows, num_slots);
+  if (g < 0) return LORA_ERR_SHAPE;
+  return launched(launch_decode_expand(d, g, static_cast<hipStream_t>(stream)));
+}
+
+lora_status_t lora_layer_shrink(const lora_module_io_t *io, uint32_t module_mask, int32_t num_rows,
+                                const lora_adapter_entry_t *table, int32_t num_slots, lora_segments_t seg,
+                                int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
+  return layer_phase(true, false, io, module_mask, num_rows, table, num_slots, seg, max_rank, ws, ws_bytes, stream);
+}
+
+lora_status_t lora_layer_expand(const lora_module_io_t *io, uint32_t module_mask, int32_t num_rows,
+                                const lora_adapter_entry_t *table, int32_t num_slots, lora_segments_t seg,
+                                int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
+  return layer_phase(false, true, io, module_mask, num_rows, table, num_slots, seg, max_rank, ws, ws_bytes, stream);
+}
+
+lora_status_t lora_apply_layer(const lora_module_io_t *io, uint32_t module_mask, int32_t num_rows,
+                               const lora_adapter_entry_t *table, int32_t num_slots, lora_segments_t seg,
+                               int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
+  return layer_phase(true, true, io, module_mask, num_rows, table, num_slots, seg, max_rank, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

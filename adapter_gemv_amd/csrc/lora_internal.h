@@ -1,0 +1,81 @@
+// Internal declarations of the gfx950 LoRA-delta library (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lora_gemv.h"
+
+namespace lora {
+
+// Segment builder: one block handles up to this many rows; beyond it the
+// rows are cut into chunks of kSegChunk and two kernels run.
+constexpr int kSegSmallMax = 1024;
+constexpr int kSegChunk = 1024;
+constexpr int kSegThreads = 1024;
+
+// Decode shrink: k-chunk per work item (the workspace is sized for the
+// smallest chunk the host may pick).
+constexpr int kKChunkMin = 1024;
+constexpr int kMaxModules = LORA_NUM_MODULES;
+
+// Threads per block of the decode kernels: 4 waves of 64.
+constexpr int kDecodeThreads = 256;
+// Rows staged in LDS per group by the decode expand.
+constexpr int kExpandRowGroup = 16;
+
+// One projection as the kernels see it.
+struct ModuleDesc {
+  const uint16_t *x;
+  int64_t ldx;
+  uint16_t *y;
+  int64_t ldy;
+  int32_t d_in;
+  int32_t d_out;
+  int32_t col;        // table column
+  int32_t item_base;  // first work item of this module inside a segment
+  int32_t n_items;    // k-chunks (shrink) or n-tiles (expand)
+  int32_t part_base;  // first partial chunk of this module
+  int32_t n_chunks;   // k-chunks of this module
+};
+
+// Everything a decode kernel needs, passed by value.
+struct LayerDesc {
+  ModuleDesc mod[kMaxModules];
+  int32_t n_active;       // modules in use (mod[0..n_active))
+  int32_t items_per_seg;  // sum of n_items over modules
+  int32_t table_cols;     // n_mod of the table
+  int32_t kc;             // shrink k-chunk
+  int32_t nt;             // expand n-tile
+  int32_t rs;             // floats per row of a partial chunk
+  int32_t num_rows;
+  int32_t num_slots;
+  int32_t max_rank;
+  const int32_t *perm;
+  const int32_t *seg_offsets;
+  const int32_t *seg_adapter;
+  const int32_t *num_segments;
+  int32_t *status;
+  const lora_adapter_entry_t *table;
+  float *part;            // partials [chunks][num_rows][rs]
+  // expand source when v comes from the caller (lora_expand): v[b][j]
+  const float *v;
+  int64_t ldv;
+  // shrink destination when v goes to the caller (lora_shrink reduce)
+  float *v_out;
+};
+
+inline int round_up(int a, int b) { return (a + b - 1) / b * b; }
+inline int partial_row_stride(int max_rank) { return round_up(max_rank, 8); }
+
+size_t segments_ws_bytes(int num_rows, int num_slots);
+size_t partials_ws_bytes(int num_rows, int max_rank, int64_t sum_d_in);
+
+hipError_t launch_build_segments(const int32_t *ids, int n, int num_slots,
+                                 const lora_segments_t &seg, void *ws,
+                                 hipStream_t stream);
+hipError_t launch_decode_shrink(const LayerDesc &d, int grid, hipStream_t stream);
+hipError_t launch_shrink_reduce(const LayerDesc &d, hipStream_t stream);
+hipError_t launch_decode_expand(const LayerDesc &d, int grid, hipStream_t stream);
+
+}  // namespace lora

@@ -1,0 +1,37 @@
+"""Algorithmic HBM bytes and FLOPs of one delta step, for roofline reporting.
+
+What the method itself must move ("m07 -- Multi-Adapter (LoRA) Serving",
+"6. Deep Dive A", "The cost is bandwidth, not compute": the base weights are
+read once per step and each distinct adapter once): every distinct adapter
+present in the batch read once at its own rank, every activation tensor read
+once, and y read once and written once.  The rank-r intermediate stays on chip
+and is not counted.  Split by kernel: the shrink moves A and x, the expand
+moves B and y.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def step_traffic(ids, num_slots, modules, ranks) -> dict:
+    """ids: int [rows] (negative = base only, >= num_slots = skipped);
+    modules: [(name, table column, d_in, d_out, x tensor name)];
+    ranks: int [num_slots, columns]."""
+    ids = np.asarray(ids)
+    valid = (ids >= 0) & (ids < num_slots)
+    slots, counts = np.unique(ids[valid], return_counts=True)
+    a_bytes = b_bytes = y_bytes = flops = 0
+    x_rows = {}
+    for name, col, d_in, d_out, x_name in modules:
+        r = np.asarray(ranks)[slots, col].astype(np.int64)
+        on = r > 0
+        a_bytes += int(2 * (r[on] * d_in).sum())
+        b_bytes += int(2 * (r[on] * d_out).sum())
+        rows = int(counts[on].sum())
+        y_bytes += 4 * rows * d_out
+        flops += int((counts[on] * 2 * r[on] * (d_in + d_out)).sum())
+        x_rows[x_name] = (max(rows, x_rows.get(x_name, (0, 0))[0]), d_in)
+    x_bytes = sum(2 * n * d for n, d in x_rows.values())
+    return {"adapters": a_bytes + b_bytes, "x": x_bytes, "y": y_bytes,
+            "total": a_bytes + b_bytes + x_bytes + y_bytes,
+            "shrink_bytes": a_bytes + x_bytes, "expand_bytes": b_bytes + y_bytes, "flops": flops}

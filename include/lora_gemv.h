@@ -1,0 +1,263 @@
+/*
+ * lora_gemv.h -- C ABI of the heterogeneous-adapter LoRA delta on MI355X
+ * (gfx950).
+ *
+ * For a batch of rows in which every row b names its own adapter slot
+ * a = row_adapter[b], the library adds that adapter's low-rank delta to the
+ * base output of each projection:
+ *
+ *     v[b]  = A_a . x[b]                       (shrink, rank-r vector)
+ *     y[b] += scale_a * B_a . v[b]             (expand, fused into y)
+ *
+ * Sources:
+ *  - "m07 -- Multi-Adapter (LoRA) Serving", "2. Scale Numbers": a LoRA on a
+ *    weight W of shape (d_out, d_in) is B.A with A of shape (r, d_in) and B of
+ *    shape (d_out, r); r * (d_in + d_out) parameters per projection.
+ *  - same page, "6. Deep Dive A: Batching Heterogeneous Adapters": the forward
+ *    is y = Wx + (B.A)x(alpha/r); the base term is shared, the adapter term is
+ *    per row; one batched kernel takes the batch, an index vector mapping each
+ *    sequence to an adapter slot and the adapter buffer, and gathers inside
+ *    the kernel (BGMV for decode, SGMV for variable-length prefill segments).
+ *  - "12. Adapter Serving and Multi-Tenant Customization", "Scheduling with
+ *    adapter awareness": the adapter products are a second, indexed operation
+ *    after the base product, with per-request adapter pointers and a
+ *    base-only group; "Interactions with other engine mechanisms", CUDA
+ *    graphs: adapter addresses are read from a buffer at run time rather than
+ *    baked into a captured graph; "vLLM's pre-allocated LoRA buffers" and
+ *    "S-LoRA's unified paging": adapters live in fixed-size slots reached
+ *    through a table.
+ *  - "LoRA, quotas and noisy neighbours", "One weight read, many adapters":
+ *    rows are tagged with their adapter and grouped; the update is applied in
+ *    registers.
+ *
+ * Conventions for every call:
+ *  - bf16 tensors are raw 16-bit bfloat16 values, row-major.
+ *  - Every pointer argument marked "device" is device memory owned by the
+ *    caller.  The library allocates nothing, keeps no pointer after a call
+ *    returns and has no global state; it is reentrant.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues work on it and returns; nothing synchronises the host.  Buffers
+ *    must stay alive until the stream has passed the call.  No call
+ *    allocates, frees or memsets through the runtime, so calls may be
+ *    captured into a HIP graph; the table, the row ids and the segments are
+ *    read from device memory when the kernels run.
+ *  - Host-detectable errors (listed per call) return a status and enqueue
+ *    nothing.  Errors in device data never fault: the affected rows or
+ *    (segment, projection) pairs are skipped, leaving y unchanged, and the
+ *    device status word `*seg.status` becomes nonzero.
+ *  - Dimensions d_in, d_out and leading dimensions are counted in elements;
+ *    d_in, d_out, ldx and ldy must be multiples of 8 and x, y pointers
+ *    16-byte aligned (16-byte vector access).
+ */
+#ifndef LORA_GEMV_H
+#define LORA_GEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest adapter rank the kernels accept (the pages' serving ranks run from
+ * 8 to 64: "12. Adapter Serving ...", "What an adapter adds"). */
+#define LORA_MAX_RANK 64
+
+/* Table columns of a transformer layer, in this order. */
+#define LORA_NUM_MODULES 7
+enum {
+  LORA_Q = 0, LORA_K = 1, LORA_V = 2, LORA_O = 3,
+  LORA_GATE = 4, LORA_UP = 5, LORA_DOWN = 6
+};
+
+typedef enum lora_status {
+  LORA_OK = 0,
+  LORA_ERR_NULL = 1,       /* a required pointer is NULL                      */
+  LORA_ERR_SHAPE = 2,      /* a size or leading dimension is out of range     */
+  LORA_ERR_RANK = 3,       /* max_rank outside [1, LORA_MAX_RANK]             */
+  LORA_ERR_ALIGN = 4,      /* a pointer or leading dimension is not 16-byte
+                              aligned, or a dimension is not a multiple of 8  */
+  LORA_ERR_WORKSPACE = 5,  /* ws_bytes < lora_workspace_bytes(...)            */
+  LORA_ERR_MODULE = 6,     /* bad module index, n_mod or module mask          */
+  LORA_ERR_LAUNCH = 7      /* the HIP runtime refused a kernel launch         */
+} lora_status_t;
+
+/*
+ * One entry of the device-resident adapter table: the factors of one adapter
+ * for one projection ("m07 ...", "2. Scale Numbers" for the shapes).
+ * A table is an array of these indexed [slot * n_mod + module].
+ *   A      device, bf16 [rank][d_in], row-major, leading dimension d_in,
+ *          16-byte aligned.
+ *   B      device, bf16 [d_out][rank], row-major, leading dimension rank,
+ *          16-byte aligned (ranks that are not a multiple of 8 take a slower
+ *          element-wise path for B).
+ *   rank   0 .. max_rank; 0 means the projection is not targeted by this
+ *          adapter (zero delta, A and B not read).  A rank outside
+ *          [0, max_rank] is a device-data error.
+ *   scale  alpha / r of the forward y = Wx + (B.A)x(alpha/r) ("m07 ...",
+ *          "6. Deep Dive A"); 1.0f when the adapter gives no alpha.
+ * Slots can live anywhere (fixed-size pages of one pool, separate buffers):
+ * row ids index the table, not memory.  32 bytes.
+ */
+typedef struct lora_adapter_entry {
+  const void *A;
+  const void *B;
+  int32_t rank;
+  float scale;
+  int64_t reserved; /* set to 0 */
+} lora_adapter_entry_t;
+
+/*
+ * Segments: the rows of the batch grouped by adapter ("LoRA, quotas and noisy
+ * neighbours", "One weight read, many adapters").  All device int32 arrays,
+ * written by lora_build_segments and read by the other calls.
+ *   perm          [num_rows]      original row of each sorted position
+ *   seg_offsets   [num_rows + 1]  segment s = sorted positions
+ *                                 [seg_offsets[s], seg_offsets[s+1])
+ *   seg_adapter   [num_rows]      adapter slot of segment s
+ *   num_segments  [1]             number of segments
+ *   status        [1]             0, or the number of rows with an id
+ *                                 >= num_slots at the last build plus one per
+ *                                 (segment, projection) skipped since then
+ * Only the first num_segments (+1) entries are meaningful.
+ */
+typedef struct lora_segments {
+  int32_t *perm;
+  int32_t *seg_offsets;
+  int32_t *seg_adapter;
+  int32_t *num_segments;
+  int32_t *status;
+} lora_segments_t;
+
+/* One projection of a layer for lora_apply_layer. */
+typedef struct lora_module_io {
+  const void *x; /* device, bf16 [num_rows][ldx]: input of the projection   */
+  int64_t ldx;
+  void *y;       /* device, bf16 [num_rows][ldy]: base output W.x, updated  */
+  int64_t ldy;   /* in place                                                */
+  int32_t d_in;
+  int32_t d_out;
+} lora_module_io_t;
+
+/*
+ * Workspace (device scratch) that a call with these sizes needs, in bytes.
+ * sum_d_in is the sum of d_in over the projections the call will process:
+ * d_in for lora_shrink, 0 for lora_expand and lora_build_segments, the sum
+ * over the mask for the layer calls.  One workspace of the largest size serves every call
+ * on the same stream.  Returns 0 for invalid arguments.
+ */
+size_t lora_workspace_bytes(int32_t num_rows, int32_t num_slots,
+                            int32_t max_rank, int64_t sum_d_in);
+
+/*
+ * lora_build_segments -- group the rows of a batch by adapter.
+ * Source: "m07 ...", "6. Deep Dive A" (index vector mapping each sequence to
+ * an adapter slot); "LoRA, quotas and noisy neighbours", "One weight read,
+ * many adapters" (tag each row with its adapter and group); "12. Adapter
+ * Serving ...", "Scheduling with adapter awareness" (base-only requests form
+ * their own group).
+ *
+ *   row_adapter  device int32 [num_rows]: slot of each row; a negative id
+ *                means base only (the row joins no segment and its y is never
+ *                touched); an id >= num_slots is a device-data error (the row
+ *                is skipped and counted into *seg.status).
+ * Result: segments in ascending slot order, rows ascending inside a segment
+ * (a stable sort by id); *seg.status is reset to the number of bad ids.
+ * Errors: LORA_ERR_NULL (row_adapter with num_rows > 0, any seg pointer,
+ * ws), LORA_ERR_SHAPE (num_rows < 0, num_slots < 1), LORA_ERR_WORKSPACE.
+ */
+lora_status_t lora_build_segments(const int32_t *row_adapter, int32_t num_rows,
+                                  int32_t num_slots, lora_segments_t seg,
+                                  void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * lora_shrink -- v[b][j] = sum_k A_a[j][k] * x[b][k] for every row b in a
+ * segment, a its adapter, j < rank (the left factor of (B.A)x, "m07 ...",
+ * "6. Deep Dive A").  v is not scaled.
+ *
+ *   x       device bf16 [num_rows][ldx]
+ *   table   device lora_adapter_entry_t [num_slots * n_mod]; this call uses
+ *           column `module` (0 <= module < n_mod <= 7)
+ *   v       device float [num_rows][ldv]: for rows in a segment, columns
+ *           [0, rank) get the result and [rank, max_rank) get 0; other rows
+ *           are not written.  ldv >= max_rank, multiple of 4.
+ * Errors: LORA_ERR_NULL, LORA_ERR_SHAPE (num_rows < 0, d_in <= 0, ldx < d_in,
+ * ldv < max_rank, num_slots < 1), LORA_ERR_ALIGN, LORA_ERR_RANK,
+ * LORA_ERR_MODULE, LORA_ERR_WORKSPACE, LORA_ERR_LAUNCH.
+ */
+lora_status_t lora_shrink(const void *x, int64_t ldx, int32_t num_rows,
+                          int32_t d_in, const lora_adapter_entry_t *table,
+                          int32_t num_slots, int32_t n_mod, int32_t module,
+                          lora_segments_t seg, int32_t max_rank, float *v,
+                          int64_t ldv, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * lora_expand -- y[b][n] = bf16_rne( y[b][n] + scale_a * sum_j B_a[n][j] *
+ * v[b][j] ) for every row b in a segment (the right factor of (B.A)x and the
+ * sum with the shared base output, "m07 ...", "6. Deep Dive A").  The sum is
+ * accumulated in fp32 and rounded to bf16 once, round-to-nearest-even.
+ *
+ *   v       device float [num_rows][ldv], as written by lora_shrink
+ *           (columns [0, rank) are read)
+ *   y       device bf16 [num_rows][ldy], base output, updated in place; rows
+ *           in no segment are not touched.
+ * Errors: as lora_shrink, with d_out in place of d_in.
+ */
+lora_status_t lora_expand(const float *v, int64_t ldv, int32_t num_rows,
+                          int32_t d_out, const lora_adapter_entry_t *table,
+                          int32_t num_slots, int32_t n_mod, int32_t module,
+                          lora_segments_t seg, int32_t max_rank, void *y,
+                          int64_t ldy, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * lora_apply_layer -- the delta of every projection of one transformer layer
+ * whose bit is set in module_mask (bit m = table column m: q, k, v, o, gate,
+ * up, down), in one grouped shrink launch and one grouped expand launch.  The
+ * rank-r vectors stay in the workspace and never reach the caller.
+ * Projection shapes are the caller's (the 70B layer of "m07 ...",
+ * "2. Scale Numbers": q, o 8192->8192; k, v 8192->1024; gate, up
+ * 8192->28672; down 28672->8192).
+ *
+ *   io      host array lora_module_io_t[7]; entries outside the mask are
+ *           ignored.  Projections may share x (q, k and v do in a layer).
+ *   table   device lora_adapter_entry_t [num_slots * 7]
+ * Equivalent to lora_layer_shrink followed by lora_layer_expand with the
+ * same arguments.
+ * Errors: LORA_ERR_NULL, LORA_ERR_SHAPE, LORA_ERR_ALIGN, LORA_ERR_RANK,
+ * LORA_ERR_MODULE (mask 0 or above 0x7f), LORA_ERR_WORKSPACE,
+ * LORA_ERR_LAUNCH.
+ */
+lora_status_t lora_apply_layer(const lora_module_io_t *io, uint32_t module_mask,
+                               int32_t num_rows,
+                               const lora_adapter_entry_t *table,
+                               int32_t num_slots, lora_segments_t seg,
+                               int32_t max_rank, void *ws, size_t ws_bytes,
+                               void *stream);
+
+/*
+ * The two launches of lora_apply_layer, for callers that interleave other
+ * work or time them apart.  lora_layer_shrink leaves the rank-r partial sums
+ * in the workspace; lora_layer_expand, enqueued later on the same stream with
+ * the same arguments and workspace, consumes them.
+ */
+lora_status_t lora_layer_shrink(const lora_module_io_t *io, uint32_t module_mask,
+                                int32_t num_rows,
+                                const lora_adapter_entry_t *table,
+                                int32_t num_slots, lora_segments_t seg,
+                                int32_t max_rank, void *ws, size_t ws_bytes,
+                                void *stream);
+lora_status_t lora_layer_expand(const lora_module_io_t *io, uint32_t module_mask,
+                                int32_t num_rows,
+                                const lora_adapter_entry_t *table,
+                                int32_t num_slots, lora_segments_t seg,
+                                int32_t max_rank, void *ws, size_t ws_bytes,
+                                void *stream);
+
+/* A static, human-readable name for a status code. */
+const char *lora_status_string(lora_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_GEMV_H */

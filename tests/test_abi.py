@@ -1,0 +1,148 @@
+"""The C-ABI library loads, exports every function include/lora_gemv.h declares,
+and rejects bad host arguments with the documented status codes.
+
+Every call here fails validation, which runs before the first HIP call, so no
+device is touched (the pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import adapter_gemv_amd as lg
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "lora_gemv.h")
+OK, NULL, SHAPE, RANK, ALIGN, WS, MODULE, LAUNCH = range(8)
+P = 0x10000          # an aligned fake device address (never dereferenced)
+BIG = 1 << 40
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lora_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared()
+    assert {"lora_build_segments", "lora_shrink", "lora_expand", "lora_apply_layer"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", lg.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (lora_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    L = lg.lib()
+    for n in names:
+        getattr(L, n)
+
+
+def seg(**kw):
+    d = dict(perm=P, seg_offsets=P, seg_adapter=P, num_segments=P, status=P)
+    d.update(kw)
+    return lg._Seg(**d)
+
+
+def test_status_strings():
+    for c in range(8):
+        s = lg.status_string(c)
+        assert s.startswith("LORA_")
+    assert "unknown" in lg.status_string(99)
+
+
+def test_workspace_query():
+    L = lg.lib()
+    assert L.lora_workspace_bytes(128, 128, 64, 8192) > 0
+    assert L.lora_workspace_bytes(-1, 128, 64, 0) == 0
+    assert L.lora_workspace_bytes(128, 0, 64, 0) == 0
+    assert L.lora_workspace_bytes(128, 128, 0, 0) == 0
+    assert L.lora_workspace_bytes(128, 128, 65, 0) == 0
+    # grows with rows, rank and the projections' input sizes
+    assert L.lora_workspace_bytes(256, 128, 64, 8192) > L.lora_workspace_bytes(128, 128, 64, 8192)
+    assert L.lora_workspace_bytes(128, 128, 64, 65536) > L.lora_workspace_bytes(128, 128, 64, 8192)
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(seg=seg(perm=None)), NULL),
+    (dict(seg=seg(status=None)), NULL),
+    (dict(n=-1), SHAPE),
+    (dict(slots=0), SHAPE),
+    (dict(ids=None), NULL),
+    (dict(ws=None), NULL),
+    (dict(ws_bytes=0), WS),
+])
+def test_build_segments_rejects(args, code):
+    a = dict(ids=P, n=128, slots=16, seg=seg(), ws=P, ws_bytes=BIG)
+    a.update(args)
+    assert lg.lib().lora_build_segments(a["ids"], a["n"], a["slots"], a["seg"], a["ws"], a["ws_bytes"], None) == code
+
+
+SHRINK = dict(x=P, ldx=1024, n=64, d=1024, table=P, slots=8, n_mod=7, module=0, seg=seg(), max_rank=16, v=P, ldv=16,
+              ws=P, ws_bytes=BIG)
+
+
+@pytest.mark.parametrize("fn", ["lora_shrink", "lora_expand"])
+@pytest.mark.parametrize("args,code", [
+    (dict(x=None), NULL), (dict(table=None), NULL), (dict(v=None), NULL), (dict(ws=None), NULL),
+    (dict(seg=seg(seg_adapter=None)), NULL),
+    (dict(n_mod=0), MODULE), (dict(n_mod=8), MODULE), (dict(module=7), MODULE), (dict(module=-1), MODULE),
+    (dict(max_rank=0), RANK), (dict(max_rank=65), RANK),
+    (dict(n=-1), SHAPE), (dict(slots=0), SHAPE), (dict(d=0), SHAPE), (dict(ldx=1016), SHAPE), (dict(ldv=8), SHAPE),
+    (dict(d=1020, ldx=1024), ALIGN), (dict(ldx=1028), ALIGN), (dict(x=P + 8), ALIGN), (dict(v=P + 4), ALIGN),
+    (dict(ldv=18), ALIGN),
+    (dict(ws_bytes=16), WS),
+])
+def test_shrink_expand_reject(fn, args, code):
+    a = dict(SHRINK)
+    a.update(args)
+    L = lg.lib()
+    if fn == "lora_shrink":
+        r = L.lora_shrink(a["x"], a["ldx"], a["n"], a["d"], a["table"], a["slots"], a["n_mod"], a["module"], a["seg"],
+                          a["max_rank"], a["v"], a["ldv"], a["ws"], a["ws_bytes"], None)
+    else:  # same roles: v in, x plays y
+        r = L.lora_expand(a["v"], a["ldv"], a["n"], a["d"], a["table"], a["slots"], a["n_mod"], a["module"], a["seg"],
+                          a["max_rank"], a["x"], a["ldx"], a["ws"], a["ws_bytes"], None)
+    assert r == code
+
+
+def ios(**over):
+    arr = (lg._IO * 7)()
+    for i in range(7):
+        arr[i] = lg._IO(P, 8192, P, 8192, 8192, 8192)
+    for k, v in over.items():
+        i, field = k.split("_", 1)
+        setattr(arr[int(i)], field, v)
+    return arr
+
+
+@pytest.mark.parametrize("fn", ["lora_apply_layer", "lora_layer_shrink", "lora_layer_expand"])
+@pytest.mark.parametrize("args,code", [
+    (dict(io=None), NULL), (dict(table=None), NULL), (dict(ws=None), NULL), (dict(seg=seg(num_segments=None)), NULL),
+    (dict(mask=0), MODULE), (dict(mask=0x80), MODULE),
+    (dict(n=-1), SHAPE), (dict(slots=0), SHAPE),
+    (dict(max_rank=0), RANK), (dict(max_rank=100), RANK),
+    (dict(io=ios(**{"3_x": None})), NULL), (dict(io=ios(**{"0_y": None})), NULL),
+    (dict(io=ios(**{"2_d_out": 0})), SHAPE), (dict(io=ios(**{"1_ldy": 4096})), SHAPE),
+    (dict(io=ios(**{"6_d_in": 1004, "6_ldx": 1008})), ALIGN), (dict(io=ios(**{"4_y": P + 2})), ALIGN),
+    (dict(ws_bytes=1024), WS),
+])
+def test_layer_rejects(fn, args, code):
+    a = dict(io=ios(), mask=0x7F, n=128, table=P, slots=128, seg=seg(), max_rank=64, ws=P, ws_bytes=BIG)
+    a.update(args)
+    f = getattr(lg.lib(), fn)
+    assert f(a["io"], a["mask"], a["n"], a["table"], a["slots"], a["seg"], a["max_rank"], a["ws"], a["ws_bytes"],
+             None) == code
+
+
+def test_masked_out_modules_are_not_checked():
+    # an invalid projection outside the mask is ignored; the call then fails
+    # only at the (too small) workspace check
+    a = ios(**{"5_x": None, "5_d_in": 3})
+    r = lg.lib().lora_apply_layer(a, 0x01, 128, P, 128, seg(), 64, P, 16, None)
+    assert r == WS
+
+
+def test_python_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    s = lg.Segments.__new__(lg.Segments)
+    with pytest.raises((TypeError, ValueError)):
+        lg.build_segments(torch.zeros(4, dtype=torch.int32), 4, s, torch.zeros(16, dtype=torch.uint8))

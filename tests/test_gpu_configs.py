@@ -1,0 +1,56 @@
+"""GPU parity on the five seeded workloads at their full sizes.
+
+Rows are compared element by element with the oracle: every row where the
+oracle finishes in seconds (decode workloads), and for prefill the first,
+middle and last row of every segment of both projections.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests.parity import bf16_host, check_rows, note
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import adapter_gemv_amd as lg  # noqa: E402,F401
+from workloads.device import DeviceWorkload  # noqa: E402
+
+
+def sample_rows(w):
+    if w.seq_lens is None:
+        return None
+    starts = np.concatenate([[0], np.cumsum(w.seq_lens)[:-1]])
+    rows = np.concatenate([starts, starts + w.seq_lens // 2, starts + w.seq_lens - 1])
+    return np.unique(rows).astype(np.int32)
+
+
+@pytest.mark.parametrize("name", ["tiny", "q_proj_r16", "full_layer_r64", "zipf_paged", "prefill_r16", "prefill_r64"])
+def test_workload_full_size(name):
+    note(f"workload {name}: generate")
+    w = gen.make_workload(name)
+    rows = sample_rows(w)
+    ref = oracle.lora_layer(w, rows=rows)
+    note(f"workload {name}: {w.num_rows} rows, {w.num_slots} slots, modules {[m.name for m in w.modules]}")
+    dw = DeviceWorkload(w)
+    # delta alone
+    dw.reset_y(zero=True)
+    dw.step()
+    torch.cuda.synchronize()
+    sel = slice(None) if rows is None else rows
+    for m in w.modules:
+        check_rows(bf16_host(dw.y[m.name])[sel], ref[m.name].delta, f"{name}/{m.name} delta")
+    # onto the base output
+    dw.reset_y()
+    dw.step()
+    torch.cuda.synchronize()
+    for m in w.modules:
+        check_rows(bf16_host(dw.y[m.name])[sel], ref[m.name].y, f"{name}/{m.name} y")
+    _, offs, adap, status = dw.seg.host()
+    seg_ref = oracle.build_segments(w.ids, w.num_slots)
+    assert np.array_equal(offs, seg_ref.seg_offsets) and np.array_equal(adap, seg_ref.seg_adapter)
+    assert status == 0
