@@ -17,7 +17,7 @@ lora_status_t check_segments(const lora_segments_t &seg) {
   return LORA_OK;
 }
 
-size_t ws_need(int num_rows, int num_slots, int max_rank, int64_t sum_d_in) {
+size_t ws_need(int num_rows, int num_slots, int max_rank, int64_t sum_d_in) {  // covers every call
   const size_t a = segments_ws_bytes(num_rows, num_slots);
   const size_t b = partials_ws_bytes(num_rows, max_rank, sum_d_in);
   return a > b ? a : b;
@@ -26,12 +26,11 @@ size_t ws_need(int num_rows, int num_slots, int max_rank, int64_t sum_d_in) {
 // Work decomposition: the n-tile of the expand (the shrink k-chunk is
 // kKChunkMin).
 int pick_nt(int max_rank) {
-  // One expand item streams 16 loads of 16 bytes per lane; an n-tile of
-  // that many outputs at the table's largest rank, at least 1024.
+  // One load pass of the expand is 16 loads of 16 bytes per lane (64 KiB
+  // per block) at the table's largest rank; an item streams four passes.
   int cls = max_rank <= 8 ? 8 : max_rank <= 16 ? 16 : max_rank <= 32 ? 32 : 64;
   int lpr = cls / 8;
-  int sub = 16 * kDecodeThreads / lpr;
-  return sub < 1024 ? 1024 : sub;
+  return 4 * 16 * kDecodeThreads / lpr;
 }
 
 struct ModuleArgs {
@@ -46,13 +45,21 @@ struct ModuleArgs {
 
 // Fill the descriptor for a set of modules; items are k-chunks (shrink) or
 // n-tiles (expand).
-void fill_desc(LayerDesc &d, const ModuleArgs *ms, int n, bool shrink_items, int num_rows, int num_slots,
-               int max_rank, int table_cols, const lora_adapter_entry_t *table, const lora_segments_t &seg,
-               void *ws) {
+lora_status_t launched(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_ERR_LAUNCH; }
+
+// Shrink k-chunk: small for decode batches (parallelism over few rows),
+// larger for prefill-sized batches (fewer partials to write and sum).
+int pick_kc(int num_rows) { return num_rows >= kPrefillRows ? 2 * kKChunkMin : kKChunkMin; }
+
+// Fill the descriptor: items per segment are k-chunks (shrink) or decode
+// n-tiles (expand); sg_* give the SGMV expand n-tiles per row tile.
+void fill_desc(LayerDesc &d, const ModuleArgs *ms, int n, bool shrink, int num_rows, int num_slots, int max_rank,
+               int table_cols, const lora_adapter_entry_t *table, const lora_segments_t &seg, void *ws) {
   d = LayerDesc{};
-  d.kc = kKChunkMin;
+  d.kc = pick_kc(num_rows);
   d.nt = pick_nt(max_rank);
-  int item = 0, chunk = 0;
+  d.sg_nt = kSgmvExpandCols;
+  int item = 0, chunk = 0, sg = 0;
   for (int i = 0; i < n; ++i) {
     ModuleDesc &m = d.mod[i];
     m.x = static_cast<const uint16_t *>(ms[i].x);
@@ -65,17 +72,22 @@ void fill_desc(LayerDesc &d, const ModuleArgs *ms, int n, bool shrink_items, int
     m.n_chunks = m.d_in > 0 ? (m.d_in + d.kc - 1) / d.kc : 0;
     m.part_base = chunk;
     chunk += m.n_chunks;
-    m.n_items = shrink_items ? m.n_chunks : (m.d_out + d.nt - 1) / d.nt;
+    m.n_items = shrink ? m.n_chunks : (m.d_out + d.nt - 1) / d.nt;
     m.item_base = item;
     item += m.n_items;
+    m.sg_n_items = (m.d_out + d.sg_nt - 1) / d.sg_nt;
+    m.sg_item_base = sg;
+    sg += m.sg_n_items;
   }
   d.n_active = n;
   d.items_per_seg = item;
+  d.sg_items = sg;
   d.table_cols = table_cols;
   d.rs = partial_row_stride(max_rank);
   d.num_rows = num_rows;
   d.num_slots = num_slots;
   d.max_rank = max_rank;
+  d.long_min = num_rows >= kLongSegRows ? kLongSegRows : 0x7fffffff;
   d.perm = seg.perm;
   d.seg_offsets = seg.seg_offsets;
   d.seg_adapter = seg.seg_adapter;
@@ -85,19 +97,35 @@ void fill_desc(LayerDesc &d, const ModuleArgs *ms, int n, bool shrink_items, int
   d.part = static_cast<float *>(ws);
 }
 
-int grid_for(const LayerDesc &d, int num_rows, int num_slots) {
-  const int64_t max_seg = num_rows < num_slots ? num_rows : num_slots;
-  const int64_t g = max_seg * d.items_per_seg;
-  return g > 0x7fffffff ? -1 : (int)g;
-}
+// The SGMV kernels address an activation matrix with 32-bit byte offsets.
+bool fits_u32(int64_t rows, int64_t ld) { return rows * ld * 2 <= (int64_t)0xFFFFFF00; }
 
-lora_status_t launched(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_ERR_LAUNCH; }
+// Launch one phase (shrink or expand) over every module: decode items for
+// every possible segment, then SGMV items for every row tile that segments
+// of at least kLongSegRows rows can produce.
+lora_status_t launch_phase(bool shrink, const ModuleArgs *ms, int n, int num_rows, int num_slots, int max_rank,
+                           int table_cols, const lora_adapter_entry_t *table, const lora_segments_t &seg, void *ws,
+                           const float *v_in, int64_t ldv, hipStream_t s) {
+  LayerDesc d;
+  fill_desc(d, ms, n, shrink, num_rows, num_slots, max_rank, table_cols, table, seg, ws);
+  d.v = v_in;
+  d.ldv = ldv;
+  const int64_t max_seg = num_rows < num_slots ? num_rows : num_slots;
+  const int64_t dec = max_seg * d.items_per_seg;
+  int64_t sg = 0;
+  if (num_rows >= kLongSegRows)
+    sg = (int64_t)long_tiles_max(num_rows, num_slots, shrink ? sgmv_shrink_rows() : sgmv_expand_rows()) *
+         (shrink ? d.items_per_seg : d.sg_items);
+  if (dec + sg > 0x7fffffff) return LORA_ERR_SHAPE;
+  const hipError_t e = shrink ? launch_shrink(d, (int)dec, (int)(dec + sg), s) : launch_expand(d, (int)dec, (int)(dec + sg), s);
+  return launched(e);
+}
 
 // Common checks of the layer calls; fills the module list.
 lora_status_t check_layer(const lora_module_io_t *io, uint32_t module_mask, int32_t num_rows,
                           const lora_adapter_entry_t *table, int32_t num_slots, const lora_segments_t &seg,
                           int32_t max_rank, void *ws, size_t ws_bytes, ModuleArgs *ms, int *n_out) {
-  if (!io || !table || !ws) return LORA_ERR_NULL;
+  if (!io || !table) return LORA_ERR_NULL;
   lora_status_t st = check_segments(seg);
   if (st != LORA_OK) return st;
   if (module_mask == 0 || module_mask >= (1u << LORA_NUM_MODULES)) return LORA_ERR_MODULE;
@@ -112,11 +140,14 @@ lora_status_t check_layer(const lora_module_io_t *io, uint32_t module_mask, int3
     if (m.d_in <= 0 || m.d_out <= 0 || m.ldx < m.d_in || m.ldy < m.d_out) return LORA_ERR_SHAPE;
     if ((m.d_in & 7) || (m.d_out & 7) || (m.ldx & 7) || (m.ldy & 7) || !aligned16(m.x) || !aligned16(m.y))
       return LORA_ERR_ALIGN;
+    if (!fits_u32(num_rows, m.ldx) || !fits_u32(num_rows, m.ldy)) return LORA_ERR_SHAPE;
     ms[n] = ModuleArgs{m.x, m.ldx, m.y, m.ldy, m.d_in, m.d_out, c};
     sum_d_in += m.d_in;
     ++n;
   }
-  if (ws_bytes < ws_need(num_rows, num_slots, max_rank, sum_d_in)) return LORA_ERR_WORKSPACE;
+  const size_t need = partials_ws_bytes(num_rows, max_rank, sum_d_in);
+  if (need > 0 && !ws) return LORA_ERR_NULL;
+  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
   *n_out = n;
   return LORA_OK;
 }
@@ -130,20 +161,12 @@ lora_status_t layer_phase(bool do_shrink, bool do_expand, const lora_module_io_t
   if (st != LORA_OK) return st;
   if (num_rows == 0) return LORA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  LayerDesc d;
   if (do_shrink) {
-    fill_desc(d, ms, n, true, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws);
-    const int g = grid_for(d, num_rows, num_slots);
-    if (g < 0) return LORA_ERR_SHAPE;
-    st = launched(launch_decode_shrink(d, g, s));
+    st = launch_phase(true, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
     if (st != LORA_OK) return st;
   }
-  if (do_expand) {
-    fill_desc(d, ms, n, false, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws);
-    const int g = grid_for(d, num_rows, num_slots);
-    if (g < 0) return LORA_ERR_SHAPE;
-    st = launched(launch_decode_expand(d, g, s));
-  }
+  if (do_expand)
+    st = launch_phase(false, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
   return st;
 }
 
@@ -176,8 +199,9 @@ lora_status_t lora_build_segments(const int32_t *row_adapter, int32_t num_rows, 
   if (st != LORA_OK) return st;
   if (num_rows < 0 || num_slots < 1) return LORA_ERR_SHAPE;
   if (num_rows > 0 && !row_adapter) return LORA_ERR_NULL;
-  if (!ws) return LORA_ERR_NULL;
-  if (ws_bytes < segments_ws_bytes(num_rows, num_slots)) return LORA_ERR_WORKSPACE;
+  const size_t need = segments_ws_bytes(num_rows, num_slots);
+  if (need > 0 && !ws) return LORA_ERR_NULL;
+  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
   return launched(launch_build_segments(row_adapter, num_rows, num_slots, seg, ws, static_cast<hipStream_t>(stream)));
 }
 
@@ -185,25 +209,26 @@ lora_status_t lora_shrink(const void *x, int64_t ldx, int32_t num_rows, int32_t 
                           const lora_adapter_entry_t *table, int32_t num_slots, int32_t n_mod, int32_t module,
                           lora_segments_t seg, int32_t max_rank, float *v, int64_t ldv, void *ws, size_t ws_bytes,
                           void *stream) {
-  if (!x || !table || !v || !ws) return LORA_ERR_NULL;
+  if (!x || !table || !v) return LORA_ERR_NULL;
   lora_status_t st = check_segments(seg);
   if (st != LORA_OK) return st;
   if (n_mod < 1 || n_mod > LORA_NUM_MODULES || module < 0 || module >= n_mod) return LORA_ERR_MODULE;
   if (max_rank < 1 || max_rank > LORA_MAX_RANK) return LORA_ERR_RANK;
   if (num_rows < 0 || num_slots < 1 || d_in <= 0 || ldx < d_in || ldv < max_rank) return LORA_ERR_SHAPE;
   if ((d_in & 7) || (ldx & 7) || (ldv & 3) || !aligned16(x) || !aligned16(v)) return LORA_ERR_ALIGN;
-  if (ws_bytes < ws_need(num_rows, num_slots, max_rank, d_in)) return LORA_ERR_WORKSPACE;
+  if (!fits_u32(num_rows, ldx)) return LORA_ERR_SHAPE;
+  const size_t need = partials_ws_bytes(num_rows, max_rank, d_in);
+  if (need > 0 && !ws) return LORA_ERR_NULL;
+  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
   if (num_rows == 0) return LORA_OK;
   ModuleArgs m{x, ldx, nullptr, 0, d_in, 0, module};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launch_phase(true, &m, 1, num_rows, num_slots, max_rank, n_mod, table, seg, ws, nullptr, 0, s);
+  if (st != LORA_OK) return st;
   LayerDesc d;
   fill_desc(d, &m, 1, true, num_rows, num_slots, max_rank, n_mod, table, seg, ws);
   d.v_out = v;
   d.ldv = ldv;
-  const int g = grid_for(d, num_rows, num_slots);
-  if (g < 0) return LORA_ERR_SHAPE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  st = launched(launch_decode_shrink(d, g, s));
-  if (st != LORA_OK) return st;
   return launched(launch_shrink_reduce(d, s));
 }
 
@@ -211,23 +236,20 @@ lora_status_t lora_expand(const float *v, int64_t ldv, int32_t num_rows, int32_t
                           const lora_adapter_entry_t *table, int32_t num_slots, int32_t n_mod, int32_t module,
                           lora_segments_t seg, int32_t max_rank, void *y, int64_t ldy, void *ws, size_t ws_bytes,
                           void *stream) {
-  if (!v || !table || !y || !ws) return LORA_ERR_NULL;
+  if (!v || !table || !y) return LORA_ERR_NULL;
   lora_status_t st = check_segments(seg);
   if (st != LORA_OK) return st;
   if (n_mod < 1 || n_mod > LORA_NUM_MODULES || module < 0 || module >= n_mod) return LORA_ERR_MODULE;
   if (max_rank < 1 || max_rank > LORA_MAX_RANK) return LORA_ERR_RANK;
   if (num_rows < 0 || num_slots < 1 || d_out <= 0 || ldy < d_out || ldv < max_rank) return LORA_ERR_SHAPE;
   if ((d_out & 7) || (ldy & 7) || (ldv & 3) || !aligned16(y) || !aligned16(v)) return LORA_ERR_ALIGN;
-  if (ws_bytes < ws_need(num_rows, num_slots, max_rank, 0)) return LORA_ERR_WORKSPACE;
+  if (!fits_u32(num_rows, ldy)) return LORA_ERR_SHAPE;
+  (void)ws;
+  (void)ws_bytes;  // the expand of a caller-provided v needs no workspace
   if (num_rows == 0) return LORA_OK;
   ModuleArgs m{nullptr, 0, y, ldy, 0, d_out, module};
-  LayerDesc d;
-  fill_desc(d, &m, 1, false, num_rows, num_slots, max_rank, n_mod, table, seg, ws);
-  d.v = v;
-  d.ldv = ldv;
-  const int g = grid_for(d, num_rows, num_slots);
-  if (g < 0) return LORA_ERR_SHAPE;
-  return launched(launch_decode_expand(d, g, static_cast<hipStream_t>(stream)));
+  return launch_phase(false, &m, 1, num_rows, num_slots, max_rank, n_mod, table, seg, ws, v, ldv,
+                      static_cast<hipStream_t>(stream));
 }
 
 lora_status_t lora_layer_shrink(const lora_module_io_t *io, uint32_t module_mask, int32_t num_rows,

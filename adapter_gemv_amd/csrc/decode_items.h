@@ -1,0 +1,299 @@
+// Decode (BGMV-style) work items: segments shorter than kLongSegRows rows.
+//
+// "m07 -- Multi-Adapter (LoRA) Serving", "6. Deep Dive A": one batched kernel
+// gathers each sequence's adapter through the index vector and applies it
+// without materialising per-sequence weights; the cost is bandwidth, since
+// each distinct adapter in the batch is read once per step.
+// "LoRA, quotas and noisy neighbours", "One weight read, many adapters": the
+// update is applied in registers.
+//
+// Items are (segment, projection, k-chunk) for the shrink and (segment,
+// projection, n-tile) for the expand; a 256-thread block takes one item, and
+// a segment's rows share every load of its adapter's factors.
+//
+// Shrink  v = A.x: rows of A are spread over the 4 waves; each lane streams 8
+//   consecutive k (16 bytes) of every A row and of each x row, so one wave
+//   load covers 1 KiB of contiguous memory.  bf16 pairs meet in
+//   v_dot2_f32_bf16 (exact products, fp32 sums).  The per-lane sums are
+//   reduced across the wave by a reduce-scatter butterfly that leaves every
+//   sum on one lane; the block writes its k-chunk's partial v to the
+//   workspace (fixed order, no atomics: results are bit-reproducible).
+// Expand  y += scale * B.v: the item sums the k-chunk partials of its rows
+//   into LDS (times scale) and streams its tile of B, which is contiguous
+//   because B is [d_out][ldb] row-major: LPR = rank/8 lanes share an output
+//   row and each lane loads 16 bytes.  v (fp32) is split once per row into
+//   bf16 hi + lo, so the products with B run on v_dot2_f32_bf16 without
+//   converting B.  A reduce-scatter over the LPR lanes finishes the dot
+//   products, and the owning lane reads y, adds, rounds to bf16 (RNE) and
+//   writes it back.  Each (row, output) has one writer.
+#pragma once
+
+#include "device_common.h"
+
+namespace lora {
+
+// ---------------------------------------------------------------- shrink --
+
+// Wave w owns rows [w*jw, w*jw + jw) of A with jw = ceil(rank / 4) <= JW, so
+// all waves share the stream whatever the entry's rank.  RG rows of x are
+// processed together.
+template <int JW, int RG>
+__device__ __forceinline__ void decode_shrink_rows(const LayerDesc &d, const ModuleDesc &m,
+                                                   const uint16_t *__restrict__ A, int rank, int jw, int pos0,
+                                                   int nrows, int chunk) {
+  const int lane = threadIdx.x & 63;
+  const int j0 = wave_id() * jw;
+  const int k_begin = chunk * d.kc;
+  const int k_end = min(k_begin + d.kc, m.d_in);
+  const uint32_t row_bytes = (uint32_t)m.d_in * 2;
+  rsrc_t rx[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) {
+    const int b = r < nrows ? uniform(d.perm[pos0 + r]) : 0;
+    const bool ok = (unsigned)b < (unsigned)d.num_rows;  // a stray index reads zeros
+    rx[r] = make_rsrc(m.x + (int64_t)(ok ? b : 0) * m.ldx, ok ? row_bytes : 0u);
+  }
+  const rsrc_t ra = make_rsrc(A, (uint32_t)rank * row_bytes);
+  float acc[JW * RG];
+#pragma unroll
+  for (int i = 0; i < JW * RG; ++i) acc[i] = 0.f;
+  for (int k = k_begin + lane * 8; k < k_end; k += 512) {
+    const uint32_t voff = (uint32_t)k * 2;
+    u32x4 xv[RG], av[JW];
+#pragma unroll
+    for (int r = 0; r < RG; ++r) xv[r] = r < nrows ? buf_ld16(rx[r], voff, 0) : zero4();
+#pragma unroll
+    for (int jj = 0; jj < JW; ++jj)
+      av[jj] = (jj < jw && j0 + jj < rank) ? buf_ld16_stream(ra, voff, (uint32_t)(j0 + jj) * row_bytes) : zero4();
+#pragma unroll
+    for (int jj = 0; jj < JW; ++jj)
+#pragma unroll
+      for (int r = 0; r < RG; ++r) acc[jj * RG + r] = dot8_bf16(av[jj], xv[r], acc[jj * RG + r]);
+  }
+  reduce_scatter<JW * RG, 64>(acc);
+  float *out = d.part + ((int64_t)(m.part_base + chunk) * d.num_rows + pos0) * d.rs;
+  constexpr int NV = JW * RG;
+  if constexpr (NV >= 64) {
+#pragma unroll
+    for (int i = 0; i < NV / 64; ++i) {
+      const int idx = i + (NV / 64) * lane;
+      const int jj = idx / RG, r = idx % RG;
+      if (r < nrows && jj < jw && j0 + jj < rank) out[(int64_t)r * d.rs + j0 + jj] = acc[i];
+    }
+  } else {
+    constexpr int GS = 64 / NV;
+    if (lane % GS == 0) {
+      const int idx = lane / GS;
+      const int jj = idx / RG, r = idx % RG;
+      if (r < nrows && jj < jw && j0 + jj < rank) out[(int64_t)r * d.rs + j0 + jj] = acc[0];
+    }
+  }
+}
+
+// Block `blk` of the decode shrink numbering.  JW = rows of A per wave at the
+// largest rank of the launch (4*JW).
+template <int JW>
+__device__ __forceinline__ void decode_shrink_block(const LayerDesc &d, int blk) {
+  constexpr int RGM = JW >= 16 ? 2 : 4;  // rows of x per pass for multi-row segments
+  const int s = blk / d.items_per_seg;
+  if (s >= uniform(*d.num_segments)) return;
+  const int it = blk - s * d.items_per_seg;
+  const ModuleDesc m = module_of_item(d, it);
+  const int chunk = it - m.item_base;
+  int a, pos0, len;
+  if (!load_segment(d, s, it == 0, &a, &pos0, &len)) return;
+  if (len >= d.long_min) return;  // an SGMV item takes this segment
+  lora_adapter_entry_t e;
+  if (!load_entry(d, a, m.col, chunk == 0, &e)) return;
+  const uint16_t *A = static_cast<const uint16_t *>(e.A);
+  const int rank = e.rank;
+  const int jw = (rank + 3) >> 2;
+  if (len == 1) {
+    decode_shrink_rows<JW, 1>(d, m, A, rank, jw, pos0, 1, chunk);
+  } else {
+    for (int r0 = 0; r0 < len; r0 += RGM)
+      decode_shrink_rows<JW, RGM>(d, m, A, rank, jw, pos0 + r0, min(RGM, len - r0), chunk);
+  }
+}
+
+// ---------------------------------------------------------------- expand --
+
+// Row stride of B: the rank rounded up to a multiple of 8, so every row is
+// 16-byte aligned.  Columns in [rank, ldb) are padding with finite values;
+// they meet zeros of v and add nothing.
+__device__ __forceinline__ int b_stride(int rank) { return (rank + 7) & ~7; }
+
+// Eight elements B[n][jq .. jq+8) of a B tile, zero for lanes past the rank
+// and rows past the tile.
+__device__ __forceinline__ u32x4 load_b8(rsrc_t rb, int n, int ldb, int rank, int jq) {
+  return buf_ld16_stream(rb, jq < rank ? ((uint32_t)n * ldb + jq) * 2 : kOutOfRange, 0);
+}
+
+// Sum of the k-chunk partials of row p (sorted position), column j.
+__device__ __forceinline__ float partial_sum(const LayerDesc &d, const ModuleDesc &m, int p, int j) {
+  if (d.v != nullptr) {
+    const int b = d.perm[p];
+    return (unsigned)b < (unsigned)d.num_rows ? d.v[(int64_t)b * d.ldv + j] : 0.f;
+  }
+  float sum = 0.f;
+  for (int c = 0; c < m.n_chunks; ++c) sum += d.part[((int64_t)(m.part_base + c) * d.num_rows + p) * d.rs + j];
+  return sum;
+}
+
+// One n-tile of one projection for every row of a multi-row segment.  The B
+// tile is loaded once and kept in registers across the rows; y of a few rows
+// is requested together.
+template <int LPR>
+__device__ __forceinline__ void decode_expand_rows(const LayerDesc &d, const ModuleDesc &m,
+                                                   const uint16_t *__restrict__ B, int rank, float scale, int pos0,
+                                                   int len, int tile, float *v_lds) {
+  constexpr int G = kDecodeThreads / LPR;  // output rows per load pass of the block
+  constexpr int P = 16;                    // load passes per sub-tile
+  constexpr int SUB = P * G;               // outputs per sub-tile
+  constexpr int PL = P / LPR;              // outputs per lane per row after the reduce-scatter
+  constexpr int YR = PL <= 4 ? 4 : 1;      // rows whose y is requested together
+  const int t = threadIdx.x, g = t / LPR, q = t % LPR, jq = q * 8;
+  const int n_tile0 = tile * d.nt;
+  const int n_tile1 = min(n_tile0 + d.nt, m.d_out);
+  const uint32_t tile_len = (uint32_t)(n_tile1 - n_tile0);
+  const int ldb = b_stride(rank);
+  const rsrc_t rb = make_rsrc(B + (int64_t)n_tile0 * ldb, tile_len * ldb * 2);  // past the tile: zero
+  auto y_rsrc = [&](int i) {
+    const int b = i < len ? uniform(d.perm[pos0 + i]) : -1;
+    const bool ok = (unsigned)b < (unsigned)d.num_rows;  // a stray index touches nothing
+    return make_rsrc(m.y + (int64_t)(ok ? b : 0) * m.ldy + n_tile0, ok ? tile_len * 2 : 0u);
+  };
+  for (int n0 = 0; n0 < (int)tile_len; n0 += SUB) {
+    u32x4 bv[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) bv[p] = load_b8(rb, n0 + p * G + g, ldb, rank, jq);
+    for (int r0 = 0; r0 < len; r0 += kExpandRowGroup) {
+      const int nr = min(kExpandRowGroup, len - r0);
+      __syncthreads();
+      for (int idx = t; idx < nr * 64; idx += kDecodeThreads) {
+        const int i = idx >> 6, j = idx & 63;
+        v_lds[idx] = j < rank ? partial_sum(d, m, pos0 + r0 + i, j) * scale : 0.f;
+      }
+      __syncthreads();
+      for (int i0 = 0; i0 < nr; i0 += YR) {
+        rsrc_t ry[YR];
+        uint16_t yv[YR][PL];
+#pragma unroll
+        for (int u = 0; u < YR; ++u) {
+          ry[u] = y_rsrc(r0 + i0 + u < r0 + nr ? r0 + i0 + u : len);
+#pragma unroll
+          for (int ii = 0; ii < PL; ++ii) yv[u][ii] = buf_ld_u16(ry[u], (uint32_t)(n0 + (ii + PL * q) * G + g) * 2);
+        }
+#pragma unroll
+        for (int u = 0; u < YR; ++u) {
+          const int i = i0 + u;
+          if (i >= nr) break;
+            float vv[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) vv[k] = v_lds[i * 64 + jq + k];
+          const V8Split vs = split_v8(vv);
+          float acc[P];
+#pragma unroll
+          for (int p = 0; p < P; ++p) acc[p] = dot8_bf16_split(bv[p], vs, 0.f);
+          reduce_scatter<P, LPR>(acc);
+#pragma unroll
+          for (int ii = 0; ii < PL; ++ii) {
+            const uint32_t off = (uint32_t)(n0 + (ii + PL * q) * G + g) * 2;
+            buf_st_u16(ry[u], off, f32_to_bf16(bf16_to_f32(yv[u][ii]) + acc[ii]));
+          }
+        }
+      }
+    }
+  }
+}
+
+// The same for a segment of one row (every decode row with its own adapter),
+// streamed: the item covers several
+// sub-tiles of B and each register of the tile is refilled with the next
+// sub-tile's data as soon as its dot product is taken, so 16 loads per lane
+// stay in flight for the whole item.  A load's offset is the lane's offset
+// inside a pass plus a per-pass constant; the sub-tile base goes in the
+// scalar offset.  Lanes past the rank or the tile get an out-of-range lane
+// offset and read zero.
+template <int LPR>
+__device__ __forceinline__ void decode_expand_one_row(const LayerDesc &d, const ModuleDesc &m,
+                                                      const uint16_t *__restrict__ B, int rank, float scale, int pos0,
+                                                      int tile, float *v_lds) {
+  constexpr int G = kDecodeThreads / LPR;
+  constexpr int P = 16;
+  constexpr int SUB = P * G;
+  constexpr int PL = P / LPR;
+  const int t = threadIdx.x, g = t / LPR, q = t % LPR, jq = q * 8;
+  const int n_tile0 = tile * d.nt;
+  const int n_tile1 = min(n_tile0 + d.nt, m.d_out);
+  const int tile_len = n_tile1 - n_tile0;
+  const int nsub = (tile_len + SUB - 1) / SUB;
+  const int ldb = b_stride(rank);
+  const rsrc_t rb = make_rsrc(B + (int64_t)n_tile0 * ldb, (uint32_t)tile_len * ldb * 2);
+  const uint32_t lane_off = (uint32_t)(g * ldb + jq) * 2;
+  const uint32_t pass_bytes = (uint32_t)G * ldb * 2;
+  const bool lane_on = jq < rank;
+  auto b_load = [&](int n0, int p) {  // past the tile (also past the last sub-tile) reads zero
+    const bool on = lane_on && n0 + p * G + g < tile_len;
+    return buf_ld16_stream(rb, on ? lane_off + p * pass_bytes : kOutOfRange, (uint32_t)n0 * ldb * 2);
+  };
+  const int b = uniform(d.perm[pos0]);
+  const bool row_ok = (unsigned)b < (unsigned)d.num_rows;
+  const rsrc_t ry = make_rsrc(m.y + (int64_t)(row_ok ? b : 0) * m.ldy + n_tile0, row_ok ? (uint32_t)tile_len * 2 : 0u);
+  auto y_off = [&](int n0, int ii) {
+    const int n = n0 + (ii + PL * q) * G + g;
+    return n < tile_len ? (uint32_t)n * 2 : kOutOfRange;
+  };
+  u32x4 bv[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) bv[p] = b_load(0, p);
+  uint16_t yv[PL];
+#pragma unroll
+  for (int ii = 0; ii < PL; ++ii) yv[ii] = buf_ld_u16(ry, y_off(0, ii));
+  if (t < 64) v_lds[t] = t < rank ? partial_sum(d, m, pos0, t) * scale : 0.f;
+  __syncthreads();
+  float vv[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) vv[k] = v_lds[jq + k];
+  const V8Split vs = split_v8(vv);
+  for (int st = 0; st < nsub; ++st) {
+    const int n0 = st * SUB;
+    float acc[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      acc[p] = dot8_bf16_split(bv[p], vs, 0.f);
+      bv[p] = b_load(n0 + SUB, p);  // unconditional: a branch here would copy the tile registers
+    }
+    uint16_t ynext[PL];
+#pragma unroll
+    for (int ii = 0; ii < PL; ++ii) ynext[ii] = buf_ld_u16(ry, y_off(n0 + SUB, ii));
+    reduce_scatter<P, LPR>(acc);
+#pragma unroll
+    for (int ii = 0; ii < PL; ++ii) {
+      buf_st_u16(ry, y_off(n0, ii), f32_to_bf16(bf16_to_f32(yv[ii]) + acc[ii]));
+      yv[ii] = ynext[ii];
+    }
+  }
+}
+
+// Block `blk` of the decode expand numbering.  LPR = lanes per output row at
+// the largest rank of the launch (8*LPR).
+template <int LPR>
+__device__ __forceinline__ void decode_expand_block(const LayerDesc &d, int blk, float *v_lds) {
+  const int s = blk / d.items_per_seg;
+  if (s >= uniform(*d.num_segments)) return;
+  const int it = blk - s * d.items_per_seg;
+  const ModuleDesc m = module_of_item(d, it);
+  const int tile = it - m.item_base;
+  int a, pos0, len;
+  if (!load_segment(d, s, it == 0, &a, &pos0, &len)) return;
+  if (len >= d.long_min) return;  // an SGMV item takes this segment
+  lora_adapter_entry_t e;
+  if (!load_entry(d, a, m.col, tile == 0, &e)) return;
+  const uint16_t *B = static_cast<const uint16_t *>(e.B);
+  const int rank = e.rank;
+  if (len == 1) decode_expand_one_row<LPR>(d, m, B, rank, e.scale, pos0, tile, v_lds);
+  else decode_expand_rows<LPR>(d, m, B, rank, e.scale, pos0, len, tile, v_lds);
+}
+
+}  // namespace lora

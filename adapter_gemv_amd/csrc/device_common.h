@@ -1,0 +1,222 @@
+// Device helpers shared by the gfx950 delta kernels.
+#pragma once
+
+#include "lora_internal.h"
+
+namespace lora {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
+
+// Memory access goes through raw buffer instructions: a scalar resource
+// (base address and byte size) plus one 32-bit per-lane offset and an
+// optional scalar offset.  The hardware returns zero for lane offsets at or
+// beyond the size and drops such stores.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kBufferWord3 = 0x00020000;  // 32-bit data format, no swizzle
+// Streaming access (nt): data read once per step should not displace reused
+// lines from the caches.
+constexpr int kNonTemporal = 2;
+// A lane offset past every buffer this library builds (all are below 4 GiB):
+// loads there return zero and stores are dropped, which masks lanes without
+// a branch (a branch around each load would make the compiler wait for all
+// outstanding loads where the paths join).
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferWord3);
+}
+__device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ u32x4 buf_ld16_stream(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNonTemporal);
+}
+template <int AUX = 0>
+__device__ __forceinline__ u32x2 buf_ld8(rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, AUX);
+}
+__device__ __forceinline__ void buf_st8(rsrc_t r, uint32_t voff, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, 0, 0);
+}
+__device__ __forceinline__ uint16_t buf_ld_u16(rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0);
+}
+__device__ __forceinline__ void buf_st_u16(rsrc_t r, uint32_t voff, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, 0, 0);
+}
+
+// ---- bf16 arithmetic: products of bf16 values are exact in fp32.
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+__device__ __forceinline__ float dot8_bf16(const u32x4 &a, const u32x4 &b, float c) {
+  c = dot2(a.x, b.x, c);
+  c = dot2(a.y, b.y, c);
+  c = dot2(a.z, b.z, c);
+  c = dot2(a.w, b.w, c);
+  return c;
+}
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Eight fp32 values v as two bf16 vectors, v = hi + lo to about 2^-16
+// relative: hi = bf16(v), lo = bf16(v - hi).  A dot product with bf16 data
+// then runs on v_dot2_f32_bf16 (exact products, fp32 sums) with no
+// conversion of the data to fp32.
+struct V8Split {
+  u32x4 hi, lo;
+};
+__device__ __forceinline__ V8Split split_v8(const float *v) {
+  V8Split r;
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float h0 = (float)(__bf16)v[2 * i], h1 = (float)(__bf16)v[2 * i + 1];
+    h[i] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)h0) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)h1) << 16);
+    l[i] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(v[2 * i] - h0)) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(v[2 * i + 1] - h1)) << 16);
+  }
+  r.hi = u32x4{h[0], h[1], h[2], h[3]};
+  r.lo = u32x4{l[0], l[1], l[2], l[3]};
+  return r;
+}
+
+// Eight bf16 values (one 16-byte load) times eight floats given as hi + lo.
+__device__ __forceinline__ float dot8_bf16_split(const u32x4 &b, const V8Split &v, float c) {
+  return dot8_bf16(b, v.lo, dot8_bf16(b, v.hi, c));
+}
+
+// Eight bf16 values (one 16-byte load) times eight floats.
+__device__ __forceinline__ float dot8_bf16_f32(const u32x4 &b, const float *v, float c) {
+  c = fmaf(bf16_lo(b.x), v[0], c);
+  c = fmaf(bf16_hi(b.x), v[1], c);
+  c = fmaf(bf16_lo(b.y), v[2], c);
+  c = fmaf(bf16_hi(b.y), v[3], c);
+  c = fmaf(bf16_lo(b.z), v[4], c);
+  c = fmaf(bf16_hi(b.z), v[5], c);
+  c = fmaf(bf16_lo(b.w), v[6], c);
+  c = fmaf(bf16_hi(b.w), v[7], c);
+  return c;
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float((h & 0xffffu) << 16); }
+// float -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ float bf16_round(float a) { return (float)(__bf16)a; }
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// Reduce-scatter of NV per-lane values over aligned groups of NL lanes.
+// Afterwards, if NV >= NL, lane q = lane % NL holds in v[i] (i < NV/NL) the
+// group sum of value index i + (NV/NL)*q; if NV < NL, v[0] holds the sum of
+// value index q / (NL/NV).  Stage MASK pairs lanes that differ in bit MASK;
+// the lane with that bit set keeps the upper half of its N live values.
+// Every array index is a compile-time constant.
+template <int N, int MASK, int NV>
+__device__ __forceinline__ void rs_stage(float (&v)[NV], int lane) {
+  if constexpr (MASK >= 1) {
+    if constexpr (N > 1) {
+      const bool hi = (lane & MASK) != 0;
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) {
+        const float send = hi ? v[i] : v[i + N / 2];
+        const float keep = hi ? v[i + N / 2] : v[i];
+        v[i] = keep + __shfl_xor(send, MASK, 64);
+      }
+      rs_stage<N / 2, MASK / 2, NV>(v, lane);
+    } else {
+      v[0] += __shfl_xor(v[0], MASK, 64);
+      rs_stage<1, MASK / 2, NV>(v, lane);
+    }
+  }
+}
+
+template <int NV, int NL>
+__device__ __forceinline__ void reduce_scatter(float (&v)[NV]) {
+  rs_stage<NV, NL / 2, NV>(v, threadIdx.x & 63);
+}
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// The descriptor of the running kernel, read from the kernel argument
+// segment (it is the first argument of every kernel of this library).  Lets
+// a non-inlined function reach it without a copy in scratch memory.
+__device__ __forceinline__ const LayerDesc &kernel_desc() {
+  return *(const LayerDesc *)(const void *)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
+// The module of item `it` of a segment (SG: in the SGMV expand numbering).
+// The index is found with scalar compares; the chosen descriptor is then read
+// straight from the kernel argument segment, where the LayerDesc is the first
+// argument of every kernel of this library (indexing the by-value argument
+// itself makes the compiler copy the whole descriptor to scratch memory).
+template <bool SG = false>
+__device__ __forceinline__ ModuleDesc module_of_item(const LayerDesc &d, int it) {
+  int mi = 0;
+#pragma unroll
+  for (int k = 1; k < kMaxModules; ++k)
+    if (k < d.n_active && it >= (SG ? d.mod[k].sg_item_base : d.mod[k].item_base)) mi = k;
+  return kernel_desc().mod[mi];
+}
+
+// Values that are the same for the whole block, moved to scalar registers.
+// Without this a buffer resource built from a loaded pointer can be taken as
+// varying per lane, and every access through it becomes a loop over lanes.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uniform(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+template <typename T>
+__device__ __forceinline__ const T *uniform(const T *p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const T *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Validated segment of a block: slot, first sorted row and length; false
+// (and the status word counted once) when the segments do not fit this batch.
+__device__ __forceinline__ bool load_segment(const LayerDesc &d, int s, bool count, int *a, int *pos0, int *len) {
+  *a = uniform(d.seg_adapter[s]);
+  *pos0 = uniform(d.seg_offsets[s]);
+  *len = uniform(d.seg_offsets[s + 1]) - *pos0;
+  if ((unsigned)*a >= (unsigned)d.num_slots || *pos0 < 0 || *len <= 0 || *pos0 + *len > d.num_rows) {
+    if (count && threadIdx.x == 0) atomicAdd(d.status, 1);
+    return false;
+  }
+  return true;
+}
+
+// Whether a table entry describes a delta this launch can apply.
+__device__ __forceinline__ bool entry_ok(const lora_adapter_entry_t &e, int max_rank) {
+  return e.rank > 0 && e.rank <= max_rank && e.A != nullptr && ((uintptr_t)e.A & 15) == 0 && e.B != nullptr &&
+         ((uintptr_t)e.B & 15) == 0;
+}
+
+// Table entry of (slot, module) for a whole block (the slot is the same for
+// every lane): false for rank 0 (no delta) and for a malformed entry
+// (counted once through `count`).
+__device__ __forceinline__ bool load_entry(const LayerDesc &d, int a, int col, bool count, lora_adapter_entry_t *e) {
+  const lora_adapter_entry_t t = d.table[(int64_t)a * d.table_cols + col];
+  e->A = uniform(t.A);
+  e->B = uniform(t.B);
+  e->rank = uniform(t.rank);
+  e->scale = uniform(t.scale);
+  e->reserved = 0;
+  if (e->rank == 0) return false;
+  if (!entry_ok(*e, d.max_rank)) {
+    if (count && threadIdx.x == 0) atomicAdd(d.status, 1);
+    return false;
+  }
+  return true;
+}
+
+}  // namespace lora

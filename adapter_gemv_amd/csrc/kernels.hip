@@ -1,0 +1,102 @@
+// The delta kernels: one launch per phase covers every projection of the
+// call and every segment.  Blocks [0, decode_blocks) take decode items
+// (segments shorter than long_min rows), the rest take SGMV row tiles.  The
+// rank class of the launch (smallest of 8, 16, 32, 64 holding max_rank) fixes
+// the register tiling of both paths.
+#include "decode_items.h"
+#include "sgmv_items.h"
+
+namespace lora {
+namespace {
+
+template <int CLS>
+__global__ __launch_bounds__(256) void lora_shrink_kernel(LayerDesc d, int decode_blocks) {
+  constexpr int JW = 2 << CLS;                          // A rows per wave (decode)
+  constexpr int NT = CLS <= 1 ? 1 : CLS == 2 ? 2 : 4;   // 16-column rank tiles (SGMV)
+  if ((int)blockIdx.x < decode_blocks) decode_shrink_block<JW>(d, blockIdx.x);
+  else sgmv_shrink_block<NT>(d, blockIdx.x - decode_blocks);
+}
+
+template <int CLS>
+__global__ __launch_bounds__(256) void lora_expand_kernel(LayerDesc d, int decode_blocks) {
+  __shared__ float lds[kSgmvExpandRows * 64];
+  constexpr int LPR = 1 << CLS;                          // lanes per output row (decode)
+  constexpr int KT = CLS <= 1 ? 1 : CLS == 2 ? 2 : 4;    // 16-wide rank steps (SGMV)
+  if ((int)blockIdx.x < decode_blocks) decode_expand_block<LPR>(d, blockIdx.x, lds);
+  else sgmv_expand_block<KT>(d, blockIdx.x - decode_blocks, lds);
+}
+
+// lora_shrink: sum the k-chunk partials of each row in a segment into
+// v[b][0..max_rank) (zero past the entry's rank).
+__global__ __launch_bounds__(256) void shrink_reduce_kernel(LayerDesc d) {
+  const int nseg = min(*d.num_segments, min(d.num_rows, d.num_slots));
+  if (nseg <= 0) return;
+  const int nvalid = min(d.seg_offsets[nseg], d.num_rows);
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int p = (int)(idx / d.max_rank);
+  const int j = (int)(idx - (int64_t)p * d.max_rank);
+  if (p >= nvalid) return;
+  int lo = 0, hi = nseg - 1;  // segment s with seg_offsets[s] <= p < seg_offsets[s+1]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (d.seg_offsets[mid] <= p) lo = mid;
+    else hi = mid - 1;
+  }
+  const ModuleDesc &m = d.mod[0];
+  const int a = d.seg_adapter[lo];
+  if ((unsigned)a >= (unsigned)d.num_slots) return;
+  const lora_adapter_entry_t e = d.table[(int64_t)a * d.table_cols + m.col];  // varies per lane
+  const bool ok = entry_ok(e, d.max_rank);
+  float sum = 0.f;
+  if (ok && j < e.rank)
+    for (int c = 0; c < m.n_chunks; ++c) sum += d.part[((int64_t)(m.part_base + c) * d.num_rows + p) * d.rs + j];
+  const int b = d.perm[p];
+  if ((unsigned)b < (unsigned)d.num_rows) d.v_out[(int64_t)b * d.ldv + j] = sum;
+}
+
+int rank_class(int max_rank) { return max_rank <= 8 ? 0 : max_rank <= 16 ? 1 : max_rank <= 32 ? 2 : 3; }
+
+}  // namespace
+
+int long_tiles_max(int num_rows, int num_slots, int rows_per_tile) {
+  const int long_segs = min(num_slots, num_rows / kLongSegRows);
+  return num_rows / rows_per_tile + long_segs + 1;
+}
+int sgmv_shrink_rows() { return kSgmvShrinkRows; }
+int sgmv_expand_rows() { return kSgmvExpandRows; }
+
+hipError_t launch_shrink(const LayerDesc &d, int decode_blocks, int grid, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  switch (rank_class(d.max_rank)) {
+    case 0: lora_shrink_kernel<0><<<grid, 256, 0, stream>>>(d, decode_blocks); break;
+    case 1: lora_shrink_kernel<1><<<grid, 256, 0, stream>>>(d, decode_blocks); break;
+    case 2: lora_shrink_kernel<2><<<grid, 256, 0, stream>>>(d, decode_blocks); break;
+    default: lora_shrink_kernel<3><<<grid, 256, 0, stream>>>(d, decode_blocks); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_expand(const LayerDesc &d, int decode_blocks, int grid, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  switch (rank_class(d.max_rank)) {
+    case 0: lora_expand_kernel<0><<<grid, 256, 0, stream>>>(d, decode_blocks); break;
+    case 1: lora_expand_kernel<1><<<grid, 256, 0, stream>>>(d, decode_blocks); break;
+    case 2: lora_expand_kernel<2><<<grid, 256, 0, stream>>>(d, decode_blocks); break;
+    default: lora_expand_kernel<3><<<grid, 256, 0, stream>>>(d, decode_blocks); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_shrink_reduce(const LayerDesc &d, hipStream_t stream) {
+  const int64_t total = (int64_t)d.num_rows * d.max_rank;
+  if (total <= 0) return hipSuccess;
+  shrink_reduce_kernel<<<(int)((total + 255) / 256), 256, 0, stream>>>(d);
+  return hipGetLastError();
+}
+
+size_t partials_ws_bytes(int num_rows, int max_rank, int64_t sum_d_in) {
+  const int64_t chunks = sum_d_in / kKChunkMin + kMaxModules;
+  return (size_t)((int64_t)num_rows * partial_row_stride(max_rank) * 4 * chunks);
+}
+
+}  // namespace lora

@@ -19,6 +19,14 @@ constexpr int kSegThreads = 1024;
 constexpr int kKChunkMin = 1024;
 constexpr int kMaxModules = LORA_NUM_MODULES;
 
+// Segments of at least this many rows go to the matrix-core (SGMV) kernels;
+// shorter ones to the decode kernels.
+constexpr int kLongSegRows = 16;
+// Batches of at least this many rows use a larger shrink k-chunk.
+constexpr int kPrefillRows = 2048;
+// Output columns per SGMV expand block.
+constexpr int kSgmvExpandCols = 1024;
+
 // Threads per block of the decode kernels: 4 waves of 64.
 constexpr int kDecodeThreads = 256;
 // Rows staged in LDS per group by the decode expand.
@@ -37,6 +45,8 @@ struct ModuleDesc {
   int32_t n_items;    // k-chunks (shrink) or n-tiles (expand)
   int32_t part_base;  // first partial chunk of this module
   int32_t n_chunks;   // k-chunks of this module
+  int32_t sg_item_base;  // first SGMV expand item (n-tile) of this module in a row tile
+  int32_t sg_n_items;    // SGMV expand n-tiles of this module
 };
 
 // Everything a decode kernel needs, passed by value.
@@ -51,6 +61,9 @@ struct LayerDesc {
   int32_t num_rows;
   int32_t num_slots;
   int32_t max_rank;
+  int32_t long_min;       // segments with at least this many rows: SGMV path
+  int32_t sg_items;       // SGMV expand items (n-tiles over all modules) per row tile
+  int32_t sg_nt;          // SGMV expand n-tile
   const int32_t *perm;
   const int32_t *seg_offsets;
   const int32_t *seg_adapter;
@@ -74,8 +87,14 @@ size_t partials_ws_bytes(int num_rows, int max_rank, int64_t sum_d_in);
 hipError_t launch_build_segments(const int32_t *ids, int n, int num_slots,
                                  const lora_segments_t &seg, void *ws,
                                  hipStream_t stream);
-hipError_t launch_decode_shrink(const LayerDesc &d, int grid, hipStream_t stream);
 hipError_t launch_shrink_reduce(const LayerDesc &d, hipStream_t stream);
-hipError_t launch_decode_expand(const LayerDesc &d, int grid, hipStream_t stream);
+// One launch per phase: blocks [0, decode_blocks) take decode items, the
+// rest SGMV row tiles.
+hipError_t launch_shrink(const LayerDesc &d, int decode_blocks, int grid, hipStream_t stream);
+hipError_t launch_expand(const LayerDesc &d, int decode_blocks, int grid, hipStream_t stream);
+
+int long_tiles_max(int num_rows, int num_slots, int rows_per_tile);
+int sgmv_shrink_rows();
+int sgmv_expand_rows();
 
 }  // namespace lora

@@ -86,23 +86,34 @@ __device__ void scan_slots(int32_t *counts, int num_slots, const lora_segments_t
   }
 }
 
-// Rows of this block with the same id before / after row t (ids in LDS).
+// Rows of this block with the same id before / after row t.  s_ids holds the
+// block's ids in LDS (16-byte aligned, -1 past the end, so a valid id never
+// matches padding); four ids per LDS read.
 __device__ void same_id_counts(const int *s_ids, int len, int t, int id, int *before, int *after) {
-  int bf = 0, af = 0;
-  for (int b = 0; b < len; ++b) {
-    const int o = s_ids[b];
-    bf += (o == id) & (b < t);
-    af += (o == id) & (b > t);
+  const int4 *s4 = reinterpret_cast<const int4 *>(s_ids);
+  const int n4 = (len + 3) >> 2;
+  int bf = 0, tot = 0;
+  for (int b4 = 0; b4 < n4; ++b4) {
+    const int4 v = s4[b4];
+    const int b = b4 * 4;
+    const int e0 = v.x == id, e1 = v.y == id, e2 = v.z == id, e3 = v.w == id;
+    tot += e0 + e1 + e2 + e3;
+    bf += (e0 & (b < t)) + (e1 & (b + 1 < t)) + (e2 & (b + 2 < t)) + (e3 & (b + 3 < t));
   }
   *before = bf;
-  *after = af;
+  *after = tot - bf - 1;  // tot counts row t itself
 }
+
+// Slot tables up to this size keep their counts in LDS.
+constexpr int kSegLdsSlots = 8192;
 
 __global__ __launch_bounds__(kSegThreads) void seg_small_kernel(const int32_t *__restrict__ ids, int n,
                                                                 int num_slots, lora_segments_t seg,
-                                                                int32_t *__restrict__ counts) {
-  __shared__ int s_ids[kSegSmallMax];
+                                                                int32_t *__restrict__ ws_counts) {
+  __shared__ __align__(16) int s_ids[kSegSmallMax];
+  __shared__ int s_counts[kSegLdsSlots];
   __shared__ int s_w[kWaves + 1];
+  int32_t *counts = num_slots <= kSegLdsSlots ? s_counts : ws_counts;
   const int t = threadIdx.x;
   int id = -1, bad = 0;
   if (t < n) {
@@ -129,7 +140,7 @@ __global__ __launch_bounds__(kSegThreads) void seg_chunk_kernel(const int32_t *_
                                                                 int num_slots, int32_t *__restrict__ hist,
                                                                 int32_t *__restrict__ lrank,
                                                                 int32_t *__restrict__ badc) {
-  __shared__ int s_ids[kSegChunk];
+  __shared__ __align__(16) int s_ids[kSegChunk];
   __shared__ int s_w[kWaves + 1];
   const int t = threadIdx.x;
   const int c = blockIdx.x;
@@ -188,7 +199,7 @@ inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 }  // namespace
 
 size_t segments_ws_bytes(int num_rows, int num_slots) {
-  if (num_rows <= kSegSmallMax) return align256((size_t)num_slots * 4);
+  if (num_rows <= kSegSmallMax) return num_slots <= kSegLdsSlots ? 0 : align256((size_t)num_slots * 4);
   const size_t nchunks = ((size_t)num_rows + kSegChunk - 1) / kSegChunk;
   return align256((size_t)num_rows * 4) + align256(nchunks * 4) + align256((size_t)num_slots * 4) +
          align256(nchunks * (size_t)num_slots * 4);

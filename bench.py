@@ -80,6 +80,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0,
                     help="independent copies of the adapters to rotate through (0 = enough to exceed 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (3 times), to scale HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -88,6 +90,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": args.copy_calibration, "launches": 3}), flush=True)
+        return
 
     from workloads import gen
     from workloads.device import DeviceWorkload

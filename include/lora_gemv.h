@@ -88,9 +88,11 @@ typedef enum lora_status {
  * A table is an array of these indexed [slot * n_mod + module].
  *   A      device, bf16 [rank][d_in], row-major, leading dimension d_in,
  *          16-byte aligned.
- *   B      device, bf16 [d_out][rank], row-major, leading dimension rank,
- *          16-byte aligned (ranks that are not a multiple of 8 take a slower
- *          element-wise path for B).
+ *   B      device, bf16 [d_out][ldb], row-major, 16-byte aligned, with
+ *          ldb = rank rounded up to a multiple of 8 (so every row is 16-byte
+ *          aligned; for ranks 8, 16, 32, 64 B is compact).  Columns
+ *          [rank, ldb) are padding: they must hold finite values (zero is
+ *          fine) and contribute nothing.
  *   rank   0 .. max_rank; 0 means the projection is not targeted by this
  *          adapter (zero delta, A and B not read).  A rank outside
  *          [0, max_rank] is a device-data error.
@@ -140,11 +142,12 @@ typedef struct lora_module_io {
 } lora_module_io_t;
 
 /*
- * Workspace (device scratch) that a call with these sizes needs, in bytes.
- * sum_d_in is the sum of d_in over the projections the call will process:
- * d_in for lora_shrink, 0 for lora_expand and lora_build_segments, the sum
- * over the mask for the layer calls.  One workspace of the largest size serves every call
- * on the same stream.  Returns 0 for invalid arguments.
+ * Workspace (device scratch) that covers every call with these sizes, in
+ * bytes.  sum_d_in is the sum of d_in over the projections a call processes
+ * (d_in for lora_shrink, the sum over the mask for the layer calls).  One
+ * workspace of this size serves every call on the same stream.  A call that
+ * needs none (lora_expand; lora_build_segments on up to 1024 rows and 8192
+ * slots) accepts ws = NULL.  Returns 0 for invalid arguments.
  */
 size_t lora_workspace_bytes(int32_t num_rows, int32_t num_slots,
                             int32_t max_rank, int64_t sum_d_in);
@@ -163,8 +166,9 @@ size_t lora_workspace_bytes(int32_t num_rows, int32_t num_slots,
  *                is skipped and counted into *seg.status).
  * Result: segments in ascending slot order, rows ascending inside a segment
  * (a stable sort by id); *seg.status is reset to the number of bad ids.
- * Errors: LORA_ERR_NULL (row_adapter with num_rows > 0, any seg pointer,
- * ws), LORA_ERR_SHAPE (num_rows < 0, num_slots < 1), LORA_ERR_WORKSPACE.
+ * Errors: LORA_ERR_NULL (row_adapter with num_rows > 0, any seg pointer, ws
+ * when workspace is needed), LORA_ERR_SHAPE (num_rows < 0, num_slots < 1),
+ * LORA_ERR_WORKSPACE, LORA_ERR_LAUNCH.
  */
 lora_status_t lora_build_segments(const int32_t *row_adapter, int32_t num_rows,
                                   int32_t num_slots, lora_segments_t seg,

@@ -92,13 +92,16 @@ void oracle_shrink_row(const uint16_t *x, int32_t d_in, const uint16_t *A,
     }
 }
 
-/* delta[n] = scale * sum_j B[n][j] * v[j]  (B row-major, leading dim rank). */
+/* delta[n] = scale * sum_j B[n][j] * v[j]  (B row-major; its rows are
+ * stored rank rounded up to a multiple of 8 apart, the columns past the rank
+ * being padding that is never read). */
 void oracle_expand_row(const double *v, int32_t rank, const uint16_t *B,
                        int32_t d_out, double scale, double *delta)
 {
+    const int64_t ldb = ((int64_t)rank + 7) / 8 * 8;
     for (int32_t n = 0; n < d_out; ++n) {
         double s = 0.0;
-        const uint16_t *b = B + (int64_t)n * rank;
+        const uint16_t *b = B + (int64_t)n * ldb;
         for (int32_t j = 0; j < rank; ++j)
             s += bf16_value(b[j]) * v[j];
         delta[n] = scale * s;

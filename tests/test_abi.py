@@ -67,8 +67,9 @@ def test_workspace_query():
     (dict(n=-1), SHAPE),
     (dict(slots=0), SHAPE),
     (dict(ids=None), NULL),
-    (dict(ws=None), NULL),
-    (dict(ws_bytes=0), WS),
+    (dict(n=5000, ws=None), NULL),           # long batches need workspace
+    (dict(n=5000, ws_bytes=0), WS),          # long batches need workspace
+    (dict(n=128, slots=20000, ws_bytes=0), WS),  # so do very large slot tables
 ])
 def test_build_segments_rejects(args, code):
     a = dict(ids=P, n=128, slots=16, seg=seg(), ws=P, ws_bytes=BIG)
@@ -82,14 +83,13 @@ SHRINK = dict(x=P, ldx=1024, n=64, d=1024, table=P, slots=8, n_mod=7, module=0, 
 
 @pytest.mark.parametrize("fn", ["lora_shrink", "lora_expand"])
 @pytest.mark.parametrize("args,code", [
-    (dict(x=None), NULL), (dict(table=None), NULL), (dict(v=None), NULL), (dict(ws=None), NULL),
+    (dict(x=None), NULL), (dict(table=None), NULL), (dict(v=None), NULL),
     (dict(seg=seg(seg_adapter=None)), NULL),
     (dict(n_mod=0), MODULE), (dict(n_mod=8), MODULE), (dict(module=7), MODULE), (dict(module=-1), MODULE),
     (dict(max_rank=0), RANK), (dict(max_rank=65), RANK),
     (dict(n=-1), SHAPE), (dict(slots=0), SHAPE), (dict(d=0), SHAPE), (dict(ldx=1016), SHAPE), (dict(ldv=8), SHAPE),
     (dict(d=1020, ldx=1024), ALIGN), (dict(ldx=1028), ALIGN), (dict(x=P + 8), ALIGN), (dict(v=P + 4), ALIGN),
     (dict(ldv=18), ALIGN),
-    (dict(ws_bytes=16), WS),
 ])
 def test_shrink_expand_reject(fn, args, code):
     a = dict(SHRINK)
@@ -101,6 +101,15 @@ def test_shrink_expand_reject(fn, args, code):
     else:  # same roles: v in, x plays y
         r = L.lora_expand(a["v"], a["ldv"], a["n"], a["d"], a["table"], a["slots"], a["n_mod"], a["module"], a["seg"],
                           a["max_rank"], a["x"], a["ldx"], a["ws"], a["ws_bytes"], None)
+    assert r == code
+
+
+@pytest.mark.parametrize("args,code", [(dict(ws=None), NULL), (dict(ws_bytes=16), WS)])
+def test_shrink_workspace(args, code):
+    a = dict(SHRINK)
+    a.update(args)
+    r = lg.lib().lora_shrink(a["x"], a["ldx"], a["n"], a["d"], a["table"], a["slots"], a["n_mod"], a["module"],
+                             a["seg"], a["max_rank"], a["v"], a["ldv"], a["ws"], a["ws_bytes"], None)
     assert r == code
 
 

@@ -269,3 +269,36 @@ def test_graph_replay_follows_device_data():
         ref = oracle.lora_module(w2.x["x"], w2.y0["q"], ids, A[perm_slots], B[perm_slots], R[perm_slots],
                                  S[perm_slots], 16)
         check_rows(got, ref.y, f"graph replay {rep}")
+
+
+# ------------------------------------------------------------------ long segments (matrix-core path)
+
+LONG = [
+    # segment lengths, ranks per slot, d_in, d_out
+    ([16, 17, 31, 64, 65, 128, 129, 300], (16, 64, 24, 40, 8, 32, 48, 56), 2056, 1000),
+    ([16, 40, 200], (4, 12, 1), 1024, 520),
+    ([19, 5, 77, 1, 130], (7, 64, 63, 33, 9), 3080, 2048),
+]
+
+
+@pytest.mark.parametrize("runner", ["split", "layer", "phases"])
+@pytest.mark.parametrize("case", range(len(LONG)))
+def test_long_segments(case, runner):
+    lens, ranks_, d_in, d_out = LONG[case]
+    ids = np.repeat(np.arange(len(lens)), lens)
+    ids = np.random.default_rng(case).permutation(ids)   # rows of a segment need not be adjacent
+    ranks = np.zeros((len(lens), 7), np.int32)
+    ranks[:, 0] = ranks_
+    w = bw(100 + case, ids.size, len(lens), d_in, d_out, None, ids, ranks=ranks, x_std=1.0)
+    check_workload(w, oracle_all(w), runner)
+
+
+def test_long_segments_with_short_and_base_rows():
+    # a prefill-like batch: a few long sequences, many single decode rows, base-only rows
+    lens = [600, 1, 1, 2, 250, 1, 3, 15, 16, 1000]
+    ids = np.concatenate([np.repeat(np.arange(len(lens)), lens), -np.ones(50, int)])
+    ranks = np.zeros((len(lens), 7), np.int32)
+    ranks[:, 0] = [16, 16, 64, 8, 32, 16, 16, 64, 64, 16]
+    w = bw(200, ids.size, len(lens), 4096, 2048, None, ids, ranks=ranks, x_std=1.0)
+    for runner in ("split", "layer"):
+        check_workload(w, oracle_all(w), runner)

@@ -18,6 +18,7 @@ MUTATIONS = {
     "A_transposed": ("s += bf16_value(a[k]) * bf16_value(x[k]);",
                      "s += bf16_value(A[(int64_t)k * rank + j]) * bf16_value(x[k]); (void)a;"),
     "B_transposed": ("s += bf16_value(b[j]) * v[j];", "s += bf16_value(B[(int64_t)j * d_out + n]) * v[j]; (void)b;"),
+    "B_compact_rows": ("const uint16_t *b = B + (int64_t)n * ldb;", "const uint16_t *b = B + (int64_t)n * rank; (void)ldb;"),
     "drop_last_rank_term": ("for (int32_t j = 0; j < rank; ++j)\n            s += bf16_value(b[j])",
                             "for (int32_t j = 0; j < rank - 1; ++j)\n            s += bf16_value(b[j])"),
     "no_scale": ("delta[n] = scale * s;", "delta[n] = s; (void)scale;"),

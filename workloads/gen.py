@@ -41,7 +41,7 @@ _CHUNK = 1 << 22
 _THREADS = max(1, min(16, os.cpu_count() or 1))
 
 # Roles of the independent draws.
-_R_IDS, _R_RANK, _R_PLACE, _R_X, _R_Y, _R_A, _R_B, _R_LEN = range(8)
+_R_IDS, _R_RANK, _R_PLACE, _R_X, _R_Y, _R_A, _R_B, _R_LEN, _R_PAD = range(9)
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -97,7 +97,9 @@ class Workload:
 
     Every A and B lives in one flat bf16 ``pool``; ``a_off``/``b_off`` give the
     element offset of entry (slot, column) (-1 where the rank is 0).  A is
-    [rank, d_in] and B is [d_out, rank], both row-major and compact.
+    [rank, d_in] row-major and compact; B is [d_out, rank] row-major with its
+    rows ``ldb(rank)`` (rank rounded up to a multiple of 8) elements apart.
+    The padding columns hold random values that no computation may use.
     """
     name: str
     seed: int
@@ -136,10 +138,11 @@ class Workload:
         return self.pool[o:o + r * d_in].reshape(r, d_in)
 
     def B(self, slot: int, col: int) -> np.ndarray:
+        """[d_out, rank] view (rows ldb(rank) apart in the pool)."""
         r = int(self.ranks[slot, col])
         d_out = self._spec_col(col).d_out
         o = int(self.b_off[slot, col])
-        return self.pool[o:o + d_out * r].reshape(d_out, r)
+        return self.pool[o:o + d_out * ldb(r)].reshape(d_out, ldb(r))[:, :r]
 
     def _spec_col(self, col):
         for s in self.modules:
@@ -155,8 +158,14 @@ class Workload:
         return a, b, self.ranks[:, col].copy(), self.scales[:, col].copy()
 
     def adapter_bytes_used(self) -> int:
+        """bf16 bytes of A and B at their ranks (padding not counted)."""
         return 2 * int(sum(self.ranks[a, s.index] * (s.d_in + s.d_out)
                            for s in self.modules for a in range(self.num_slots)))
+
+
+def ldb(rank: int) -> int:
+    """Row stride of B: the rank rounded up to a multiple of 8."""
+    return (int(rank) + 7) // 8 * 8
 
 
 def _fill_adapters(seed, pool, modules, ranks, a_off, b_off, ab_std, slots):
@@ -171,7 +180,13 @@ def _fill_adapters(seed, pool, modules, ranks, a_off, b_off, ab_std, slots):
         a, s, r = job
         oa, ob = int(a_off[a, s.index]), int(b_off[a, s.index])
         normal_bf16(seed, (_R_A, a, s.index), r * s.d_in, ab_std, out=pool[oa:oa + r * s.d_in])
-        normal_bf16(seed, (_R_B, a, s.index), s.d_out * r, ab_std, out=pool[ob:ob + s.d_out * r])
+        lb = ldb(r)
+        if lb == r:
+            normal_bf16(seed, (_R_B, a, s.index), s.d_out * r, ab_std, out=pool[ob:ob + s.d_out * r])
+        else:
+            full = pool[ob:ob + s.d_out * lb].reshape(s.d_out, lb)
+            full[:, :r] = normal_bf16(seed, (_R_B, a, s.index), s.d_out * r, ab_std).reshape(s.d_out, r)
+            full[:, r:] = normal_bf16(seed, (_R_PAD, a, s.index), s.d_out * (lb - r), 1.0).reshape(s.d_out, lb - r)
 
     with ThreadPoolExecutor(_THREADS) as ex:
         list(ex.map(fill, jobs))
@@ -212,7 +227,7 @@ def build_workload(name, seed, num_rows, num_slots, shapes: dict, ids, ranks,
                     a_off[a, s.index] = pos
                     pos = _align(pos + r * s.d_in)
                     b_off[a, s.index] = pos
-                    pos = _align(pos + s.d_out * r)
+                    pos = _align(pos + s.d_out * ldb(r))
         pool = np.zeros(max(pos, 64), np.uint16)
     else:
         cap = int(paged_capacity_rank)
