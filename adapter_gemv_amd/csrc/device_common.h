@@ -42,6 +42,9 @@ template <int AUX = 0>
 __device__ __forceinline__ u32x2 buf_ld8(rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, AUX);
 }
+__device__ __forceinline__ void buf_st16(rsrc_t r, uint32_t voff, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, 0);
+}
 __device__ __forceinline__ void buf_st8(rsrc_t r, uint32_t voff, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, 0, 0);
 }

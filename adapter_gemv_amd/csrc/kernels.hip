@@ -21,7 +21,7 @@ template <int CLS>
 __global__ __launch_bounds__(256) void lora_expand_kernel(LayerDesc d, int decode_blocks) {
   __shared__ float lds[kSgmvExpandRows * 64];
   constexpr int LPR = 1 << CLS;                          // lanes per output row (decode)
-  constexpr int KT = CLS <= 1 ? 1 : CLS == 2 ? 2 : 4;    // 16-wide rank steps (SGMV)
+  constexpr int KT = CLS <= 2 ? 1 : 2;                   // 32-wide rank steps (SGMV)
   if ((int)blockIdx.x < decode_blocks) decode_expand_block<LPR>(d, blockIdx.x, lds);
   else sgmv_expand_block<KT>(d, blockIdx.x - decode_blocks, lds);
 }

@@ -25,7 +25,7 @@ constexpr int kLongSegRows = 16;
 // Batches of at least this many rows use a larger shrink k-chunk.
 constexpr int kPrefillRows = 2048;
 // Output columns per SGMV expand block.
-constexpr int kSgmvExpandCols = 1024;
+constexpr int kSgmvExpandCols = 2048;
 
 // Threads per block of the decode kernels: 4 waves of 64.
 constexpr int kDecodeThreads = 256;

@@ -26,12 +26,14 @@
 //   registers refilled as each step is consumed).  The chunk's partial V goes
 //   to the workspace layout of the decode shrink ([chunk][sorted row][rank]).
 // Expand: a block takes 64 rows of one segment and an n-tile; the chunk
-//   partials of its rows are summed into LDS (times scale), and each wave
-//   turns its 16 rows into matrix operands, splitting each fp32 value v into
+//   partials of its rows are summed into LDS (times scale), and every wave
+//   turns all 64 rows into matrix operands, splitting each fp32 value v into
 //   bf16 hi = bf16(v) and lo = bf16(v - hi) so the product keeps about fp32
-//   accuracy (B is exact in bf16).  The operands are swapped (C = B . V^T)
-//   so a lane's four results are four consecutive outputs of one row: y is
-//   read and written 8 bytes per lane, with DE column steps in flight.
+//   accuracy (B is exact in bf16).  The waves split the columns (32-column
+//   steps, round robin), so each B element is read once per block.  The
+//   operands are swapped (C = B . V^T) and the B rows permuted so a lane's
+//   results are 8 consecutive outputs of one row: y is read and written 16
+//   bytes per lane, with DE column steps in flight.
 #pragma once
 
 #include "device_common.h"
@@ -79,7 +81,7 @@ __device__ __forceinline__ bool find_long_tile(const LayerDesc &d, int tile, int
 // NT = 16-column tiles of the rank per wave (1, 2 or 4).
 template <int NT>
 __device__ __forceinline__ void sgmv_shrink_block(const LayerDesc &d, int blk) {
-  constexpr int D = NT >= 4 ? 2 : 4;  // k steps in flight
+  constexpr int D = NT >= 2 ? 2 : 4;  // k steps per register set (two sets in flight)
   const int lane = threadIdx.x & 63, w = wave_id();
   const int tile = blk / d.items_per_seg;
   const int it = blk - tile * d.items_per_seg;
@@ -125,21 +127,32 @@ __device__ __forceinline__ void sgmv_shrink_block(const LayerDesc &d, int blk) {
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  u32x4 xb[D][2], ab[D][NT];
+  auto mfma_steps = [&](u32x4(&xs)[D][2], u32x4(&as)[D][NT]) {
 #pragma unroll
-  for (int u = 0; u < D; ++u) load(k_begin + 32 * u, xb[u], ab[u]);
-  for (int k = k_begin; k < k_end; k += 32 * D) {
-#pragma unroll
-    for (int u = 0; u < D; ++u) {
+    for (int u = 0; u < D; ++u)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xb[u][mt]),
-                                                                __builtin_bit_cast(bf16x8_t, ab[u][nt]), acc[mt][nt],
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xs[u][mt]),
+                                                                __builtin_bit_cast(bf16x8_t, as[u][nt]), acc[mt][nt],
                                                                 0, 0, 0);
-      load(k + 32 * (u + D), xb[u], ab[u]);
-    }
+  };
+  // Ping-pong over two register sets of D k-steps each: the next set's loads
+  // are issued before the current set is consumed, so 2*D steps are in
+  // flight.  Steps past the chunk read zero and add nothing.
+  u32x4 x0[D][2], a0[D][NT], x1[D][2], a1[D][NT];
+#pragma unroll
+  for (int u = 0; u < D; ++u) load(k_begin + 32 * u, x0[u], a0[u]);
+  for (int k = k_begin; k < k_end; k += 64 * D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) load(k + 32 * (D + u), x1[u], a1[u]);
+    __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the math
+    mfma_steps(x0, a0);
+#pragma unroll
+    for (int u = 0; u < D; ++u) load(k + 32 * (2 * D + u), x0[u], a0[u]);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_steps(x1, a1);
   }
   // C[4*(l/16) + i][l%16] of tile (mt, nt): row 32w + 16mt + 4*(l/16) + i, column 16nt + l%16.
   float *out = d.part + ((int64_t)(m.part_base + chunk) * d.num_rows + seg0) * d.rs;
@@ -160,45 +173,65 @@ __device__ __forceinline__ void sgmv_shrink_block(const LayerDesc &d, int blk) {
 
 // ---------------------------------------------------------------- expand --
 
-// KT = 16-wide steps over the rank (1, 2 or 4).  B rows are a multiple of 8
-// elements apart, so a lane's 4 values of a B row are one 8-byte load.
+// KT = 32-wide steps over the rank (1: rank <= 32, 2: rank <= 64).  B rows
+// are a multiple of 8 elements apart, so a lane's 8 values of a B row are one
+// 16-byte load; past the rank they are zero (masked) or padding that meets
+// zeros of V.
 template <int KT>
 __device__ __forceinline__ void sgmv_expand_tile(const LayerDesc &d, const ModuleDesc &m, const uint16_t *B, int rank,
                                                  float scale, int seg0, int len, int rt, int tile, float *v_lds) {
-  constexpr int DE = KT >= 4 ? 4 : 8;  // 16-column steps in flight
+  constexpr int DE = 1;  // 32-column steps per register set (two sets in flight)
+  constexpr int NQ = kSgmvExpandRows / 16;  // 16-row tiles per block, all handled by every wave
   const int t = threadIdx.x, lane = t & 63, w = wave_id();
-  const int r_in = lane & 15, kq = (lane >> 4) * 4;
+  const int r_in = lane & 15, g = lane >> 4;
   const int row0 = rt * kSgmvExpandRows;
   const int nrows = min(kSgmvExpandRows, len - row0);
   const int n_tile0 = tile * d.sg_nt;
-  const int n_tile1 = min(n_tile0 + d.sg_nt, m.d_out);
-  const int tile_len = n_tile1 - n_tile0;
-  // This lane's output row and the B tile.
-  const int r = row0 + w * 16 + r_in;
-  const int b = r < len ? d.perm[seg0 + r] : -1;
-  const bool yon = (unsigned)b < (unsigned)d.num_rows;
+  const int tile_len = min(n_tile0 + d.sg_nt, m.d_out) - n_tile0;
+  // Output rows of this lane, one per 16-row tile (offsets of the tile's
+  // first column; out of range past the segment).
   const rsrc_t ry = make_rsrc(m.y, (uint32_t)((int64_t)d.num_rows * m.ldy * 2));
-  const uint32_t yrow = yon ? (uint32_t)((int64_t)b * m.ldy * 2) : 0u;
-  const int ldb = (rank + 7) & ~7;  // B row stride; columns past the rank meet zeros of V
-  const rsrc_t rb = make_rsrc(B + (int64_t)n_tile0 * ldb, (uint32_t)tile_len * ldb * 2);
-  auto y_off = [&](int n0) {  // this lane's 4 outputs of columns n0 + 4*(l/16) .. +4
-    const int nc = n0 + kq;
-    return yon && nc < tile_len ? yrow + (uint32_t)(n_tile0 + nc) * 2 : kOutOfRange;
-  };
-  auto load_b = [&](int n, int kt) -> s16x4_t {  // B[n][16kt + kq .. +4], zero past the rank / tile
-    const int k = kt * 16 + kq;
-    return __builtin_bit_cast(
-        s16x4_t, buf_ld8<kNonTemporal>(rb, k < rank && n < tile_len ? ((uint32_t)n * ldb + k) * 2 : kOutOfRange));
-  };
-  // Requests for the first DE column steps go out before the V prologue.
-  s16x4_t bop[DE][KT];
-  u32x2 yv[DE];
+  uint32_t yrow[NQ];
 #pragma unroll
-  for (int u = 0; u < DE; ++u) {
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) bop[u][kt] = load_b(16 * u + r_in, kt);
-    yv[u] = buf_ld8(ry, y_off(16 * u));
+  for (int q = 0; q < NQ; ++q) {
+    const int r = row0 + q * 16 + r_in;
+    const int b = r < len ? d.perm[seg0 + r] : -1;
+    yrow[q] = (unsigned)b < (unsigned)d.num_rows ? (uint32_t)(((int64_t)b * m.ldy + n_tile0) * 2) : kOutOfRange;
   }
+  const int ldb = (rank + 7) & ~7;
+  const rsrc_t rb = make_rsrc(B + (int64_t)n_tile0 * ldb, (uint32_t)tile_len * ldb * 2);
+  // Wave w takes the 32-column steps w, w+4, w+8, ... of the tile.  Matrix
+  // row i of half h stands for column n0 + 8*(i/4) + 4h + i%4, so the results
+  // of the two halves give lane l the 8 consecutive columns n0 + 8*(l/16) ..
+  // +8 of its row: y moves 16 bytes per lane.
+  auto col0 = [&](int step) { return (4 * step + w) * 32; };
+  auto y_off = [&](int q, int n0) {
+    const int nc = n0 + 8 * g;
+    return yrow[q] != kOutOfRange && nc < tile_len ? yrow[q] + (uint32_t)nc * 2 : kOutOfRange;
+  };
+  auto load_b = [&](int n0, int h, int kt) {  // B[col][32kt + 8g .. +8]; zero past the rank / tile
+    const int n = n0 + 8 * (r_in >> 2) + 4 * h + (r_in & 3);
+    const int k = kt * 32 + 8 * g;
+    return buf_ld16(rb, k < rank && n < tile_len ? ((uint32_t)n * ldb + k) * 2 : kOutOfRange, 0);
+  };
+  struct Set {
+    u32x4 bop[DE][2][KT];
+    u32x4 yv[DE][NQ];
+  };
+  auto issue = [&](Set &st, int step) {  // steps step .. step+DE; past the tile: zero, no traffic
+#pragma unroll
+    for (int u = 0; u < DE; ++u) {
+      const int n0 = col0(step + u);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) st.bop[u][h][kt] = load_b(n0, h, kt);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) st.yv[u][q] = buf_ld16(ry, y_off(q, n0), 0);
+    }
+  };
+  Set s0, s1;
+  issue(s0, 0);  // before the V prologue
   // V rows of the tile (times scale) into LDS: [64][64] fp32.
   for (int idx = t; idx < kSgmvExpandRows * 64; idx += 256) {
     const int i = idx >> 6, j = idx & 63;
@@ -215,42 +248,50 @@ __device__ __forceinline__ void sgmv_expand_tile(const LayerDesc &d, const Modul
     v_lds[idx] = sum * scale;
   }
   __syncthreads();
-  // This wave's 16 rows as hi/lo bf16 operands: row 16w + l%16, k = 16kt + 4*(l/16) .. +4.
-  s16x4_t vhi[KT], vlo[KT];
+  // All 64 rows as hi/lo bf16 operands: tile q, lane l holds row 16q + l%16,
+  // k = 32kt + 8*(l/16) .. +8.
+  V8Split vop[NQ][KT];
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    const float *src = v_lds + (w * 16 + r_in) * 64 + kt * 16 + kq;
-    float hv[4], lv[4];
+  for (int q = 0; q < NQ; ++q)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      hv[c] = bf16_round(src[c]);
-      lv[c] = src[c] - hv[c];
-    }
-    vhi[kt] = __builtin_bit_cast(s16x4_t, u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])});
-    vlo[kt] = __builtin_bit_cast(s16x4_t, u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])});
-  }
-  // Columns in steps of 16: A-operand = B rows n0 + l%16; result lane (l, i)
-  // = output column n0 + 4*(l/16) + i of row 16w + l%16.
-  for (int n0 = 0; n0 < tile_len; n0 += 16 * DE) {
+    for (int kt = 0; kt < KT; ++kt) vop[q][kt] = split_v8(v_lds + (q * 16 + r_in) * 64 + kt * 32 + 8 * g);
+  auto finish = [&](const Set &st, int step) {
 #pragma unroll
     for (int u = 0; u < DE; ++u) {
-      f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int n0 = col0(step + u);
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bop[u][kt], vhi[kt], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bop[u][kt], vlo[kt], acc, 0, 0, 0);
+      for (int q = 0; q < NQ; ++q) {
+        f32x4_t acc[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          acc[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) {
+            const bf16x8_t bo = __builtin_bit_cast(bf16x8_t, st.bop[u][h][kt]);
+            acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bo, __builtin_bit_cast(bf16x8_t, vop[q][kt].hi), acc[h],
+                                                             0, 0, 0);
+            acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bo, __builtin_bit_cast(bf16x8_t, vop[q][kt].lo), acc[h],
+                                                             0, 0, 0);
+          }
+        }
+        const u32x4 yv = st.yv[u][q];
+        u32x4 o;
+        o.x = pack_bf16x2(bf16_to_f32(yv.x) + acc[0][0], bf16_to_f32(yv.x >> 16) + acc[0][1]);
+        o.y = pack_bf16x2(bf16_to_f32(yv.y) + acc[0][2], bf16_to_f32(yv.y >> 16) + acc[0][3]);
+        o.z = pack_bf16x2(bf16_to_f32(yv.z) + acc[1][0], bf16_to_f32(yv.z >> 16) + acc[1][1]);
+        o.w = pack_bf16x2(bf16_to_f32(yv.w) + acc[1][2], bf16_to_f32(yv.w >> 16) + acc[1][3]);
+        buf_st16(ry, y_off(q, n0), o);
       }
-      const float o0 = bf16_to_f32(yv[u].x) + acc[0];
-      const float o1 = bf16_to_f32(yv[u].x >> 16) + acc[1];
-      const float o2 = bf16_to_f32(yv[u].y) + acc[2];
-      const float o3 = bf16_to_f32(yv[u].y >> 16) + acc[3];
-      buf_st8(ry, y_off(n0 + 16 * u), u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)});
-      // refill this slot with the step DE ahead (past the tile: zero, no traffic)
-      const int nn = n0 + 16 * (u + DE);
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) bop[u][kt] = load_b(nn + r_in, kt);
-      yv[u] = buf_ld8(ry, y_off(nn));
     }
+  };
+  const int steps = (tile_len + 127) / 128;  // per wave (upper bound; extra steps are masked)
+  for (int i = 0; i < steps; i += 2 * DE) {
+    issue(s1, i + DE);
+    __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the math
+    finish(s0, i);
+    issue(s0, i + 2 * DE);
+    __builtin_amdgcn_sched_barrier(0);
+    finish(s1, i + DE);
   }
 }
 
