@@ -147,6 +147,7 @@ lora_status_t check_layer(const lora_module_io_t *io, uint32_t module_mask, int3
   }
   const size_t need = partials_ws_bytes(num_rows, max_rank, sum_d_in);
   if (need > 0 && !ws) return LORA_ERR_NULL;
+  if (need > 0 && !aligned16(ws)) return LORA_ERR_ALIGN;
   if (ws_bytes < need) return LORA_ERR_WORKSPACE;
   *n_out = n;
   return LORA_OK;
@@ -201,6 +202,7 @@ lora_status_t lora_build_segments(const int32_t *row_adapter, int32_t num_rows, 
   if (num_rows > 0 && !row_adapter) return LORA_ERR_NULL;
   const size_t need = segments_ws_bytes(num_rows, num_slots);
   if (need > 0 && !ws) return LORA_ERR_NULL;
+  if (need > 0 && !aligned16(ws)) return LORA_ERR_ALIGN;
   if (ws_bytes < need) return LORA_ERR_WORKSPACE;
   return launched(launch_build_segments(row_adapter, num_rows, num_slots, seg, ws, static_cast<hipStream_t>(stream)));
 }
@@ -219,6 +221,7 @@ lora_status_t lora_shrink(const void *x, int64_t ldx, int32_t num_rows, int32_t 
   if (!fits_u32(num_rows, ldx)) return LORA_ERR_SHAPE;
   const size_t need = partials_ws_bytes(num_rows, max_rank, d_in);
   if (need > 0 && !ws) return LORA_ERR_NULL;
+  if (need > 0 && !aligned16(ws)) return LORA_ERR_ALIGN;
   if (ws_bytes < need) return LORA_ERR_WORKSPACE;
   if (num_rows == 0) return LORA_OK;
   ModuleArgs m{x, ldx, nullptr, 0, d_in, 0, module};

@@ -129,17 +129,6 @@ __device__ __forceinline__ u32x4 load_b8(rsrc_t rb, int n, int ldb, int rank, in
   return buf_ld16_stream(rb, jq < rank ? ((uint32_t)n * ldb + jq) * 2 : kOutOfRange, 0);
 }
 
-// Sum of the k-chunk partials of row p (sorted position), column j.
-__device__ __forceinline__ float partial_sum(const LayerDesc &d, const ModuleDesc &m, int p, int j) {
-  if (d.v != nullptr) {
-    const int b = d.perm[p];
-    return (unsigned)b < (unsigned)d.num_rows ? d.v[(int64_t)b * d.ldv + j] : 0.f;
-  }
-  float sum = 0.f;
-  for (int c = 0; c < m.n_chunks; ++c) sum += d.part[((int64_t)(m.part_base + c) * d.num_rows + p) * d.rs + j];
-  return sum;
-}
-
 // One n-tile of one projection for every row of a multi-row segment.  The B
 // tile is loaded once and kept in registers across the rows; y of a few rows
 // is requested together.
@@ -170,11 +159,7 @@ __device__ __forceinline__ void decode_expand_rows(const LayerDesc &d, const Mod
     for (int r0 = 0; r0 < len; r0 += kExpandRowGroup) {
       const int nr = min(kExpandRowGroup, len - r0);
       __syncthreads();
-      for (int idx = t; idx < nr * 64; idx += kDecodeThreads) {
-        const int i = idx >> 6, j = idx & 63;
-        v_lds[idx] = j < rank ? partial_sum(d, m, pos0 + r0 + i, j) * scale : 0.f;
-      }
-      __syncthreads();
+      stage_v<kExpandRowGroup>(d, m, pos0 + r0, nr, rank, scale, v_lds);
       for (int i0 = 0; i0 < nr; i0 += YR) {
         rsrc_t ry[YR];
         uint16_t yv[YR][PL];
@@ -250,8 +235,7 @@ __device__ __forceinline__ void decode_expand_one_row(const LayerDesc &d, const 
   uint16_t yv[PL];
 #pragma unroll
   for (int ii = 0; ii < PL; ++ii) yv[ii] = buf_ld_u16(ry, y_off(0, ii));
-  if (t < 64) v_lds[t] = t < rank ? partial_sum(d, m, pos0, t) * scale : 0.f;
-  __syncthreads();
+  stage_v<1>(d, m, pos0, 1, rank, scale, v_lds);
   float vv[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) vv[k] = v_lds[jq + k];

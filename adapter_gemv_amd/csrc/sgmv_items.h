@@ -233,21 +233,7 @@ __device__ __forceinline__ void sgmv_expand_tile(const LayerDesc &d, const Modul
   Set s0, s1;
   issue(s0, 0);  // before the V prologue
   // V rows of the tile (times scale) into LDS: [64][64] fp32.
-  for (int idx = t; idx < kSgmvExpandRows * 64; idx += 256) {
-    const int i = idx >> 6, j = idx & 63;
-    float sum = 0.f;
-    if (i < nrows && j < rank) {
-      const int p = seg0 + row0 + i;
-      if (d.v != nullptr) {
-        const int bb = d.perm[p];
-        if ((unsigned)bb < (unsigned)d.num_rows) sum = d.v[(int64_t)bb * d.ldv + j];
-      } else {
-        for (int c = 0; c < m.n_chunks; ++c) sum += d.part[((int64_t)(m.part_base + c) * d.num_rows + p) * d.rs + j];
-      }
-    }
-    v_lds[idx] = sum * scale;
-  }
-  __syncthreads();
+  stage_v<kSgmvExpandRows>(d, m, seg0 + row0, nrows, rank, scale, v_lds);
   // All 64 rows as hi/lo bf16 operands: tile q, lane l holds row 16q + l%16,
   // k = 32kt + 8*(l/16) .. +8.
   V8Split vop[NQ][KT];

@@ -104,7 +104,7 @@ def test_shrink_expand_reject(fn, args, code):
     assert r == code
 
 
-@pytest.mark.parametrize("args,code", [(dict(ws=None), NULL), (dict(ws_bytes=16), WS)])
+@pytest.mark.parametrize("args,code", [(dict(ws=None), NULL), (dict(ws_bytes=16), WS), (dict(ws=P + 8), ALIGN)])
 def test_shrink_workspace(args, code):
     a = dict(SHRINK)
     a.update(args)
@@ -132,7 +132,7 @@ def ios(**over):
     (dict(io=ios(**{"3_x": None})), NULL), (dict(io=ios(**{"0_y": None})), NULL),
     (dict(io=ios(**{"2_d_out": 0})), SHAPE), (dict(io=ios(**{"1_ldy": 4096})), SHAPE),
     (dict(io=ios(**{"6_d_in": 1004, "6_ldx": 1008})), ALIGN), (dict(io=ios(**{"4_y": P + 2})), ALIGN),
-    (dict(ws_bytes=1024), WS),
+    (dict(ws_bytes=1024), WS), (dict(ws=P + 4), ALIGN),
 ])
 def test_layer_rejects(fn, args, code):
     a = dict(io=ios(), mask=0x7F, n=128, table=P, slots=128, seg=seg(), max_rank=64, ws=P, ws_bytes=BIG)
