@@ -129,66 +129,71 @@ __device__ __forceinline__ u32x4 load_b8(rsrc_t rb, int n, int ldb, int rank, in
   return buf_ld16_stream(rb, jq < rank ? ((uint32_t)n * ldb + jq) * 2 : kOutOfRange, 0);
 }
 
-// One n-tile of one projection for every row of a multi-row segment.  The B
-// tile is loaded once and kept in registers across the rows; y of a few rows
-// is requested together.
+// One n-tile of one projection for every row of a multi-row segment (fewer
+// than kLongSegRows rows: longer ones go to the SGMV items).  v of every row
+// is staged once; the B sub-tile is loaded once into registers and used by
+// all rows, and the next sub-tile is requested when the rows are done; y of
+// a few rows is requested together.
 template <int LPR>
 __device__ __forceinline__ void decode_expand_rows(const LayerDesc &d, const ModuleDesc &m,
                                                    const uint16_t *__restrict__ B, int rank, float scale, int pos0,
                                                    int len, int tile, float *v_lds) {
+  static_assert(kLongSegRows <= kExpandRowGroup, "a decode segment is staged in one group");
   constexpr int G = kDecodeThreads / LPR;  // output rows per load pass of the block
   constexpr int P = 16;                    // load passes per sub-tile
   constexpr int SUB = P * G;               // outputs per sub-tile
   constexpr int PL = P / LPR;              // outputs per lane per row after the reduce-scatter
   constexpr int YR = PL <= 4 ? 4 : 1;      // rows whose y is requested together
   const int t = threadIdx.x, g = t / LPR, q = t % LPR, jq = q * 8;
+  const int nr = min(len, kExpandRowGroup);
   const int n_tile0 = tile * d.nt;
   const int n_tile1 = min(n_tile0 + d.nt, m.d_out);
   const uint32_t tile_len = (uint32_t)(n_tile1 - n_tile0);
   const int ldb = b_stride(rank);
   const rsrc_t rb = make_rsrc(B + (int64_t)n_tile0 * ldb, tile_len * ldb * 2);  // past the tile: zero
   auto y_rsrc = [&](int i) {
-    const int b = i < len ? uniform(d.perm[pos0 + i]) : -1;
+    const int b = i < nr ? uniform(d.perm[pos0 + i]) : -1;
     const bool ok = (unsigned)b < (unsigned)d.num_rows;  // a stray index touches nothing
     return make_rsrc(m.y + (int64_t)(ok ? b : 0) * m.ldy + n_tile0, ok ? tile_len * 2 : 0u);
   };
+  VStage<kExpandRowGroup> vst;
+  vst.issue(d, m, pos0, nr, rank);  // before the B stream: waiting for v does not wait for B
+  u32x4 bv[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) bv[p] = load_b8(rb, p * G + g, ldb, rank, jq);
+  vst.finish(d, m, scale, v_lds);
   for (int n0 = 0; n0 < (int)tile_len; n0 += SUB) {
-    u32x4 bv[P];
+    for (int i0 = 0; i0 < nr; i0 += YR) {
+      rsrc_t ry[YR];
+      uint16_t yv[YR][PL];
 #pragma unroll
-    for (int p = 0; p < P; ++p) bv[p] = load_b8(rb, n0 + p * G + g, ldb, rank, jq);
-    for (int r0 = 0; r0 < len; r0 += kExpandRowGroup) {
-      const int nr = min(kExpandRowGroup, len - r0);
-      __syncthreads();
-      stage_v<kExpandRowGroup>(d, m, pos0 + r0, nr, rank, scale, v_lds);
-      for (int i0 = 0; i0 < nr; i0 += YR) {
-        rsrc_t ry[YR];
-        uint16_t yv[YR][PL];
+      for (int u = 0; u < YR; ++u) {
+        ry[u] = y_rsrc(i0 + u);
 #pragma unroll
-        for (int u = 0; u < YR; ++u) {
-          ry[u] = y_rsrc(r0 + i0 + u < r0 + nr ? r0 + i0 + u : len);
+        for (int ii = 0; ii < PL; ++ii) yv[u][ii] = buf_ld_u16(ry[u], (uint32_t)(n0 + (ii + PL * q) * G + g) * 2);
+      }
 #pragma unroll
-          for (int ii = 0; ii < PL; ++ii) yv[u][ii] = buf_ld_u16(ry[u], (uint32_t)(n0 + (ii + PL * q) * G + g) * 2);
+      for (int u = 0; u < YR; ++u) {
+        const int i = i0 + u;
+        if (i >= nr) break;
+        float vv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) vv[k] = v_lds[i * 64 + jq + k];
+        const V8Split vs = split_v8(vv);
+        float acc[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) acc[p] = dot8_bf16_split(bv[p], vs, 0.f);
+        reduce_scatter<P, LPR>(acc);
+#pragma unroll
+        for (int ii = 0; ii < PL; ++ii) {
+          const uint32_t off = (uint32_t)(n0 + (ii + PL * q) * G + g) * 2;
+          buf_st_u16(ry[u], off, f32_to_bf16(bf16_to_f32(yv[u][ii]) + acc[ii]));
         }
-#pragma unroll
-        for (int u = 0; u < YR; ++u) {
-          const int i = i0 + u;
-          if (i >= nr) break;
-            float vv[8];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) vv[k] = v_lds[i * 64 + jq + k];
-          const V8Split vs = split_v8(vv);
-          float acc[P];
-#pragma unroll
-          for (int p = 0; p < P; ++p) acc[p] = dot8_bf16_split(bv[p], vs, 0.f);
-          reduce_scatter<P, LPR>(acc);
-#pragma unroll
-          for (int ii = 0; ii < PL; ++ii) {
-            const uint32_t off = (uint32_t)(n0 + (ii + PL * q) * G + g) * 2;
-            buf_st_u16(ry[u], off, f32_to_bf16(bf16_to_f32(yv[u][ii]) + acc[ii]));
-          }
-        }
+        __builtin_amdgcn_sched_barrier(0);  // one row's sums live at a time
       }
     }
+#pragma unroll
+    for (int p = 0; p < P; ++p) bv[p] = load_b8(rb, n0 + SUB + p * G + g, ldb, rank, jq);  // past the tile: zero
   }
 }
 
@@ -229,13 +234,15 @@ __device__ __forceinline__ void decode_expand_one_row(const LayerDesc &d, const 
     const int n = n0 + (ii + PL * q) * G + g;
     return n < tile_len ? (uint32_t)n * 2 : kOutOfRange;
   };
+  VStage<1> vst;
+  vst.issue(d, m, pos0, 1, rank);  // before the B stream: waiting for v does not wait for B
   u32x4 bv[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) bv[p] = b_load(0, p);
   uint16_t yv[PL];
 #pragma unroll
   for (int ii = 0; ii < PL; ++ii) yv[ii] = buf_ld_u16(ry, y_off(0, ii));
-  stage_v<1>(d, m, pos0, 1, rank, scale, v_lds);
+  vst.finish(d, m, scale, v_lds);
   float vv[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) vv[k] = v_lds[jq + k];

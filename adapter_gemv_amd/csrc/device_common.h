@@ -222,87 +222,109 @@ __device__ __forceinline__ bool load_entry(const LayerDesc &d, int a, int col, b
   return true;
 }
 
-// v_lds[i*64 + j] = scale * v[i][j] for the sorted rows p0 + i (i < nr) of
-// a module and j < rank, zero elsewhere in the first ROWS rows; v is the sum
-// of the k-chunk partials (or the caller's v when d.v is set).  A thread
-// loads 4 columns of a row at a time and issues all its loads of a round
-// together, so the staging costs a few memory latencies, not one per chunk.
-// With few rows the chunks are also split across threads and combined in LDS
-// (v_lds needs 64*ROWS + 1024 floats then).  Ends with a block barrier.
+// Staging of v into LDS: v_lds[i*64 + j] = scale * v[i][j] for the sorted
+// rows p0 + i (i < nr) of a module and j < rank, zero elsewhere in the first
+// ROWS rows; v is the sum of the k-chunk partials (or the caller's v when d.v
+// is set).  A thread loads 4 columns of a row at a time.  issue() sends the
+// first round of loads (a round covers U chunks); the caller then issues its
+// own streaming loads, and finish() adds the remaining rounds and writes
+// LDS, so the wait for v does not wait for the caller's stream.  With few
+// rows the chunks are also split across threads and combined in LDS (v_lds
+// needs 64*ROWS + 1024 floats then).  finish() ends with a block barrier.
 template <int ROWS>
-__device__ __forceinline__ void stage_v(const LayerDesc &d, const ModuleDesc &m, int p0, int nr, int rank,
-                                        float scale, float *v_lds) {
-  constexpr int PAIRS = ROWS * 16;  // (row, 4-column group) pairs
-  constexpr int PER = PAIRS >= kDecodeThreads ? PAIRS / kDecodeThreads : 1;
-  constexpr int SPLIT = PAIRS >= kDecodeThreads ? 1 : kDecodeThreads / PAIRS;  // threads per pair
-  constexpr int U = PER >= 4 ? 2 : SPLIT > 1 ? 2 : 8;                           // chunks per round
+struct VStage {
+  static constexpr int PAIRS = ROWS * 16;  // (row, 4-column group) pairs
+  static constexpr int PER = PAIRS >= kDecodeThreads ? PAIRS / kDecodeThreads : 1;
+  static constexpr int SPLIT = PAIRS >= kDecodeThreads ? 1 : kDecodeThreads / PAIRS;  // threads per pair
+  static constexpr int U = PER >= 4 ? 2 : SPLIT > 1 ? 2 : 8;                           // chunks per round
   static_assert(PAIRS % kDecodeThreads == 0 || kDecodeThreads % PAIRS == 0, "rows per stage");
-  const int t = threadIdx.x;
-  const int part = t / PAIRS;  // chunk phase (0 when SPLIT == 1)
-  f32x4_t sum[PER];
+
+  int p0, nr, rank, part;
   int row[PER], jq[PER];
   bool on[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int pair = (t % PAIRS) + k * kDecodeThreads;
-    row[k] = pair >> 4;
-    jq[k] = (pair & 15) * 4;
-    on[k] = row[k] < nr && jq[k] < rank;
-    sum[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  if (d.v != nullptr) {
-    if (part == 0) {
-      f32x4_t got[PER];
-#pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int b = on[k] ? d.perm[p0 + row[k]] : -1;
-        const bool ok = (unsigned)b < (unsigned)d.num_rows;
-        got[k] = *(const f32x4_t *)(ok ? d.v + (int64_t)b * d.ldv + jq[k] : d.v);
-        if (!ok) got[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int k = 0; k < PER; ++k) sum[k] = got[k];
-    }
-  } else {
+  f32x4_t got[U][PER];
+
+  __device__ __forceinline__ void load_round(const LayerDesc &d, const ModuleDesc &m, int c0) {
     const int64_t chunk_stride = (int64_t)d.num_rows * d.rs;
     const float *base = d.part + ((int64_t)m.part_base * d.num_rows + p0) * d.rs;
-    for (int c0 = part; c0 < m.n_chunks; c0 += U * SPLIT) {
-      f32x4_t got[U][PER];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-          const bool ok = on[k] && c0 + u * SPLIT < m.n_chunks;
-          got[u][k] = *(const f32x4_t *)(ok ? base + (c0 + u * SPLIT) * chunk_stride + (int64_t)row[k] * d.rs + jq[k]
-                                            : d.part);
-          if (!ok) got[u][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
+      for (int k = 0; k < PER; ++k) {
+        const bool ok = on[k] && c0 + u * SPLIT < m.n_chunks;
+        got[u][k] = *(const f32x4_t *)(ok ? base + (c0 + u * SPLIT) * chunk_stride + (int64_t)row[k] * d.rs + jq[k]
+                                          : d.part);
+        if (!ok) got[u][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+  }
+
+  __device__ __forceinline__ void issue(const LayerDesc &d, const ModuleDesc &m, int p0_, int nr_, int rank_) {
+    p0 = p0_;
+    nr = nr_;
+    rank = rank_;
+    const int t = threadIdx.x;
+    part = t / PAIRS;  // chunk phase (0 when SPLIT == 1)
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+    for (int k = 0; k < PER; ++k) {
+      const int pair = (t % PAIRS) + k * kDecodeThreads;
+      row[k] = pair >> 4;
+      jq[k] = (pair & 15) * 4;
+      on[k] = row[k] < nr && jq[k] < rank;
+    }
+    if (d.v != nullptr) {
 #pragma unroll
-        for (int k = 0; k < PER; ++k) sum[k] += got[u][k];
+      for (int k = 0; k < PER; ++k) {
+        const int b = on[k] && part == 0 ? d.perm[p0 + row[k]] : -1;
+        const bool ok = (unsigned)b < (unsigned)d.num_rows;
+        got[0][k] = *(const f32x4_t *)(ok ? d.v + (int64_t)b * d.ldv + jq[k] : d.v);
+        if (!ok) got[0][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 1; u < U; ++u) got[u][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    } else {
+      load_round(d, m, part);
     }
   }
-  if constexpr (SPLIT == 1) {
+
+  __device__ __forceinline__ void finish(const LayerDesc &d, const ModuleDesc &m, float scale, float *v_lds) {
+    f32x4_t sum[PER];
 #pragma unroll
-    for (int k = 0; k < PER; ++k)
+    for (int k = 0; k < PER; ++k) {
+      sum[k] = got[0][k];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        v_lds[row[k] * 64 + jq[k] + c] = row[k] < nr && jq[k] + c < rank ? sum[0 + k][c] * scale : 0.f;
-    __syncthreads();
-  } else {
-    float *red = v_lds + ROWS * 64;  // [SPLIT][PAIRS][4]
-    *(f32x4_t *)(red + t * 4) = sum[0];
-    __syncthreads();
-    if (t < PAIRS * 4) {
-      const int i = t >> 6, j = t & 63;
-      float v = 0.f;
-#pragma unroll
-      for (int q = 0; q < SPLIT; ++q) v += red[(q * PAIRS + (t >> 2)) * 4 + (t & 3)];
-      v_lds[i * 64 + j] = i < nr && j < rank ? v * scale : 0.f;
+      for (int u = 1; u < U; ++u) sum[k] += got[u][k];
     }
-    __syncthreads();
+    if (d.v == nullptr) {
+      for (int c0 = part + U * SPLIT; c0 < m.n_chunks; c0 += U * SPLIT) {
+        load_round(d, m, c0);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int k = 0; k < PER; ++k) sum[k] += got[u][k];
+      }
+    }
+    if constexpr (SPLIT == 1) {
+#pragma unroll
+      for (int k = 0; k < PER; ++k)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          v_lds[row[k] * 64 + jq[k] + c] = row[k] < nr && jq[k] + c < rank ? sum[k][c] * scale : 0.f;
+      __syncthreads();
+    } else {
+      const int t = threadIdx.x;
+      float *red = v_lds + ROWS * 64;  // [SPLIT][PAIRS][4]
+      *(f32x4_t *)(red + t * 4) = sum[0];
+      __syncthreads();
+      if (t < PAIRS * 4) {
+        const int i = t >> 6, j = t & 63;
+        float v = 0.f;
+#pragma unroll
+        for (int q = 0; q < SPLIT; ++q) v += red[(q * PAIRS + (t >> 2)) * 4 + (t & 3)];
+        v_lds[i * 64 + j] = i < nr && j < rank ? v * scale : 0.f;
+      }
+      __syncthreads();
+    }
   }
-}
+};
 
 }  // namespace lora

@@ -230,10 +230,13 @@ __device__ __forceinline__ void sgmv_expand_tile(const LayerDesc &d, const Modul
       for (int q = 0; q < NQ; ++q) st.yv[u][q] = buf_ld16(ry, y_off(q, n0), 0);
     }
   };
+  // V rows of the tile (times scale) into LDS, [64][64] fp32; the first
+  // round of its loads goes out before the first register set.
+  VStage<kSgmvExpandRows> vst;
+  vst.issue(d, m, seg0 + row0, nrows, rank);
   Set s0, s1;
-  issue(s0, 0);  // before the V prologue
-  // V rows of the tile (times scale) into LDS: [64][64] fp32.
-  stage_v<kSgmvExpandRows>(d, m, seg0 + row0, nrows, rank, scale, v_lds);
+  issue(s0, 0);
+  vst.finish(d, m, scale, v_lds);
   // All 64 rows as hi/lo bf16 operands: tile q, lane l holds row 16q + l%16,
   // k = 32kt + 8*(l/16) .. +8.
   V8Split vop[NQ][KT];

@@ -71,6 +71,136 @@ def cpu_baseline(w, min_seconds=10.0, max_passes=64):
                       f"host {platform.processor() or platform.machine()}, {os.cpu_count()} logical CPUs"}
 
 
+def rank_class(max_rank):
+    """Template class of the grouped kernels for a launch's largest rank."""
+    return 0 if max_rank <= 8 else 1 if max_rank <= 16 else 2 if max_rank <= 32 else 3
+
+
+def sources_sha256():
+    """Hash of the kernel sources and the ABI header: counter figures taken
+    with other sources no longer describe the kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    files = []
+    for sub in ("adapter_gemv_amd/csrc", "include"):
+        d = os.path.join(ROOT, sub)
+        files += sorted(os.path.join(d, f) for f in os.listdir(d) if f.endswith((".hip", ".h")))
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profile_records():
+    """The machine-readable blocks of the counter summaries in profiles/."""
+    import re
+    out = []
+    d = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(d):
+        return out
+    for f in sorted(os.listdir(d)):
+        if not f.endswith(".md"):
+            continue
+        text = open(os.path.join(d, f)).read()
+        for block in re.findall(r"```json\n(.*?)\n```", text, re.S):
+            try:
+                rec = json.loads(block)
+            except ValueError:
+                continue
+            rec["_file"] = f"profiles/{f}"
+            out.append(rec)
+    return out
+
+
+def counter_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary of
+    this workload, or None when there is none or the kernels have changed
+    since the counters were taken."""
+    digest = sources_sha256()
+    for rec in profile_records():
+        k = rec.get("kernels", {}).get(kernel)
+        if rec.get("workload") == workload and rec.get("sources_sha256") == digest and k and \
+                k.get("bytes_per_launch") is not None:
+            return {"bytes_per_launch": k["bytes_per_launch"], "source": rec["_file"]}
+    return None
+
+
+def _short_kernel_name(name):
+    import re
+    m = re.search(r"(\w+_kernel)(<\d+>)?", name)
+    return (m.group(1) + (m.group(2) or "")) if m else name.strip('"')[:60]
+
+
+def summarize_profile(a):
+    """Markdown summary of one profiled workload from rocprofv3 CSV output:
+    per-kernel durations (kernel trace), FETCH_SIZE / WRITE_SIZE per dispatch
+    scaled by a plain copy of known size, and the algorithmic bytes of the
+    bench line of the traced run."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def csvs(d, pattern):
+        return sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+
+    stats = {}
+    for f in csvs(a.trace, "*kernel_stats.csv"):
+        for r in csv.DictReader(open(f)):
+            stats[_short_kernel_name(r["Name"])] = r
+
+    def counter(d, kernel_filter=None):
+        agg = defaultdict(list)
+        for f in csvs(d, "*counter_collection.csv"):
+            for r in csv.DictReader(open(f)):
+                agg[_short_kernel_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in agg.items()}, {k: len(v) for k, v in agg.items()}
+
+    fetch, n_fetch = counter(a.fetch)
+    write, n_write = counter(a.write)
+    cf, _ = counter(a.copy_fetch)
+    cw, _ = counter(a.copy_write)
+    copy_name = "__amd_rocclr_copyBuffer"
+    copy_kib = a.copy_bytes / 1024.0
+    f_scale = copy_kib / cf[copy_name]
+    w_scale = copy_kib / cw[copy_name]
+    bench = json.loads(open(a.bench_json).read().strip().splitlines()[-1])
+    alg = bench["hbm"]["algorithmic_bytes_per_launch"]
+    lines = [f"# Kernel profile: {bench['config']['name']} ({bench['config']['workload']})", ""]
+    lines += ["Commands, run from the repository root on one MI355X (rocprofv3, ROCm 7):", "", "```"]
+    lines += open(a.commands).read().strip().splitlines() + ["```", ""]
+    lines += ["## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+              "| kernel | calls | avg us | min us | max us | share |", "|---|---:|---:|---:|---:|---:|"]
+    for k, r in sorted(stats.items(), key=lambda kv: -float(kv[1]["TotalDurationNs"])):
+        lines.append(f"| `{k}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    lines += ["", f"Bench events in the traced run: {json.dumps(bench['phases_us'])} us per launch.", ""]
+    lines += ["## HBM bytes (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE; KiB per dispatch)", "",
+              f"Scale: a plain device copy of {a.copy_bytes} bytes reads FETCH_SIZE {cf[copy_name]:.1f} KiB and "
+              f"WRITE_SIZE {cw[copy_name]:.1f} KiB per dispatch, so FETCH_SIZE x {f_scale:.4f} and "
+              f"WRITE_SIZE x {w_scale:.4f} give bytes.", "",
+              "| kernel | dispatches | FETCH KiB | WRITE KiB | HBM bytes / launch | algorithmic bytes / launch | "
+              "ratio |", "|---|---:|---:|---:|---:|---:|---:|"]
+    record = {"workload": bench["config"]["name"], "sources_sha256": sources_sha256(),
+              "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    for k in sorted(fetch):
+        if k not in write or not k.startswith(("lora_", "seg_", "shrink_")):
+            continue
+        b = (fetch[k] * f_scale + write[k] * w_scale) * 1024.0
+        phase = "shrink" if "shrink" in k else "expand" if "expand" in k else None
+        alg_b = alg.get(phase) if phase else None
+        ratio = f"{b / alg_b:.3f}" if alg_b else "-"
+        lines.append(f"| `{k}` | {n_fetch[k]} | {fetch[k]:.1f} | {write[k]:.1f} | {b:.4g} | "
+                     f"{alg_b if alg_b else '-'} | {ratio} |")
+        st = stats.get(k)
+        record["kernels"][k] = {"fetch_kib": round(fetch[k], 1), "write_kib": round(write[k], 1),
+                                "bytes_per_launch": round(b), "algorithmic_bytes_per_launch": alg_b,
+                                "avg_us": round(float(st["AverageNs"]) / 1e3, 2) if st else None}
+    lines += ["", "Machine-readable record (the benchmark reports `traffic` from it while the kernel sources "
+              "hash to `sources_sha256`):", "", "```json", json.dumps(record, indent=1), "```", ""]
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,7 +212,20 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (3 times), to scale HBM byte counters")
+    ap.add_argument("--summarize-profile", action="store_true",
+                    help="only print a markdown summary of rocprofv3 CSV output (needs the options below)")
+    ap.add_argument("--trace", help="rocprofv3 --kernel-trace --stats output directory")
+    ap.add_argument("--fetch", help="rocprofv3 --pmc FETCH_SIZE output directory")
+    ap.add_argument("--write", help="rocprofv3 --pmc WRITE_SIZE output directory")
+    ap.add_argument("--copy-fetch", help="FETCH_SIZE output directory of the copy calibration")
+    ap.add_argument("--copy-write", help="WRITE_SIZE output directory of the copy calibration")
+    ap.add_argument("--copy-bytes", type=int, help="bytes of the copy calibration")
+    ap.add_argument("--bench-json", help="the bench line printed by the traced run")
+    ap.add_argument("--commands", help="text file with the commands that made the profile")
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the design of sharding is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
@@ -114,41 +257,48 @@ def main():
     dws = [DeviceWorkload(w) for _ in range(reps)]
     torch.cuda.synchronize()
 
-    def step(i):
-        dws[i % reps].step()
+    import adapter_gemv_amd as lg
+
+    # Every launch and every event goes on one stream of default priority.
+    stream = torch.cuda.Stream()
+
+    def launch(i, ev=None):
+        d = dws[i % reps]
+        if ev is not None:
+            ev[0].record(stream)
+        d.build_segments(stream)
+        if ev is not None:
+            ev[1].record(stream)
+        lg.layer_shrink(d.ios, w.num_rows, d.table, w.num_slots, d.seg, w.max_rank, d.ws, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        lg.layer_expand(d.ios, w.num_rows, d.table, w.num_slots, d.seg, w.max_rank, d.ws, stream)
+        if ev is not None:
+            ev[3].record(stream)
 
     for i in range(args.warmup):
-        step(i)
+        launch(i)
     torch.cuda.synchronize()
 
-    # ---- whole-step throughput
-    stream = torch.cuda.current_stream()
+    # ---- timed region: K steps between two HIP events on the launch stream.
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(args.steps):
-        step(i)
+        launch(i)
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
     value = w.num_rows / (ms * 1e-3)
     gbps = traffic["total"] / (ms * 1e-3) / 1e9
 
-    # ---- per-launch durations of the two grouped kernels (HIP events on the
-    # launch stream around each launch)
-    import adapter_gemv_amd as lg
+    # ---- the same K steps again with HIP events on the launch stream around
+    # every launch: each kernel's average duration (events between launches
+    # add a few microseconds per step, so the step time above runs without).
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
-        d = dws[i % reps]
-        e = ev[i]
-        e[0].record(stream)
-        d.build_segments()
-        e[1].record(stream)
-        lg.layer_shrink(d.ios, w.num_rows, d.table, w.num_slots, d.seg, w.max_rank, d.ws)
-        e[2].record(stream)
-        lg.layer_expand(d.ios, w.num_rows, d.table, w.num_slots, d.seg, w.max_rank, d.ws)
-        e[3].record(stream)
+        launch(i, ev[i])
     torch.cuda.synchronize()
     seg_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
     shr_us = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
@@ -158,7 +308,8 @@ def main():
     dom = max(("shrink", "expand"), key=lambda k: phases[k][0])
     dom_us, dom_bytes = phases[dom]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    kernel_name = {"shrink": "decode_shrink_kernel", "expand": "decode_expand_kernel"}[dom]
+    kernel_name = f"lora_{dom}_kernel<{rank_class(w.max_rank)}>"
+    counted = counter_traffic(args.workload, kernel_name)
 
     out = {
         "metric": METRIC,
@@ -177,12 +328,17 @@ def main():
                    "distinct_adapters": int(len(np.unique(w.ids[w.ids >= 0]))),
                    "modules": [m.name for m in w.modules], "max_rank": w.max_rank,
                    "adapter_replicas": reps, "parallelism": "single GPU"},
-        "hbm": {"algorithmic_bytes_per_step": traffic["total"], "achieved_gbps": round(gbps, 1),
+        "hbm": {"algorithmic_bytes_per_step": traffic["total"],
+                "algorithmic_bytes_per_launch": {"shrink": traffic["shrink_bytes"],
+                                                 "expand": traffic["expand_bytes"]},
+                "achieved_gbps": round(gbps, 1),
                 "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2), "peak_gbps": PEAK_HBM_GBPS},
         "phases_us": {k: round(v[0], 2) for k, v in phases.items()},
         "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
-                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 2)},
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": counted["bytes_per_launch"] if counted else None,
+                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 2),
+                     "traffic_source": counted["source"] if counted else None},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
