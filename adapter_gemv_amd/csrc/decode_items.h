@@ -234,30 +234,34 @@ __device__ __forceinline__ void decode_expand_one_row(const LayerDesc &d, const 
     const int n = n0 + (ii + PL * q) * G + g;
     return n < tile_len ? (uint32_t)n * 2 : kOutOfRange;
   };
+  // Items start at different sub-tiles (by block index) and wrap around, so
+  // the blocks in flight are not all at the same offset of their tiles.
+  const int rot = blockIdx.x % nsub;
+  auto sub_base = [&](int st) { return st < nsub ? ((st + rot) % nsub) * SUB : tile_len; };
   VStage<1> vst;
   vst.issue(d, m, pos0, 1, rank);  // before the B stream: waiting for v does not wait for B
   u32x4 bv[P];
 #pragma unroll
-  for (int p = 0; p < P; ++p) bv[p] = b_load(0, p);
+  for (int p = 0; p < P; ++p) bv[p] = b_load(sub_base(0), p);
   uint16_t yv[PL];
 #pragma unroll
-  for (int ii = 0; ii < PL; ++ii) yv[ii] = buf_ld_u16(ry, y_off(0, ii));
+  for (int ii = 0; ii < PL; ++ii) yv[ii] = buf_ld_u16(ry, y_off(sub_base(0), ii));
   vst.finish(d, m, scale, v_lds);
   float vv[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) vv[k] = v_lds[jq + k];
   const V8Split vs = split_v8(vv);
   for (int st = 0; st < nsub; ++st) {
-    const int n0 = st * SUB;
+    const int n0 = sub_base(st), n1 = sub_base(st + 1);  // n1 = tile_len after the last: no traffic
     float acc[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       acc[p] = dot8_bf16_split(bv[p], vs, 0.f);
-      bv[p] = b_load(n0 + SUB, p);  // unconditional: a branch here would copy the tile registers
+      bv[p] = b_load(n1, p);  // unconditional: a branch here would copy the tile registers
     }
     uint16_t ynext[PL];
 #pragma unroll
-    for (int ii = 0; ii < PL; ++ii) ynext[ii] = buf_ld_u16(ry, y_off(n0 + SUB, ii));
+    for (int ii = 0; ii < PL; ++ii) ynext[ii] = buf_ld_u16(ry, y_off(n1, ii));
     reduce_scatter<P, LPR>(acc);
 #pragma unroll
     for (int ii = 0; ii < PL; ++ii) {
