@@ -26,11 +26,9 @@ size_t ws_need(int num_rows, int num_slots, int max_rank, int64_t sum_d_in) {  /
 // Work decomposition: the n-tile of the expand (the shrink k-chunk is
 // kKChunkMin).
 int pick_nt(int max_rank) {
-  // One load pass of the expand is 16 loads of 16 bytes per lane (64 KiB
-  // per block) at the table's largest rank; an item streams four passes.
+  // rank / 8 lanes share an output row at the table's largest rank class
   int cls = max_rank <= 8 ? 8 : max_rank <= 16 ? 16 : max_rank <= 32 ? 32 : 64;
-  int lpr = cls / 8;
-  return 4 * 16 * kDecodeThreads / lpr;
+  return decode_expand_tile(cls / 8);
 }
 
 struct ModuleArgs {

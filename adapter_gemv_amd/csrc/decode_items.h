@@ -198,25 +198,33 @@ __device__ __forceinline__ void decode_expand_rows(const LayerDesc &d, const Mod
 }
 
 // The same for a segment of one row (every decode row with its own adapter),
-// streamed: the item covers several
-// sub-tiles of B and each register of the tile is refilled with the next
-// sub-tile's data as soon as its dot product is taken, so 16 loads per lane
-// stay in flight for the whole item.  A load's offset is the lane's offset
-// inside a pass plus a per-pass constant; the sub-tile base goes in the
-// scalar offset.  Lanes past the rank or the tile get an out-of-range lane
-// offset and read zero.
+// streamed: the item covers several sub-tiles of B and each register of the
+// tile is refilled with the next sub-tile's data as soon as its dot product
+// is taken, so 16 loads per lane stay in flight for the whole item.  A load's
+// offset is the lane's offset inside a pass plus a per-pass constant; the
+// sub-tile base goes in the scalar offset.  Lanes past the rank or the tile
+// get an out-of-range lane offset and read zero.
+// y of the whole tile is requested with the first loads, 16 bytes per lane;
+// the sums of each sub-tile go to LDS, and y is written once, after the
+// last load of B.  (A store in the middle of the stream would hold up the
+// loads issued after it: one counter retires loads and stores in order.)
+constexpr int kOneRowDeltaBase = 64 + 1024;  // after the v stage and its reduction space (floats)
+
 template <int LPR>
 __device__ __forceinline__ void decode_expand_one_row(const LayerDesc &d, const ModuleDesc &m,
                                                       const uint16_t *__restrict__ B, int rank, float scale, int pos0,
-                                                      int tile, float *v_lds) {
+                                                      int tile, int item, float *v_lds) {
   constexpr int G = kDecodeThreads / LPR;
   constexpr int P = 16;
   constexpr int SUB = P * G;
   constexpr int PL = P / LPR;
+  constexpr int NT = decode_expand_tile(LPR);
+  static_assert(NT % SUB == 0 && NT % (kDecodeThreads * 8) == 0, "tile");
+  constexpr int YT = NT / (kDecodeThreads * 8);  // 16-byte y pieces per thread
   const int t = threadIdx.x, g = t / LPR, q = t % LPR, jq = q * 8;
   const int n_tile0 = tile * d.nt;
   const int n_tile1 = min(n_tile0 + d.nt, m.d_out);
-  const int tile_len = n_tile1 - n_tile0;
+  const int tile_len = n_tile1 - n_tile0;  // <= NT: the host tiles with the same constant
   const int nsub = (tile_len + SUB - 1) / SUB;
   const int ldb = b_stride(rank);
   const rsrc_t rb = make_rsrc(B + (int64_t)n_tile0 * ldb, (uint32_t)tile_len * ldb * 2);
@@ -230,27 +238,26 @@ __device__ __forceinline__ void decode_expand_one_row(const LayerDesc &d, const 
   const int b = uniform(d.perm[pos0]);
   const bool row_ok = (unsigned)b < (unsigned)d.num_rows;
   const rsrc_t ry = make_rsrc(m.y + (int64_t)(row_ok ? b : 0) * m.ldy + n_tile0, row_ok ? (uint32_t)tile_len * 2 : 0u);
-  auto y_off = [&](int n0, int ii) {
-    const int n = n0 + (ii + PL * q) * G + g;
-    return n < tile_len ? (uint32_t)n * 2 : kOutOfRange;
-  };
-  // Items start at different sub-tiles (by block index) and wrap around, so
+  auto y_col = [&](int i) { return (i * kDecodeThreads + t) * 8; };  // this thread's 8 outputs of piece i
+  auto y_off = [&](int i) { return y_col(i) < tile_len ? (uint32_t)y_col(i) * 2 : kOutOfRange; };
+  // Items start at different sub-tiles (by item index) and wrap around, so
   // the blocks in flight are not all at the same offset of their tiles.
-  const int rot = blockIdx.x % nsub;
+  const int rot = item % nsub;
   auto sub_base = [&](int st) { return st < nsub ? ((st + rot) % nsub) * SUB : tile_len; };
   VStage<1> vst;
   vst.issue(d, m, pos0, 1, rank);  // before the B stream: waiting for v does not wait for B
+  u32x4 yv[YT];
+#pragma unroll
+  for (int i = 0; i < YT; ++i) yv[i] = buf_ld16(ry, y_off(i), 0);
   u32x4 bv[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) bv[p] = b_load(sub_base(0), p);
-  uint16_t yv[PL];
-#pragma unroll
-  for (int ii = 0; ii < PL; ++ii) yv[ii] = buf_ld_u16(ry, y_off(sub_base(0), ii));
   vst.finish(d, m, scale, v_lds);
   float vv[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) vv[k] = v_lds[jq + k];
   const V8Split vs = split_v8(vv);
+  float *delta = v_lds + kOneRowDeltaBase;  // [NT] sums of the tile
   for (int st = 0; st < nsub; ++st) {
     const int n0 = sub_base(st), n1 = sub_base(st + 1);  // n1 = tile_len after the last: no traffic
     float acc[P];
@@ -259,15 +266,20 @@ __device__ __forceinline__ void decode_expand_one_row(const LayerDesc &d, const 
       acc[p] = dot8_bf16_split(bv[p], vs, 0.f);
       bv[p] = b_load(n1, p);  // unconditional: a branch here would copy the tile registers
     }
-    uint16_t ynext[PL];
-#pragma unroll
-    for (int ii = 0; ii < PL; ++ii) ynext[ii] = buf_ld_u16(ry, y_off(n1, ii));
     reduce_scatter<P, LPR>(acc);
 #pragma unroll
-    for (int ii = 0; ii < PL; ++ii) {
-      buf_st_u16(ry, y_off(n0, ii), f32_to_bf16(bf16_to_f32(yv[ii]) + acc[ii]));
-      yv[ii] = ynext[ii];
-    }
+    for (int ii = 0; ii < PL; ++ii) delta[n0 + (ii + PL * q) * G + g] = acc[ii];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < YT; ++i) {
+    const float *src = delta + y_col(i);
+    u32x4 o;
+    o.x = pack_bf16x2(bf16_to_f32(yv[i].x) + src[0], bf16_to_f32(yv[i].x >> 16) + src[1]);
+    o.y = pack_bf16x2(bf16_to_f32(yv[i].y) + src[2], bf16_to_f32(yv[i].y >> 16) + src[3]);
+    o.z = pack_bf16x2(bf16_to_f32(yv[i].z) + src[4], bf16_to_f32(yv[i].z >> 16) + src[5]);
+    o.w = pack_bf16x2(bf16_to_f32(yv[i].w) + src[6], bf16_to_f32(yv[i].w >> 16) + src[7]);
+    buf_st16<kScopeDevice>(ry, y_off(i), o);
   }
 }
 
@@ -287,7 +299,7 @@ __device__ __forceinline__ void decode_expand_block(const LayerDesc &d, int blk,
   if (!load_entry(d, a, m.col, tile == 0, &e)) return;
   const uint16_t *B = static_cast<const uint16_t *>(e.B);
   const int rank = e.rank;
-  if (len == 1) decode_expand_one_row<LPR>(d, m, B, rank, e.scale, pos0, tile, v_lds);
+  if (len == 1) decode_expand_one_row<LPR>(d, m, B, rank, e.scale, pos0, tile, blk, v_lds);
   else decode_expand_rows<LPR>(d, m, B, rank, e.scale, pos0, len, tile, v_lds);
 }
 

@@ -9,6 +9,15 @@
 namespace lora {
 namespace {
 
+// LDS of the expand kernel: the SGMV V tile, or the decode v stage plus two
+// buffers of one sub-tile's sums, whichever is larger (floats).
+template <int LPR>
+constexpr int expand_lds_floats() {
+  constexpr int sgmv = kSgmvExpandRows * 64;
+  constexpr int decode = kOneRowDeltaBase + decode_expand_tile(LPR);
+  return sgmv > decode ? sgmv : decode;
+}
+
 template <int CLS>
 __global__ __launch_bounds__(256) void lora_shrink_kernel(LayerDesc d, int decode_blocks) {
   constexpr int JW = 2 << CLS;                          // A rows per wave (decode)
@@ -19,8 +28,8 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(LayerDesc d, int decod
 
 template <int CLS>
 __global__ __launch_bounds__(256) void lora_expand_kernel(LayerDesc d, int decode_blocks) {
-  __shared__ float lds[kSgmvExpandRows * 64];
   constexpr int LPR = 1 << CLS;                          // lanes per output row (decode)
+  __shared__ float lds[expand_lds_floats<LPR>()];
   constexpr int KT = CLS <= 2 ? 1 : 2;                   // 32-wide rank steps (SGMV)
   if ((int)blockIdx.x < decode_blocks) decode_expand_block<LPR>(d, blockIdx.x, lds);
   else sgmv_expand_block<KT>(d, blockIdx.x - decode_blocks, lds);

@@ -29,6 +29,10 @@ constexpr int kSgmvExpandCols = 2048;
 
 // Threads per block of the decode kernels: 4 waves of 64.
 constexpr int kDecodeThreads = 256;
+// Decode expand n-tile (outputs per item) for LPR = rank class / 8 lanes per
+// output row: 2048 at rank 64, 4096 below (whole sub-tiles of 16 load passes;
+// the item's sums fit in LDS).
+constexpr int decode_expand_tile(int lpr) { return lpr >= 8 ? 2048 : 4096; }
 // Rows staged in LDS per group by the decode expand.
 constexpr int kExpandRowGroup = 16;
 
