@@ -8,11 +8,10 @@
 
 namespace lora {
 
-// Segment builder: one block handles up to this many rows; beyond it the
-// rows are cut into chunks of kSegChunk and two kernels run.
+// Segment builder: one block handles up to kSegSmallMax rows; beyond it the
+// rows are cut into chunks of kSegChunk rows and three kernels run.
 constexpr int kSegSmallMax = 1024;
-constexpr int kSegChunk = 1024;
-constexpr int kSegThreads = 1024;
+constexpr int kSegChunk = 256;
 
 // Decode shrink: k-chunk per work item (the workspace is sized for the
 // smallest chunk the host may pick).

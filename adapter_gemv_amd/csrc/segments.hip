@@ -9,37 +9,40 @@
 // ids are base-only rows and join no segment; ids >= num_slots are counted
 // into the status word and skipped.
 //
-// A row's place inside its segment is the number of earlier rows with the same
-// id.  Each thread finds it by scanning the ids of its block from LDS, and the
-// last row of each id in the block writes the block's count for that id, so no
-// atomics are needed and the result is deterministic.
-//   * up to kSegSmallMax rows: one block does everything (decode batches);
-//   * more rows: one block per chunk of kSegChunk rows writes per-chunk counts
-//     and in-chunk ranks, then one block turns them into offsets and scatters.
+// A row's place inside its group of equal ids is the number of earlier rows
+// with the same id.  Each thread finds it by scanning the ids of its block
+// from LDS, and the last row of each id in the block writes the block's count
+// for that id, so no atomics are needed and the result is deterministic.
+//   * up to kSegSmallMax rows: one block (sized to the batch) does everything;
+//   * more rows: per chunk of kSegChunk rows, counts per slot and in-chunk
+//     ranks; then one block scans the count table in slot-major order, which
+//     gives every (slot, chunk) its first output position and every slot its
+//     segment; then every chunk scatters its rows.
 #include "lora_internal.h"
 
 namespace lora {
 namespace {
 
-constexpr int kWaves = kSegThreads / 64;
-
-// Exclusive scan of one int per thread over the block; *total gets the sum.
+// Exclusive scan of one int per thread over a block of THREADS threads;
+// *total gets the sum.  s_w holds THREADS/64 + 1 ints.
+template <int THREADS>
 __device__ int block_excl_scan(int x, int *total, int *s_w) {
+  constexpr int kWaves = THREADS / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int inc = x;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    int y = __shfl_up(inc, d, 64);
+    const int y = __shfl_up(inc, d, 64);
     if (lane >= d) inc += y;
   }
   if (lane == 63) s_w[w] = inc;
   __syncthreads();
   if (w == 0) {
-    int v = lane < kWaves ? s_w[lane] : 0;
+    const int v = lane < kWaves ? s_w[lane] : 0;
     int vi = v;
 #pragma unroll
     for (int d = 1; d < kWaves; d <<= 1) {
-      int y = __shfl_up(vi, d, 64);
+      const int y = __shfl_up(vi, d, 64);
       if (lane >= d) vi += y;
     }
     if (lane < kWaves) s_w[lane] = vi - v;
@@ -50,40 +53,6 @@ __device__ int block_excl_scan(int x, int *total, int *s_w) {
   *total = s_w[kWaves];
   __syncthreads();
   return res;
-}
-
-__device__ int block_sum(int x, int *s_w) {
-  int total;
-  block_excl_scan(x, &total, s_w);
-  return total;
-}
-
-// counts[a] (rows of slot a) -> exclusive row offsets in place; writes the
-// segment list for every non-empty slot.
-__device__ void scan_slots(int32_t *counts, int num_slots, const lora_segments_t &seg, int *s_w) {
-  int carry_rows = 0, carry_segs = 0;
-  for (int base = 0; base < num_slots; base += kSegThreads) {
-    const int a = base + threadIdx.x;
-    const int c = a < num_slots ? counts[a] : 0;
-    const int f = c > 0;
-    int tot_c, tot_f;
-    const int ex_c = block_excl_scan(c, &tot_c, s_w);
-    const int ex_f = block_excl_scan(f, &tot_f, s_w);
-    if (a < num_slots) {
-      const int start = carry_rows + ex_c;
-      counts[a] = start;
-      if (f) {
-        seg.seg_offsets[carry_segs + ex_f] = start;
-        seg.seg_adapter[carry_segs + ex_f] = a;
-      }
-    }
-    carry_rows += tot_c;
-    carry_segs += tot_f;
-  }
-  if (threadIdx.x == 0) {
-    seg.seg_offsets[carry_segs] = carry_rows;
-    *seg.num_segments = carry_segs;
-  }
 }
 
 // Rows of this block with the same id before / after row t.  s_ids holds the
@@ -107,12 +76,15 @@ __device__ void same_id_counts(const int *s_ids, int len, int t, int id, int *be
 // Slot tables up to this size keep their counts in LDS.
 constexpr int kSegLdsSlots = 8192;
 
-__global__ __launch_bounds__(kSegThreads) void seg_small_kernel(const int32_t *__restrict__ ids, int n,
-                                                                int num_slots, lora_segments_t seg,
-                                                                int32_t *__restrict__ ws_counts) {
-  __shared__ __align__(16) int s_ids[kSegSmallMax];
+// n <= THREADS rows in one block.  Per slot, the low 16 bits of the scanned
+// value count rows and the high 16 bits count non-empty slots (n <= 1024,
+// so neither overflows), so one scan gives row offsets and segment indices.
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void seg_small_kernel(const int32_t *__restrict__ ids, int n, int num_slots,
+                                                            lora_segments_t seg, int32_t *__restrict__ ws_counts) {
+  __shared__ __align__(16) int s_ids[THREADS];
   __shared__ int s_counts[kSegLdsSlots];
-  __shared__ int s_w[kWaves + 1];
+  __shared__ int s_w[THREADS / 64 + 1];
   int32_t *counts = num_slots <= kSegLdsSlots ? s_counts : ws_counts;
   const int t = threadIdx.x;
   int id = -1, bad = 0;
@@ -122,31 +94,51 @@ __global__ __launch_bounds__(kSegThreads) void seg_small_kernel(const int32_t *_
     else if (r >= 0) id = r;
   }
   s_ids[t] = id;
-  for (int a = t; a < num_slots; a += kSegThreads) counts[a] = 0;
-  const int nbad = block_sum(bad, s_w);  // also orders the LDS and count stores
+  for (int a = t; a < num_slots; a += THREADS) counts[a] = 0;
+  int nbad;
+  block_excl_scan<THREADS>(bad, &nbad, s_w);  // also orders the LDS and count stores
   int before = 0, after = 0;
   if (id >= 0) same_id_counts(s_ids, n, t, id, &before, &after);
   if (id >= 0 && after == 0) counts[id] = before + 1;
   __syncthreads();
-  scan_slots(counts, num_slots, seg, s_w);
+  int carry = 0;  // rows | segments << 16 of the slots before this pass
+  for (int base = 0; base < num_slots; base += THREADS) {
+    const int a = base + t;
+    const int c = a < num_slots ? counts[a] : 0;
+    const int v = c | (c > 0 ? 1 << 16 : 0);
+    int tot;
+    const int ex = block_excl_scan<THREADS>(v, &tot, s_w) + carry;
+    if (a < num_slots) {
+      counts[a] = ex & 0xffff;
+      if (c > 0) {
+        seg.seg_offsets[ex >> 16] = ex & 0xffff;
+        seg.seg_adapter[ex >> 16] = a;
+      }
+    }
+    carry += tot;
+  }
+  if (t == 0) {
+    seg.seg_offsets[carry >> 16] = carry & 0xffff;
+    *seg.num_segments = carry >> 16;
+    *seg.status = nbad;
+  }
   __syncthreads();
   if (id >= 0) seg.perm[counts[id] + before] = t;
-  if (t == 0) *seg.status = nbad;
 }
 
-// Per chunk of kSegChunk rows: hist[c][a] = rows of slot a in the chunk,
-// lrank[row] = earlier rows of the same slot in the chunk, bad[c].
-__global__ __launch_bounds__(kSegThreads) void seg_chunk_kernel(const int32_t *__restrict__ ids, int n,
-                                                                int num_slots, int32_t *__restrict__ hist,
-                                                                int32_t *__restrict__ lrank,
-                                                                int32_t *__restrict__ badc) {
+// Chunk c of kSegChunk rows: hist[a * nchunks + c] = rows of slot a in the
+// chunk (slot-major), lrank[row] = earlier rows of the same slot in the
+// chunk, badc[c] = rows with an id >= num_slots.
+__global__ __launch_bounds__(kSegChunk) void seg_chunk_kernel(const int32_t *__restrict__ ids, int n, int num_slots,
+                                                              int nchunks, int32_t *__restrict__ hist,
+                                                              int32_t *__restrict__ lrank,
+                                                              int32_t *__restrict__ badc) {
   __shared__ __align__(16) int s_ids[kSegChunk];
-  __shared__ int s_w[kWaves + 1];
+  __shared__ int s_w[kSegChunk / 64 + 1];
   const int t = threadIdx.x;
   const int c = blockIdx.x;
   const int row = c * kSegChunk + t;
   const int len = min(kSegChunk, n - c * kSegChunk);
-  int32_t *hist_c = hist + (size_t)c * num_slots;
   int id = -1, bad = 0;
   if (t < len) {
     const int r = ids[row];
@@ -154,44 +146,87 @@ __global__ __launch_bounds__(kSegThreads) void seg_chunk_kernel(const int32_t *_
     else if (r >= 0) id = r;
   }
   s_ids[t] = id;
-  for (int a = t; a < num_slots; a += kSegThreads) hist_c[a] = 0;
-  const int nbad = block_sum(bad, s_w);
+  for (int a = t; a < num_slots; a += kSegChunk) hist[(size_t)a * nchunks + c] = 0;
+  int nbad;
+  block_excl_scan<kSegChunk>(bad, &nbad, s_w);  // also orders the zeroing before the counts
   int before = 0, after = 0;
   if (id >= 0) same_id_counts(s_ids, len, t, id, &before, &after);
-  if (id >= 0 && after == 0) hist_c[id] = before + 1;
+  if (id >= 0 && after == 0) hist[(size_t)id * nchunks + c] = before + 1;
   if (id >= 0) lrank[row] = before;
   if (t == 0) badc[c] = nbad;
 }
 
-// One block: chunk counts -> per-(chunk, slot) offsets, segments, scatter.
-__global__ __launch_bounds__(kSegThreads) void seg_finish_kernel(const int32_t *__restrict__ ids, int n,
-                                                                 int num_slots, int nchunks, lora_segments_t seg,
-                                                                 int32_t *__restrict__ hist,
-                                                                 const int32_t *__restrict__ lrank,
-                                                                 const int32_t *__restrict__ badc,
-                                                                 int32_t *__restrict__ start) {
-  __shared__ int s_w[kWaves + 1];
+constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 8;  // consecutive elements per thread and pass
+
+// One block: exclusive scan of hist in slot-major order (the first output
+// position of each (slot, chunk)), then the segments: slot a opens one at
+// hist[a * nchunks] when its rows are non-zero.
+__global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(int num_slots, int nchunks, lora_segments_t seg,
+                                                                int32_t *__restrict__ hist,
+                                                                const int32_t *__restrict__ badc) {
+  __shared__ int s_w[kScanThreads / 64 + 1];
   const int t = threadIdx.x;
-  for (int a = t; a < num_slots; a += kSegThreads) {
-    int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const int h = hist[(size_t)c * num_slots + a];
-      hist[(size_t)c * num_slots + a] = run;
-      run += h;
+  const int64_t total = (int64_t)num_slots * nchunks;
+  int carry = 0;
+  for (int64_t base = 0; base < total; base += (int64_t)kScanThreads * kScanPer) {
+    const int64_t i0 = base + (int64_t)t * kScanPer;
+    int v[kScanPer];
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      v[k] = i0 + k < total ? hist[i0 + k] : 0;
+      sum += v[k];
     }
-    start[a] = run;
+    int tot;
+    int ex = block_excl_scan<kScanThreads>(sum, &tot, s_w) + carry;
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      if (i0 + k < total) hist[i0 + k] = ex;
+      ex += v[k];
+    }
+    carry += tot;
   }
-  int bad = 0;
-  for (int c = t; c < nchunks; c += kSegThreads) bad += badc[c];
-  const int nbad = block_sum(bad, s_w);
-  scan_slots(start, num_slots, seg, s_w);
+  // hist now holds exclusive positions; slot a's rows are [hist[a*nchunks], next slot's).
   __syncthreads();
-  for (int row = t; row < n; row += kSegThreads) {
-    const int id = ids[row];
-    if (id >= 0 && id < num_slots)
-      seg.perm[start[id] + hist[(size_t)(row / kSegChunk) * num_slots + id] + lrank[row]] = row;
+  int bad = 0;
+  for (int c = t; c < nchunks; c += kScanThreads) bad += badc[c];
+  int nbad;
+  block_excl_scan<kScanThreads>(bad, &nbad, s_w);
+  int segs = 0;
+  for (int base = 0; base < num_slots; base += kScanThreads) {
+    const int a = base + t;
+    int first = 0, cnt = 0;
+    if (a < num_slots) {
+      first = hist[(size_t)a * nchunks];
+      const int next = a + 1 < num_slots ? hist[(size_t)(a + 1) * nchunks] : carry;
+      cnt = next - first;
+    }
+    int tot;
+    const int ex = block_excl_scan<kScanThreads>(cnt > 0, &tot, s_w) + segs;
+    if (cnt > 0) {
+      seg.seg_offsets[ex] = first;
+      seg.seg_adapter[ex] = a;
+    }
+    segs += tot;
   }
-  if (t == 0) *seg.status = nbad;
+  if (t == 0) {
+    seg.seg_offsets[segs] = carry;
+    *seg.num_segments = segs;
+    *seg.status = nbad;
+  }
+}
+
+// Chunk c: every valid row goes to its slot's position for this chunk plus
+// its rank inside the chunk.
+__global__ __launch_bounds__(kSegChunk) void seg_scatter_kernel(const int32_t *__restrict__ ids, int n, int num_slots,
+                                                                int nchunks, lora_segments_t seg,
+                                                                const int32_t *__restrict__ hist,
+                                                                const int32_t *__restrict__ lrank) {
+  const int row = blockIdx.x * kSegChunk + threadIdx.x;
+  if (row >= n) return;
+  const int id = ids[row];
+  if (id >= 0 && id < num_slots) seg.perm[hist[(size_t)id * nchunks + blockIdx.x] + lrank[row]] = row;
 }
 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -201,15 +236,19 @@ inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 size_t segments_ws_bytes(int num_rows, int num_slots) {
   if (num_rows <= kSegSmallMax) return num_slots <= kSegLdsSlots ? 0 : align256((size_t)num_slots * 4);
   const size_t nchunks = ((size_t)num_rows + kSegChunk - 1) / kSegChunk;
-  return align256((size_t)num_rows * 4) + align256(nchunks * 4) + align256((size_t)num_slots * 4) +
-         align256(nchunks * (size_t)num_slots * 4);
+  return align256((size_t)num_rows * 4) + align256(nchunks * 4) + align256(nchunks * (size_t)num_slots * 4);
 }
 
 hipError_t launch_build_segments(const int32_t *ids, int n, int num_slots, const lora_segments_t &seg, void *ws,
                                  hipStream_t stream) {
   char *w = static_cast<char *>(ws);
+  if (n <= 256) {
+    seg_small_kernel<256><<<1, 256, 0, stream>>>(ids, n, num_slots, seg, reinterpret_cast<int32_t *>(w));
+    return hipGetLastError();
+  }
   if (n <= kSegSmallMax) {
-    seg_small_kernel<<<1, kSegThreads, 0, stream>>>(ids, n, num_slots, seg, reinterpret_cast<int32_t *>(w));
+    seg_small_kernel<kSegSmallMax><<<1, kSegSmallMax, 0, stream>>>(ids, n, num_slots, seg,
+                                                                  reinterpret_cast<int32_t *>(w));
     return hipGetLastError();
   }
   const int nchunks = (n + kSegChunk - 1) / kSegChunk;
@@ -217,13 +256,14 @@ hipError_t launch_build_segments(const int32_t *ids, int n, int num_slots, const
   w += align256((size_t)n * 4);
   int32_t *badc = reinterpret_cast<int32_t *>(w);
   w += align256((size_t)nchunks * 4);
-  int32_t *start = reinterpret_cast<int32_t *>(w);
-  w += align256((size_t)num_slots * 4);
   int32_t *hist = reinterpret_cast<int32_t *>(w);
-  seg_chunk_kernel<<<nchunks, kSegThreads, 0, stream>>>(ids, n, num_slots, hist, lrank, badc);
+  seg_chunk_kernel<<<nchunks, kSegChunk, 0, stream>>>(ids, n, num_slots, nchunks, hist, lrank, badc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  seg_finish_kernel<<<1, kSegThreads, 0, stream>>>(ids, n, num_slots, nchunks, seg, hist, lrank, badc, start);
+  seg_scan_kernel<<<1, kScanThreads, 0, stream>>>(num_slots, nchunks, seg, hist, badc);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  seg_scatter_kernel<<<nchunks, kSegChunk, 0, stream>>>(ids, n, num_slots, nchunks, seg, hist, lrank);
   return hipGetLastError();
 }
 

@@ -27,7 +27,8 @@ def _name_case(request):
 
 @pytest.mark.parametrize("n,slots,lo,hi", [
     (0, 3, 0, 3), (1, 1, 0, 1), (16, 4, 0, 4), (63, 8, -1, 9), (64, 64, 0, 64), (65, 7, -2, 7),
-    (128, 128, 0, 128), (256, 512, -1, 520), (1000, 5000, -1, 5000), (1024, 3, 0, 3), (1025, 9, -1, 10),
+    (128, 128, 0, 128), (256, 512, -1, 520), (257, 40, -1, 41), (300, 9000, -1, 9001), (513, 2, 0, 2),
+    (1000, 5000, -1, 5000), (1024, 3, 0, 3), (1025, 9, -1, 10), (2000, 10000, 0, 10000),
     (5000, 512, -3, 515), (34816, 32, 0, 32), (40000, 5000, -1, 5001)])
 def test_segments_bit_exact(n, slots, lo, hi):
     ids = np.random.default_rng(n * 7 + slots).integers(lo, hi, size=n).astype(np.int32)
