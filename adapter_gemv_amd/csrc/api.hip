@@ -23,14 +23,6 @@ size_t ws_need(int num_rows, int num_slots, int max_rank, int64_t sum_d_in) {  /
   return a > b ? a : b;
 }
 
-// Work decomposition: the n-tile of the expand (the shrink k-chunk is
-// kKChunkMin).
-int pick_nt(int max_rank) {
-  // rank / 8 lanes share an output row at the table's largest rank class
-  int cls = max_rank <= 8 ? 8 : max_rank <= 16 ? 16 : max_rank <= 32 ? 32 : 64;
-  return decode_expand_tile(cls / 8);
-}
-
 struct ModuleArgs {
   const void *x;
   int64_t ldx;
@@ -40,6 +32,26 @@ struct ModuleArgs {
   int32_t d_out;
   int32_t col;
 };
+
+// Work decomposition: the n-tile of the decode expand.  An item streams
+// about 128 KiB of B (8192 / LPR outputs at LPR = rank class / 8 lanes per
+// output row), capped at the tile the kernel stages in LDS; batches that
+// would give fewer than 2048 items take smaller tiles (down to one sub-tile
+// of 16 load passes), so the work spreads over the device.
+int pick_nt(int max_rank, int64_t max_seg, const ModuleArgs *ms, int n) {
+  const int cls = max_rank <= 8 ? 8 : max_rank <= 16 ? 16 : max_rank <= 32 ? 32 : 64;
+  const int lpr = cls / 8;
+  const int sub = 16 * kDecodeThreads / lpr;
+  int nt = 8192 / lpr < decode_expand_tile(lpr) ? 8192 / lpr : decode_expand_tile(lpr);
+  if (nt < sub) nt = sub;
+  while (nt > sub) {
+    int64_t items = 0;
+    for (int i = 0; i < n; ++i) items += (ms[i].d_out + nt - 1) / nt;
+    if (max_seg * items >= 2048) break;
+    nt /= 2;
+  }
+  return nt;
+}
 
 // Fill the descriptor for a set of modules; items are k-chunks (shrink) or
 // n-tiles (expand).
@@ -55,7 +67,7 @@ void fill_desc(LayerDesc &d, const ModuleArgs *ms, int n, bool shrink, int num_r
                int table_cols, const lora_adapter_entry_t *table, const lora_segments_t &seg, void *ws) {
   d = LayerDesc{};
   d.kc = pick_kc(num_rows);
-  d.nt = pick_nt(max_rank);
+  d.nt = pick_nt(max_rank, num_rows < num_slots ? num_rows : num_slots, ms, n);
   d.sg_nt = kSgmvExpandCols;
   int item = 0, chunk = 0, sg = 0;
   for (int i = 0; i < n; ++i) {
