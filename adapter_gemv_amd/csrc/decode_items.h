@@ -94,7 +94,7 @@ __device__ __forceinline__ void decode_shrink_rows(const LayerDesc &d, const Mod
 // largest rank of the launch (4*JW).
 template <int JW>
 __device__ __forceinline__ void decode_shrink_block(const LayerDesc &d, int blk) {
-  constexpr int RGM = JW >= 16 ? 2 : 4;  // rows of x per pass for multi-row segments
+  constexpr int RGM = 4;  // rows of x per pass for multi-row segments
   const int s = blk / d.items_per_seg;
   if (s >= uniform(*d.num_segments)) return;
   const int it = blk - s * d.items_per_seg;

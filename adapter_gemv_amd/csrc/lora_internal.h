@@ -20,7 +20,7 @@ constexpr int kMaxModules = LORA_NUM_MODULES;
 
 // Segments of at least this many rows go to the matrix-core (SGMV) kernels;
 // shorter ones to the decode kernels.
-constexpr int kLongSegRows = 16;
+constexpr int kLongSegRows = 8;
 // Batches of at least this many rows use a larger shrink k-chunk.
 constexpr int kPrefillRows = 2048;
 // Output columns per SGMV expand block.
