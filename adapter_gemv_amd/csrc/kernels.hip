@@ -18,12 +18,18 @@ constexpr int expand_lds_floats() {
   return sgmv > decode ? sgmv : decode;
 }
 
+// The shrink's LDS also caps the blocks per CU at two (the decode items
+// stream fastest at that occupancy).
+constexpr int kShrinkLdsAlloc = 64 * 1024;
+static_assert(kShrinkLdsBytes <= kShrinkLdsAlloc, "shrink LDS");
+
 template <int CLS>
 __global__ __launch_bounds__(256) void lora_shrink_kernel(LayerDesc d, int decode_blocks) {
+  __shared__ __align__(16) uint8_t lds[kShrinkLdsAlloc];
   constexpr int JW = 2 << CLS;                          // A rows per wave (decode)
   constexpr int NT = CLS <= 1 ? 1 : CLS == 2 ? 2 : 4;   // 16-column rank tiles (SGMV)
   if ((int)blockIdx.x < decode_blocks) decode_shrink_block<JW>(d, blockIdx.x);
-  else sgmv_shrink_block<NT>(d, blockIdx.x - decode_blocks);
+  else sgmv_shrink_block<NT>(d, blockIdx.x - decode_blocks, lds);
 }
 
 template <int CLS>

@@ -78,11 +78,31 @@ __device__ __forceinline__ bool find_long_tile(const LayerDesc &d, int tile, int
 
 // ---------------------------------------------------------------- shrink --
 
-// NT = 16-column tiles of the rank per wave (1, 2 or 4).
+// LDS of the SGMV shrink: two buffers of one round (kShrinkRound k) of the
+// x tile [128 rows] and the A tile [64 rank rows], 16-byte pieces swizzled
+// by row (piece p of row r sits at p ^ (r & 7)), so the matrix-core reads of
+// 16 rows at one k do not collide in one bank.
+constexpr int kShrinkRound = 64;                                  // k per round: 128 bytes of a row
+constexpr int kShrinkXBytes = kSgmvShrinkRows * kShrinkRound * 2;  // 16 KiB
+constexpr int kShrinkABytes = 64 * kShrinkRound * 2;               // 8 KiB
+constexpr int kShrinkBufBytes = kShrinkXBytes + kShrinkABytes;
+constexpr int kShrinkLdsBytes = 2 * kShrinkBufBytes;
+
+__device__ __forceinline__ uint32_t shrink_lds_off(int row, int piece) {
+  return (uint32_t)row * (kShrinkRound * 2) + (uint32_t)((piece ^ (row & 7)) * 16);
+}
+
+// NT = 16-column tiles of the rank (1, 2 or 4).  The block streams x and A
+// through LDS in rounds of 64 k: every thread loads 16-byte pieces with 8
+// threads per 128-byte row segment (whole lines), two rounds ahead in
+// registers; each wave then reads its matrix operands (32 rows x the whole
+// rank) from LDS, so A is read once per block rather than once per wave.
 template <int NT>
-__device__ __forceinline__ void sgmv_shrink_block(const LayerDesc &d, int blk) {
-  constexpr int D = NT >= 2 ? 2 : 4;  // k steps per register set (two sets in flight)
-  const int lane = threadIdx.x & 63, w = wave_id();
+__device__ __forceinline__ void sgmv_shrink_block(const LayerDesc &d, int blk, uint8_t *lds) {
+  constexpr int XL = kSgmvShrinkRows * 8 / 256;  // x pieces per thread per round (4)
+  constexpr int AROWS = NT * 16;
+  constexpr int AL = AROWS * 8 >= 256 ? AROWS * 8 / 256 : 1;  // A pieces per thread per round
+  const int t = threadIdx.x, lane = t & 63, w = wave_id();
   const int tile = blk / d.items_per_seg;
   const int it = blk - tile * d.items_per_seg;
   int s, rt;
@@ -96,63 +116,83 @@ __device__ __forceinline__ void sgmv_shrink_block(const LayerDesc &d, int blk) {
   const int rank = e.rank;
   const int k_begin = chunk * d.kc;
   const int k_end = min(k_begin + d.kc, m.d_in);
-  const int r_in = lane & 15, kq = (lane >> 4) * 8;
-  // x rows of this wave's two 16-row tiles (zero past the segment).
+  const int piece = t & 7;  // this thread's 16-byte piece of a row segment
+  // Rows this thread loads: x rows t/8 + 32i of the tile, A rows t/8 + 32i.
   const rsrc_t rx = make_rsrc(m.x, (uint32_t)((int64_t)d.num_rows * m.ldx * 2));
-  uint32_t xoff[2];
+  uint32_t xoff[XL];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int r = rt * kSgmvShrinkRows + w * 32 + mt * 16 + r_in;
+  for (int i = 0; i < XL; ++i) {
+    const int r = rt * kSgmvShrinkRows + i * 32 + (t >> 3);
     const int b = r < len ? d.perm[seg0 + r] : -1;
-    xoff[mt] = (unsigned)b < (unsigned)d.num_rows ? (uint32_t)((int64_t)b * m.ldx * 2) : kOutOfRange;
+    xoff[i] = (unsigned)b < (unsigned)d.num_rows ? (uint32_t)((int64_t)b * m.ldx * 2) : kOutOfRange;
   }
   const rsrc_t ra = make_rsrc(e.A, (uint32_t)rank * m.d_in * 2);
-  uint32_t aoff[NT];
+  uint32_t aoff[AL];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int j = nt * 16 + r_in;
-    aoff[nt] = j < rank ? (uint32_t)j * m.d_in * 2 : kOutOfRange;
+  for (int i = 0; i < AL; ++i) {
+    const int j = i * 32 + (t >> 3);
+    aoff[i] = j < rank && j < AROWS ? (uint32_t)j * m.d_in * 2 : kOutOfRange;
   }
-  auto load = [&](int k, u32x4(&xv)[2], u32x4(&av)[NT]) {  // past the chunk: zero, no traffic
-    const bool kon = k + kq < k_end;
-    const uint32_t kb = (uint32_t)(k + kq) * 2;
+  struct Stage {
+    u32x4 x[XL], a[AL];
+  };
+  auto load = [&](Stage &st, int k0) {  // one round; past the chunk: zero, no traffic
+    const int k = k0 + piece * 8;
+    const bool kon = k < k_end;
+    const uint32_t kb = (uint32_t)k * 2;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) xv[mt] = buf_ld16(rx, kon && xoff[mt] != kOutOfRange ? xoff[mt] + kb : kOutOfRange, 0);
+    for (int i = 0; i < XL; ++i) st.x[i] = buf_ld16(rx, kon && xoff[i] != kOutOfRange ? xoff[i] + kb : kOutOfRange, 0);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      av[nt] = buf_ld16(ra, kon && aoff[nt] != kOutOfRange ? aoff[nt] + kb : kOutOfRange, 0);
+    for (int i = 0; i < AL; ++i) st.a[i] = buf_ld16(ra, kon && aoff[i] != kOutOfRange ? aoff[i] + kb : kOutOfRange, 0);
+  };
+  auto store = [&](const Stage &st, uint8_t *buf) {
+#pragma unroll
+    for (int i = 0; i < XL; ++i) *(u32x4 *)(buf + shrink_lds_off(i * 32 + (t >> 3), piece)) = st.x[i];
+#pragma unroll
+    for (int i = 0; i < AL; ++i)
+      if (i * 32 + (t >> 3) < AROWS) *(u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(i * 32 + (t >> 3), piece)) = st.a[i];
   };
   f32x4_t acc[2][NT];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  auto mfma_steps = [&](u32x4(&xs)[D][2], u32x4(&as)[D][NT]) {
+  const int r_in = lane & 15, g = lane >> 4;
+  auto compute = [&](const uint8_t *buf) {
 #pragma unroll
-    for (int u = 0; u < D; ++u)
+    for (int ks = 0; ks < kShrinkRound / 32; ++ks) {
+      u32x4 xo[2], ao[NT];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) xo[mt] = *(const u32x4 *)(buf + shrink_lds_off(w * 32 + mt * 16 + r_in, ks * 4 + g));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        ao[nt] = *(const u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(nt * 16 + r_in, ks * 4 + g));
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xs[u][mt]),
-                                                                __builtin_bit_cast(bf16x8_t, as[u][nt]), acc[mt][nt],
-                                                                0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xo[mt]),
+                                                                __builtin_bit_cast(bf16x8_t, ao[nt]), acc[mt][nt], 0,
+                                                                0, 0);
+    }
   };
-  // Ping-pong over two register sets of D k-steps each: the next set's loads
-  // are issued before the current set is consumed, so 2*D steps are in
-  // flight.  Steps past the chunk read zero and add nothing.
-  u32x4 x0[D][2], a0[D][NT], x1[D][2], a1[D][NT];
-#pragma unroll
-  for (int u = 0; u < D; ++u) load(k_begin + 32 * u, x0[u], a0[u]);
-  for (int k = k_begin; k < k_end; k += 64 * D) {
-#pragma unroll
-    for (int u = 0; u < D; ++u) load(k + 32 * (D + u), x1[u], a1[u]);
-    __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the math
-    mfma_steps(x0, a0);
-#pragma unroll
-    for (int u = 0; u < D; ++u) load(k + 32 * (2 * D + u), x0[u], a0[u]);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_steps(x1, a1);
+  // Two rounds in flight in registers; round i is written to buffer i & 1,
+  // one barrier per round.  A buffer is rewritten two rounds after it was
+  // read, and every wave has passed the barrier in between.
+  Stage s0, s1;
+  load(s0, k_begin);
+  load(s1, k_begin + kShrinkRound);
+  const int rounds = (k_end - k_begin + kShrinkRound - 1) / kShrinkRound;
+  for (int r = 0; r < rounds; r += 2) {
+    uint8_t *b0 = lds, *b1 = lds + kShrinkBufBytes;
+    store(s0, b0);
+    load(s0, k_begin + (r + 2) * kShrinkRound);
+    __syncthreads();
+    compute(b0);
+    store(s1, b1);
+    load(s1, k_begin + (r + 3) * kShrinkRound);
+    __syncthreads();
+    compute(b1);
   }
   // C[4*(l/16) + i][l%16] of tile (mt, nt): row 32w + 16mt + 4*(l/16) + i, column 16nt + l%16.
   float *out = d.part + ((int64_t)(m.part_base + chunk) * d.num_rows + seg0) * d.rs;
@@ -160,7 +200,7 @@ __device__ __forceinline__ void sgmv_shrink_block(const LayerDesc &d, int blk) {
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = rt * kSgmvShrinkRows + w * 32 + mt * 16 + (lane >> 4) * 4 + i;
+      const int r = rt * kSgmvShrinkRows + w * 32 + mt * 16 + g * 4 + i;
       if (r < len) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {

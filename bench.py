@@ -196,6 +196,30 @@ def summarize_profile(a):
         record["kernels"][k] = {"fetch_kib": round(fetch[k], 1), "write_kib": round(write[k], 1),
                                 "bytes_per_launch": round(b), "algorithmic_bytes_per_launch": alg_b,
                                 "avg_us": round(float(st["AverageNs"]) / 1e3, 2) if st else None}
+    if getattr(a, "mfma", None):
+        agg = defaultdict(lambda: defaultdict(list))
+        for f in csvs(a.mfma, "*counter_collection.csv"):
+            for r in csv.DictReader(open(f)):
+                agg[_short_kernel_name(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        simds = 1024  # 256 CUs x 4 SIMDs
+        lines += ["", "## Matrix cores (rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES "
+                  "GRBM_GUI_ACTIVE; per dispatch)", "",
+                  "bf16 MFMA flops = MOPS x 512; busy = MFMA busy cycles / (GPU active cycles x 1024 SIMDs); "
+                  "TFLOP/s = flops / the trace's average duration, against 2,500 TFLOP/s dense bf16.", "",
+                  "| kernel | MFMA flops / launch | busy | TFLOP/s | of peak |", "|---|---:|---:|---:|---:|"]
+        for k in sorted(agg):
+            c = agg[k]
+            if not k.startswith("lora_") or "SQ_INSTS_VALU_MFMA_MOPS_BF16" not in c:
+                continue
+            mean = {n: sum(v) / len(v) for n, v in c.items()}
+            flops = mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+            busy = mean.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / max(mean.get("GRBM_GUI_ACTIVE", 1), 1) / simds
+            st = stats.get(k)
+            tf = flops / (float(st["AverageNs"]) * 1e-9) / 1e12 if st else 0.0
+            lines.append(f"| `{k}` | {flops:.4g} | {100 * busy:.1f}% | {tf:.1f} | {100 * tf / 2500:.2f}% |")
+            if k in record["kernels"]:
+                record["kernels"][k].update({"mfma_flops": round(flops), "mfma_busy": round(busy, 4),
+                                             "mfma_tflops": round(tf, 1)})
     lines += ["", "Machine-readable record (the benchmark reports `traffic` from it while the kernel sources "
               "hash to `sources_sha256`):", "", "```json", json.dumps(record, indent=1), "```", ""]
     print("\n".join(lines))
@@ -220,6 +244,8 @@ def main():
     ap.add_argument("--copy-fetch", help="FETCH_SIZE output directory of the copy calibration")
     ap.add_argument("--copy-write", help="WRITE_SIZE output directory of the copy calibration")
     ap.add_argument("--copy-bytes", type=int, help="bytes of the copy calibration")
+    ap.add_argument("--mfma", help="rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES "
+                                   "GRBM_GUI_ACTIVE output directory (optional)")
     ap.add_argument("--bench-json", help="the bench line printed by the traced run")
     ap.add_argument("--commands", help="text file with the commands that made the profile")
     args = ap.parse_args()
