@@ -204,9 +204,11 @@ def summarize_profile(a):
         simds = 1024  # 256 CUs x 4 SIMDs
         lines += ["", "## Matrix cores (rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES "
                   "GRBM_GUI_ACTIVE; per dispatch)", "",
-                  "bf16 MFMA flops = MOPS x 512; busy = MFMA busy cycles / (GPU active cycles x 1024 SIMDs); "
-                  "TFLOP/s = flops / the trace's average duration, against 2,500 TFLOP/s dense bf16.", "",
-                  "| kernel | MFMA flops / launch | busy | TFLOP/s | of peak |", "|---|---:|---:|---:|---:|"]
+                  "bf16 MFMA flops = MOPS x 512; TFLOP/s = flops / the trace's average duration, against 2,500 "
+                  "TFLOP/s dense bf16 (the utilisation figure).  The raw counter ratio MFMA busy cycles / "
+                  "(GRBM_GUI_ACTIVE x 1024 SIMDs) is listed too; its denominator as collected here appears to "
+                  "span all XCDs, so it reads about 8x below the flops-based figure.", "",
+                  "| kernel | MFMA flops / launch | raw busy ratio | TFLOP/s | of peak |", "|---|---:|---:|---:|---:|"]
         for k in sorted(agg):
             c = agg[k]
             if not k.startswith("lora_") or "SQ_INSTS_VALU_MFMA_MOPS_BF16" not in c:
