@@ -57,16 +57,31 @@ int pick_nt(int max_rank, int64_t max_seg, const ModuleArgs *ms, int n) {
 // n-tiles (expand).
 lora_status_t launched(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_ERR_LAUNCH; }
 
-// Shrink k-chunk: small for decode batches (parallelism over few rows),
-// larger for prefill-sized batches (fewer partials to write and sum).
-int pick_kc(int num_rows) { return num_rows >= kPrefillRows ? 2 * kKChunkMin : kKChunkMin; }
+// Shrink k-chunk.  Prefill-sized batches: 2 * kKChunkMin (fewer partials to
+// write and sum).  Decode batches: about 128 KiB of A per item at the
+// launch's rank class (1024 k at rank 64, longer below), halved while the
+// batch would give fewer than 512 items, never below kKChunkMin (the
+// workspace is sized for that chunk).
+int pick_kc(int num_rows, int max_rank, int64_t max_seg, const ModuleArgs *ms, int n) {
+  if (num_rows >= kPrefillRows) return 2 * kKChunkMin;
+  const int cls = max_rank <= 8 ? 8 : max_rank <= 16 ? 16 : max_rank <= 32 ? 32 : 64;
+  int kc = kKChunkMin * (64 / cls);
+  if (kc > 4 * kKChunkMin) kc = 4 * kKChunkMin;
+  while (kc > kKChunkMin) {
+    int64_t items = 0;
+    for (int i = 0; i < n; ++i) items += (ms[i].d_in + kc - 1) / kc;
+    if (max_seg * items >= 512) break;
+    kc /= 2;
+  }
+  return kc;
+}
 
 // Fill the descriptor: items per segment are k-chunks (shrink) or decode
 // n-tiles (expand); sg_* give the SGMV expand n-tiles per row tile.
 void fill_desc(LayerDesc &d, const ModuleArgs *ms, int n, bool shrink, int num_rows, int num_slots, int max_rank,
                int table_cols, const lora_adapter_entry_t *table, const lora_segments_t &seg, void *ws) {
   d = LayerDesc{};
-  d.kc = pick_kc(num_rows);
+  d.kc = pick_kc(num_rows, max_rank, num_rows < num_slots ? num_rows : num_slots, ms, n);
   d.nt = pick_nt(max_rank, num_rows < num_slots ? num_rows : num_slots, ms, n);
   d.sg_nt = kSgmvExpandCols;
   int item = 0, chunk = 0, sg = 0;
