@@ -255,8 +255,8 @@ def main():
         summarize_profile(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the design of sharding is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path. Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -44,10 +44,18 @@
  *  - Host-detectable errors (listed per call) return a status and enqueue
  *    nothing.  Errors in device data never fault: the affected rows or
  *    (segment, projection) pairs are skipped, leaving y unchanged, and the
- *    device status word `*seg.status` becomes nonzero.
+ *    device status word `*seg.status` becomes nonzero.  lora_build_segments
+ *    sets it to the number of rows whose id is >= num_slots; each delta call
+ *    then adds one per segment that does not fit the batch and one per
+ *    (segment, projection) whose table entry cannot be applied (rank above
+ *    max_rank, a null or misaligned factor pointer).  It is a flag and a
+ *    rough count, not a number of rows.
  *  - Dimensions d_in, d_out and leading dimensions are counted in elements;
  *    d_in, d_out, ldx and ldy must be multiples of 8 and x, y pointers
  *    16-byte aligned (16-byte vector access).
+ *  - Each activation matrix (x or y: num_rows * ld * 2 bytes) must stay below
+ *    4 GiB - 256 bytes; the kernels address it with 32-bit byte offsets
+ *    (LORA_ERR_SHAPE otherwise).
  */
 #ifndef LORA_GEMV_H
 #define LORA_GEMV_H
