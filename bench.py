@@ -76,20 +76,13 @@ def rank_class(max_rank):
     return 0 if max_rank <= 8 else 1 if max_rank <= 16 else 2 if max_rank <= 32 else 3
 
 
-def sources_sha256():
-    """Hash of the kernel sources and the ABI header: counter figures taken
-    with other sources no longer describe the kernels."""
+def library_sha256():
+    """Hash of the built library: counter figures taken with another build no
+    longer describe the kernels (the build is reproducible, and comments do
+    not change it)."""
     import hashlib
-    h = hashlib.sha256()
-    files = []
-    for sub in ("adapter_gemv_amd/csrc", "include"):
-        d = os.path.join(ROOT, sub)
-        files += sorted(os.path.join(d, f) for f in os.listdir(d) if f.endswith((".hip", ".h")))
-    for f in files:
-        h.update(os.path.relpath(f, ROOT).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
+    with open(os.path.join(ROOT, "adapter_gemv_amd", "liblora_gemv.so"), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
 
 
 def profile_records():
@@ -115,12 +108,12 @@ def profile_records():
 
 def counter_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary of
-    this workload, or None when there is none or the kernels have changed
+    this workload, or None when there is none or the library has changed
     since the counters were taken."""
-    digest = sources_sha256()
+    digest = library_sha256()
     for rec in profile_records():
         k = rec.get("kernels", {}).get(kernel)
-        if rec.get("workload") == workload and rec.get("sources_sha256") == digest and k and \
+        if rec.get("workload") == workload and rec.get("library_sha256") == digest and k and \
                 k.get("bytes_per_launch") is not None:
             return {"bytes_per_launch": k["bytes_per_launch"], "source": rec["_file"]}
     return None
@@ -181,7 +174,7 @@ def summarize_profile(a):
               f"WRITE_SIZE x {w_scale:.4f} give bytes.", "",
               "| kernel | dispatches | FETCH KiB | WRITE KiB | HBM bytes / launch | algorithmic bytes / launch | "
               "ratio |", "|---|---:|---:|---:|---:|---:|---:|"]
-    record = {"workload": bench["config"]["name"], "sources_sha256": sources_sha256(),
+    record = {"workload": bench["config"]["name"], "library_sha256": library_sha256(),
               "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
     for k in sorted(fetch):
         if k not in write or not k.startswith(("lora_", "seg_", "shrink_")):
@@ -222,8 +215,8 @@ def summarize_profile(a):
             if k in record["kernels"]:
                 record["kernels"][k].update({"mfma_flops": round(flops), "mfma_busy": round(busy, 4),
                                              "mfma_tflops": round(tf, 1)})
-    lines += ["", "Machine-readable record (the benchmark reports `traffic` from it while the kernel sources "
-              "hash to `sources_sha256`):", "", "```json", json.dumps(record, indent=1), "```", ""]
+    lines += ["", "Machine-readable record (the benchmark reports `traffic` from it while the built library "
+              "hashes to `library_sha256`):", "", "```json", json.dumps(record, indent=1), "```", ""]
     print("\n".join(lines))
 
 
