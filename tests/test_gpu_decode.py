@@ -66,11 +66,12 @@ def run_split(dw):
     w = dw.w
     dw.build_segments()
     vs = {}
+    ldv = (w.max_rank + 3) // 4 * 4  # the ABI wants a multiple of 4
     for m in w.modules:
-        v = torch.full((w.num_rows, w.max_rank), float("nan"), dtype=torch.float32, device="cuda")
+        v = torch.full((w.num_rows, ldv), float("nan"), dtype=torch.float32, device="cuda")
         lg.shrink(dw.x[m.x_name], dw.table, w.num_slots, 7, m.index, dw.seg, w.max_rank, v, dw.ws)
         lg.expand(v, dw.table, w.num_slots, 7, m.index, dw.seg, w.max_rank, dw.y[m.name], dw.ws)
-        vs[m.name] = v
+        vs[m.name] = v[:, :w.max_rank]
     return vs
 
 

@@ -1,0 +1,74 @@
+"""Randomised GPU parity sweep over small multi-projection batches.
+
+Each seeded case draws its projections (1 to 3 of q/k/v/o/gate/up/down)
+with dimensions that are multiples of 8 but not of 512.  Slots carry ranks
+in [0, 64] (ranks that are not multiples of 8 included) and random scales.
+A skewed id draw gives short segments (decode path) and long ones
+(matrix-core path) in one batch; base-only rows (id -1) and ids past the
+table are mixed in.  The launch-shape choices the host makes from these
+sizes (k-chunks, n-tiles, which segments go to the matrix cores) are all
+exercised; every case is compared with the oracle on the delta alone, on y,
+and on v through the single-projection calls.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests.parity import note
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+from tests.test_gpu_decode import check_workload  # noqa: E402
+
+RANK_CHOICES = np.array([0, 1, 3, 8, 13, 16, 24, 32, 40, 57, 64])
+
+
+def random_case(seed: int, big: bool = False):
+    rng = np.random.default_rng(7000 + seed)
+    names = list(rng.choice(gen.MODULE_NAMES, size=int(rng.integers(1, 4)), replace=False))
+    dmax = 160 if big else 400
+    shapes = {n: (8 * int(rng.integers(1, dmax)), 8 * int(rng.integers(1, dmax))) for n in names}
+    rows = int(rng.integers(2048, 2600)) if big else int(rng.integers(1, 300))
+    slots = int(rng.integers(1, 40 if big else 200))
+    # skewed popularity: a few slots get long runs of rows
+    p = 1.0 / np.arange(1, slots + 1) ** 1.3
+    p = p[rng.permutation(slots)]
+    ids = rng.choice(slots, size=rows, p=p / p.sum()).astype(np.int32)
+    ids[rng.random(rows) < 0.05] = -1
+    bad = rng.random(rows) < 0.02
+    ids[bad] = slots + rng.integers(0, 5, size=int(bad.sum()))
+    cap = int(rng.choice([8, 16, 32, 64]))  # the launch's rank class varies by case
+    ranks = np.zeros((slots, gen.N_MOD), np.int32)
+    for n in names:
+        ranks[:, gen.MODULE_INDEX[n]] = rng.choice(RANK_CHOICES[RANK_CHOICES <= cap], size=slots)
+    scales = rng.uniform(0.25, 2.0, size=(slots, gen.N_MOD)).astype(np.float32)
+    max_rank = max(1, int(ranks.max()))
+    if rng.random() < 0.3:
+        max_rank = min(64, max_rank + int(rng.integers(1, 16)))  # a launch class above the largest entry
+    w = gen.build_workload(f"sweep{seed}", 7000 + seed, rows, slots, shapes, ids, ranks, x_std=1.0, scales=scales,
+                           max_rank=max_rank)
+    return w
+
+
+@pytest.mark.parametrize("seed", range(14))
+def test_random_layer_case(seed):
+    w = random_case(seed)
+    runner = ("split", "layer", "phases")[seed % 3]
+    note(f"sweep seed {seed}: {w.num_rows} rows, {w.num_slots} slots, "
+         f"{[(m.name, m.d_in, m.d_out) for m in w.modules]}, max_rank {w.max_rank}, runner {runner}")
+    check_workload(w, oracle.lora_layer(w), runner)
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_random_prefill_sized_case(seed):
+    # at least 2048 rows: the prefill-sized chunking, with short and long segments
+    w = random_case(100 + seed, big=True)
+    runner = ("split", "layer")[seed % 2]
+    note(f"sweep big seed {seed}: {w.num_rows} rows, {w.num_slots} slots, "
+         f"{[(m.name, m.d_in, m.d_out) for m in w.modules]}, max_rank {w.max_rank}, runner {runner}")
+    check_workload(w, oracle.lora_layer(w), runner)
