@@ -24,8 +24,10 @@
 //   row and each lane loads 16 bytes.  v (fp32) is split once per row into
 //   bf16 hi + lo, so the products with B run on v_dot2_f32_bf16 without
 //   converting B.  A reduce-scatter over the LPR lanes finishes the dot
-//   products, and the owning lane reads y, adds, rounds to bf16 (RNE) and
-//   writes it back.  Each (row, output) has one writer.
+//   products.  A one-row item collects its sums in LDS and updates y once,
+//   16 bytes per lane, after its last B load; a multi-row item updates y
+//   per row.  y + delta is rounded to bf16 (RNE); each (row, output) has one
+//   writer.
 #pragma once
 
 #include "device_common.h"

@@ -14,17 +14,17 @@
 // stream those once and take the adapter factors (shared by every row tile of
 // a segment) from L2.
 //
-// Matrix-core lane layouts (gfx950, checked on the device):
+// Matrix-core lane layout (gfx950, checked on the device):
 //   v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8*(l/16) .. +8],
 //     B[8*(l/16) .. +8][l%16], and C[4*(l/16) + i][l%16], i < 4.
-//   v_mfma_f32_16x16x16bf16_1k: the same with 4 values of K per lane.
 //
 // Shrink: a block takes 128 rows of one segment and one k-chunk of one
-//   projection; wave w owns rows [32w, 32w+32) as two 16-row tiles and every
-//   rank column; per 32-wide k step a lane loads 16 bytes of x per row tile
-//   and 16 bytes of each A row tile, with D steps in flight (a ring of
-//   registers refilled as each step is consumed).  The chunk's partial V goes
-//   to the workspace layout of the decode shrink ([chunk][sorted row][rank]).
+//   projection.  x and A go through LDS in rounds of 64 k, loaded as whole
+//   128-byte row segments (loading the operand layout straight from memory
+//   touches 16 rows per instruction and has every wave re-read A); wave w
+//   then reads rows [32w, 32w+32) as two 16-row tiles and every rank column
+//   from LDS.  The chunk's partial V goes to the workspace layout of the
+//   decode shrink ([chunk][sorted row][rank]).
 // Expand: a block takes 64 rows of one segment and an n-tile; the chunk
 //   partials of its rows are summed into LDS (times scale), and every wave
 //   turns all 64 rows into matrix operands, splitting each fp32 value v into
@@ -41,7 +41,7 @@
 namespace lora {
 
 constexpr int kSgmvShrinkRows = 128;  // rows per shrink block: 4 waves x 2 tiles of 16
-constexpr int kSgmvExpandRows = 64;   // rows per expand block: 4 waves x 16
+constexpr int kSgmvExpandRows = 64;   // rows per expand block: 4 tiles of 16, all in every wave
 
 // Tile (segment, row tile) of a block among the segments of at least
 // long_min rows, in segment order, `rows` rows per tile: one wave-wide scan
