@@ -28,7 +28,9 @@ MAX_RANK = 64
 MODULES = ("q", "k", "v", "o", "gate", "up", "down")
 
 # lora_adapter_entry_t, 32 bytes
-TABLE_ENTRY_DTYPE = np.dtype([("A", "<u8"), ("B", "<u8"), ("rank", "<i4"), ("scale", "<f4"), ("reserved", "<i8")])
+TABLE_ENTRY_DTYPE = np.dtype([("A", "<u8"), ("B", "<u8"), ("rank", "<i4"), ("scale", "<f4"), ("format", "<i4"),
+                              ("reserved", "<i4")])
+FORMAT_BF16, FORMAT_INT8_ROWS = 0, 1  # lora_factor_format_t
 assert TABLE_ENTRY_DTYPE.itemsize == 32
 
 
@@ -149,14 +151,17 @@ def workspace_bytes(num_rows: int, num_slots: int, max_rank: int, sum_d_in: int)
     return int(lib().lora_workspace_bytes(num_rows, num_slots, max_rank, sum_d_in))
 
 
-def pack_table(A_ptrs, B_ptrs, ranks, scales) -> np.ndarray:
-    """Host bytes of a table of lora_adapter_entry_t; arrays of shape [num_slots, n_mod]."""
+def pack_table(A_ptrs, B_ptrs, ranks, scales, formats=None) -> np.ndarray:
+    """Host bytes of a table of lora_adapter_entry_t; arrays of shape [num_slots, n_mod]
+    (formats: FORMAT_BF16 where omitted)."""
     ranks = np.asarray(ranks)
     t = np.zeros(ranks.shape, TABLE_ENTRY_DTYPE)
     t["A"] = np.asarray(A_ptrs, np.uint64)
     t["B"] = np.asarray(B_ptrs, np.uint64)
     t["rank"] = ranks.astype(np.int32)
     t["scale"] = np.asarray(scales, np.float32)
+    if formats is not None:
+        t["format"] = np.asarray(formats, np.int32)
     return t
 
 

@@ -204,8 +204,8 @@ __device__ __forceinline__ bool load_segment(const LayerDesc &d, int s, bool cou
 
 // Whether a table entry describes a delta this launch can apply.
 __device__ __forceinline__ bool entry_ok(const lora_adapter_entry_t &e, int max_rank) {
-  return e.rank > 0 && e.rank <= max_rank && e.A != nullptr && ((uintptr_t)e.A & 15) == 0 && e.B != nullptr &&
-         ((uintptr_t)e.B & 15) == 0;
+  return e.rank > 0 && e.rank <= max_rank && e.format == LORA_FORMAT_BF16 && e.A != nullptr &&
+         ((uintptr_t)e.A & 15) == 0 && e.B != nullptr && ((uintptr_t)e.B & 15) == 0;
 }
 
 // Table entry of (slot, module) for a whole block (the slot is the same for
@@ -217,6 +217,7 @@ __device__ __forceinline__ bool load_entry(const LayerDesc &d, int a, int col, b
   e->B = uniform(t.B);
   e->rank = uniform(t.rank);
   e->scale = uniform(t.scale);
+  e->format = uniform(t.format);
   e->reserved = 0;
   if (e->rank == 0) return false;
   if (!entry_ok(*e, d.max_rank)) {

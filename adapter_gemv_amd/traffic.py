@@ -13,10 +13,12 @@ from __future__ import annotations
 import numpy as np
 
 
-def step_traffic(ids, num_slots, modules, ranks) -> dict:
+def step_traffic(ids, num_slots, modules, ranks, fmt=None) -> dict:
     """ids: int [rows] (negative = base only, >= num_slots = skipped);
     modules: [(name, table column, d_in, d_out, x tensor name)];
-    ranks: int [num_slots, columns]."""
+    ranks: int [num_slots, columns]; fmt: int [num_slots, columns], 1 where
+    the factors are int8 with one fp32 scale per row (one byte per value
+    plus the scales), else bf16 (two bytes per value)."""
     ids = np.asarray(ids)
     valid = (ids >= 0) & (ids < num_slots)
     slots, counts = np.unique(ids[valid], return_counts=True)
@@ -25,8 +27,10 @@ def step_traffic(ids, num_slots, modules, ranks) -> dict:
     for name, col, d_in, d_out, x_name in modules:
         r = np.asarray(ranks)[slots, col].astype(np.int64)
         on = r > 0
-        a_bytes += int(2 * (r[on] * d_in).sum())
-        b_bytes += int(2 * (r[on] * d_out).sum())
+        q8 = (np.asarray(fmt)[slots, col] == 1) if fmt is not None else np.zeros(r.shape, bool)
+        w = np.where(q8, 1, 2)
+        a_bytes += int((w * r * d_in)[on].sum() + 4 * r[on & q8].sum())
+        b_bytes += int((w * r * d_out)[on].sum() + 4 * d_out * int((on & q8).sum()))
         rows = int(counts[on].sum())
         y_bytes += 4 * rows * d_out
         flops += int((counts[on] * 2 * r[on] * (d_in + d_out)).sum())

@@ -40,7 +40,7 @@ def algorithmic(w):
     split into the shrink side (A, x) and the expand side (B, y)."""
     from adapter_gemv_amd.traffic import step_traffic
     return step_traffic(w.ids, w.num_slots, [(m.name, m.index, m.d_in, m.d_out, m.x_name) for m in w.modules],
-                        w.ranks)
+                        w.ranks, w.fmt)
 
 
 def cpu_baseline(w, min_seconds=10.0, max_passes=64):

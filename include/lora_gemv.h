@@ -91,11 +91,28 @@ typedef enum lora_status {
 } lora_status_t;
 
 /*
+ * Storage format of an entry's factors.
+ *   LORA_FORMAT_BF16       bf16 values (the layout described below).
+ *   LORA_FORMAT_INT8_ROWS  int8 values with one fp32 scale per row, value =
+ *     scale[row] * q[row][col] ("m07 ...", "9. Bottlenecks and Evolution",
+ *     item 3: quantised adapters halve the bytes; symmetric per-row int8 is
+ *     this library's reading).  Each factor is one block, 16-byte aligned:
+ *       A block: float scale[round_up(rank, 4)], then int8 A[rank][d_in];
+ *       B block: float scale[round_up(d_out, 4)], then int8 B[d_out][ldb8],
+ *                ldb8 = rank rounded up to a multiple of 16 (bytes [rank,
+ *                ldb8) of a row are padding and contribute nothing).
+ */
+typedef enum lora_factor_format {
+  LORA_FORMAT_BF16 = 0,
+  LORA_FORMAT_INT8_ROWS = 1
+} lora_factor_format_t;
+
+/*
  * One entry of the device-resident adapter table: the factors of one adapter
  * for one projection ("m07 ...", "2. Scale Numbers" for the shapes).
  * A table is an array of these indexed [slot * n_mod + module].
  *   A      device, bf16 [rank][d_in], row-major, leading dimension d_in,
- *          16-byte aligned.
+ *          16-byte aligned (LORA_FORMAT_BF16; see above for int8).
  *   B      device, bf16 [d_out][ldb], row-major, 16-byte aligned, with
  *          ldb = rank rounded up to a multiple of 8 (so every row is 16-byte
  *          aligned; for ranks 8, 16, 32, 64 B is compact).  Columns
@@ -106,6 +123,7 @@ typedef enum lora_status {
  *          [0, max_rank] is a device-data error.
  *   scale  alpha / r of the forward y = Wx + (B.A)x(alpha/r) ("m07 ...",
  *          "6. Deep Dive A"); 1.0f when the adapter gives no alpha.
+ *   format a lora_factor_format_t; any other value is a device-data error.
  * Slots can live anywhere (fixed-size pages of one pool, separate buffers):
  * row ids index the table, not memory.  32 bytes.
  */
@@ -114,7 +132,8 @@ typedef struct lora_adapter_entry {
   const void *B;
   int32_t rank;
   float scale;
-  int64_t reserved; /* set to 0 */
+  int32_t format;   /* lora_factor_format_t */
+  int32_t reserved; /* set to 0 */
 } lora_adapter_entry_t;
 
 /*

@@ -20,6 +20,9 @@ Functions and the passages they follow:
   projection ("2. Scale Numbers" for the shapes of A and B; "6. Deep Dive A"
   for y = Wx + (B.A)x(alpha/r)).
 * ``lora_layer`` -- the same for every projection in a module mask.
+* int8 factors ("9. Bottlenecks and Evolution" on "m07", item 3: quantised
+  adapters) -- dequantised exactly (one fp32 scale per row), then the same
+  sums.
 """
 from __future__ import annotations
 
@@ -73,7 +76,7 @@ def _configure(lib):
     lib.oracle_lora_module.argtypes = [
         _u16p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
         _u16p, ctypes.c_int64, ctypes.c_int32,
-        _i32p, ctypes.c_int32, _vpp, _vpp, _i32p, _f32p, ctypes.c_int32,
+        _i32p, ctypes.c_int32, _vpp, _vpp, _i32p, _f32p, _i32p, ctypes.c_int32,
         _i32p, ctypes.c_int32, _f64p, _f64p, _f64p, _f64p]
     return lib
 
@@ -115,17 +118,22 @@ class ModuleResult:
     num_bad_rank: int
 
 
+FMT_BF16, FMT_INT8_ROWS = 0, 1
+
+
 def lora_module(x: np.ndarray, y0: np.ndarray, ids: np.ndarray,
                 A_ptrs: np.ndarray, B_ptrs: np.ndarray, ranks: np.ndarray,
                 scales: np.ndarray, max_rank: int, rows=None,
-                keep_alive=()) -> ModuleResult:
+                keep_alive=(), fmts=None) -> ModuleResult:
     """The delta of one projection for the selected rows.
 
     x   uint16 (bf16 bits) [num_rows, >= d_in]; y0 uint16 [num_rows, >= d_out]
-    A_ptrs / B_ptrs: uint64 host addresses, one per slot, of bf16 arrays
-    A [rank, d_in] and B [d_out, rank] (row-major, compact); ranks int32,
-    scales float32, one per slot.  ``keep_alive`` holds the arrays those
-    addresses point into.  ``rows``: row indices to compute (default: all).
+    A_ptrs / B_ptrs: uint64 host addresses, one per slot, of the factors:
+    bf16 A [rank, d_in] and B [d_out, round_up(rank, 8)] (row-major), or,
+    where ``fmts`` says FMT_INT8_ROWS, the int8 blocks described in
+    ``lora_oracle.c``; ranks int32, scales float32, fmts int32 (default all
+    bf16), one per slot.  ``keep_alive`` holds the arrays those addresses
+    point into.  ``rows``: row indices to compute (default: all).
     """
     lib = _load()
     assert x.dtype == np.uint16 and y0.dtype == np.uint16
@@ -144,6 +152,7 @@ def lora_module(x: np.ndarray, y0: np.ndarray, ids: np.ndarray,
     B_ptrs = np.ascontiguousarray(B_ptrs, dtype=np.uint64)
     ranks = np.ascontiguousarray(ranks, dtype=np.int32)
     scales = np.ascontiguousarray(scales, dtype=np.float32)
+    fmts = None if fmts is None else np.ascontiguousarray(fmts, dtype=np.int32)
     n_sel = rows.shape[0]
     v = np.zeros((n_sel, max_rank), np.float64)
     delta = np.zeros((n_sel, d_out), np.float64)
@@ -154,7 +163,7 @@ def lora_module(x: np.ndarray, y0: np.ndarray, ids: np.ndarray,
         _ptr(y0, _u16p), y0.strides[0] // 2, d_out,
         _ptr(ids, _i32p), num_slots,
         A_ptrs.ctypes.data_as(_vpp), B_ptrs.ctypes.data_as(_vpp),
-        _ptr(ranks, _i32p), _ptr(scales, _f32p), max_rank,
+        _ptr(ranks, _i32p), _ptr(scales, _f32p), None if fmts is None else _ptr(fmts, _i32p), max_rank,
         _ptr(rows, _i32p), n_sel, _ptr(v, _f64p), _ptr(delta, _f64p), _ptr(y, _f64p),
         _ptr(scratch, _f64p))
     return ModuleResult(v, delta, y, int(bad))
@@ -171,5 +180,6 @@ def lora_layer(workload, rows=None, modules=None) -> dict:
             continue
         A_ptrs, B_ptrs, ranks, scales = workload.host_table(m.index)
         out[m.name] = lora_module(workload.x[m.x_name], workload.y0[m.name], workload.ids,
-                                  A_ptrs, B_ptrs, ranks, scales, workload.max_rank, rows=rows)
+                                  A_ptrs, B_ptrs, ranks, scales, workload.max_rank, rows=rows,
+                                  fmts=workload.fmt[:, m.index])
     return out

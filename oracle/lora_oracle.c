@@ -33,7 +33,8 @@
  *  - rank 0 means the module is not targeted: zero delta;
  *  - a table rank outside [0, max_rank] is an error: skipped and counted;
  *  - scale (alpha/r) multiplies the delta, 1.0 when unspecified;
- *  - the oracle keeps y in double with no output rounding.
+ *  - the oracle keeps y in double with no output rounding;
+ *  - int8 factors: one fp32 scale per row (see the int8 functions below).
  */
 #include <stdint.h>
 #include <string.h>
@@ -109,28 +110,79 @@ void oracle_expand_row(const double *v, int32_t rank, const uint16_t *B,
 }
 
 /*
+ * Adapters stored in int8 ("m07 -- Multi-Adapter (LoRA) Serving", "9.
+ * Bottlenecks and Evolution", item 3: quantised adapters halve the bytes;
+ * the page fixes no scheme).  Reading taken: symmetric int8 with one fp32
+ * scale per row, value = scale[row] * q[row][col].  A factor block holds the
+ * row scales first (their count rounded up to a multiple of 4, so the int8
+ * values start 16-byte aligned), then the int8 rows:
+ *   A block: float sA[round_up(rank, 4)];  int8 A[rank][d_in]
+ *   B block: float sB[round_up(d_out, 4)]; int8 B[d_out][ldb8],
+ *            ldb8 = round_up(rank, 16) (columns past the rank never read)
+ * Each dequantised value scale * q is exact in double, and so is its product
+ * with a bf16 value.
+ */
+enum { ORACLE_FMT_BF16 = 0, ORACLE_FMT_INT8_ROWS = 1 };
+
+static int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+/* v[j] = sum_k (sA[j] * qA[j][k]) * x[k] for j < rank. */
+void oracle_shrink_row_q8(const uint16_t *x, int32_t d_in, const void *A_block,
+                          int32_t rank, double *v)
+{
+    const float *sa = (const float *)A_block;
+    const int8_t *qa = (const int8_t *)(sa + round_up(rank, 4));
+    for (int32_t j = 0; j < rank; ++j) {
+        double s = 0.0;
+        const int8_t *a = qa + (int64_t)j * d_in;
+        for (int32_t k = 0; k < d_in; ++k)
+            s += ((double)sa[j] * (double)a[k]) * bf16_value(x[k]);
+        v[j] = s;
+    }
+}
+
+/* delta[n] = scale * sum_j (sB[n] * qB[n][j]) * v[j]. */
+void oracle_expand_row_q8(const double *v, int32_t rank, const void *B_block,
+                          int32_t d_out, double scale, double *delta)
+{
+    const float *sb = (const float *)B_block;
+    const int8_t *qb = (const int8_t *)(sb + round_up(d_out, 4));
+    const int64_t ldb8 = round_up(rank, 16);
+    for (int32_t n = 0; n < d_out; ++n) {
+        double s = 0.0;
+        const int8_t *b = qb + (int64_t)n * ldb8;
+        for (int32_t j = 0; j < rank; ++j)
+            s += ((double)sb[n] * (double)b[j]) * v[j];
+        delta[n] = scale * s;
+    }
+}
+
+/*
  * One projection (module) over a set of rows.
  *
  *   x      bf16 [num_rows][ldx]        input rows
  *   y0     bf16 [num_rows][ldy]        base output W.x
  *   ids    int32 [num_rows]            row -> adapter slot (-1 = base only)
  *   A_ptr, B_ptr, rank, scale  [num_slots]   the adapter table for this module
+ *   fmt    int32 [num_slots] or NULL   factor format per slot (NULL: all bf16;
+ *                                      an unknown code is an error, skipped)
  *   rows   int32 [n_sel]               which rows to compute (any order)
  * Outputs, one line per selected row (in the order of `rows`):
  *   v      double [n_sel][max_rank]    shrink result, 0 beyond the rank
  *   delta  double [n_sel][d_out]       scale * B.v   (0 for skipped rows)
  *   y      double [n_sel][d_out]       y0 + delta    (y0 for skipped rows)
  * Any of v, delta, y may be NULL.  Returns the number of selected rows
- * skipped because the table rank is outside [0, max_rank].
+ * skipped because the table rank is outside [0, max_rank] or the format is
+ * unknown.
  */
 int32_t oracle_lora_module(const uint16_t *x, int64_t ldx, int32_t num_rows,
                            int32_t d_in, const uint16_t *y0, int64_t ldy,
                            int32_t d_out, const int32_t *ids, int32_t num_slots,
                            const uint16_t *const *A_ptr,
                            const uint16_t *const *B_ptr, const int32_t *rank,
-                           const float *scale, int32_t max_rank,
-                           const int32_t *rows, int32_t n_sel, double *v,
-                           double *delta, double *y, double *scratch)
+                           const float *scale, const int32_t *fmt,
+                           int32_t max_rank, const int32_t *rows, int32_t n_sel,
+                           double *v, double *delta, double *y, double *scratch)
 {
     int32_t bad = 0;
     /* scratch holds max_rank + d_out doubles */
@@ -141,9 +193,12 @@ int32_t oracle_lora_module(const uint16_t *x, int64_t ldx, int32_t num_rows,
         int32_t a = (b >= 0 && b < num_rows) ? ids[b] : -1;
         int32_t r = 0;
         int ok = 0;
+        int32_t f = ORACLE_FMT_BF16;
         if (a >= 0 && a < num_slots) {
             r = rank[a];
-            if (r < 0 || r > max_rank)
+            f = fmt ? fmt[a] : ORACLE_FMT_BF16;
+            if (r < 0 || r > max_rank ||
+                (r > 0 && f != ORACLE_FMT_BF16 && f != ORACLE_FMT_INT8_ROWS))
                 ++bad;
             else if (r > 0)
                 ok = 1;
@@ -152,9 +207,12 @@ int32_t oracle_lora_module(const uint16_t *x, int64_t ldx, int32_t num_rows,
             vr[j] = 0.0;
         for (int32_t n = 0; n < d_out; ++n)
             dr[n] = 0.0;
-        if (ok) {
+        if (ok && f == ORACLE_FMT_BF16) {
             oracle_shrink_row(x + (int64_t)b * ldx, d_in, A_ptr[a], r, vr);
             oracle_expand_row(vr, r, B_ptr[a], d_out, (double)scale[a], dr);
+        } else if (ok) {
+            oracle_shrink_row_q8(x + (int64_t)b * ldx, d_in, A_ptr[a], r, vr);
+            oracle_expand_row_q8(vr, r, B_ptr[a], d_out, (double)scale[a], dr);
         }
         if (v)
             for (int32_t j = 0; j < max_rank; ++j)

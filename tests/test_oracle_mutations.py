@@ -28,6 +28,14 @@ MUTATIONS = {
     "unstable_segments": ("for (int32_t b = 0; b < num_rows; ++b)\n            if (ids[b] == a)",
                           "for (int32_t b = num_rows - 1; b >= 0; --b)\n            if (ids[b] == a)"),
     "keeps_bad_ids": ("if (ids[b] >= num_slots)\n            ++bad;", "if (ids[b] >= num_slots)\n            bad += 0;"),
+    "q8_no_A_scale": ("s += ((double)sa[j] * (double)a[k]) * bf16_value(x[k]);",
+                      "s += ((double)a[k]) * bf16_value(x[k]); (void)sa;"),
+    "q8_B_scale_by_column": ("s += ((double)sb[n] * (double)b[j]) * v[j];",
+                             "s += ((double)sb[j] * (double)b[j]) * v[j];"),
+    "q8_B_rows_by_rank": ("const int8_t *b = qb + (int64_t)n * ldb8;",
+                          "const int8_t *b = qb + (int64_t)n * rank; (void)ldb8;"),
+    "q8_A_values_after_rank_scales": ("(const int8_t *)(sa + round_up(rank, 4))", "(const int8_t *)(sa + rank)"),
+    "q8_B_values_after_d_out_scales": ("(const int8_t *)(sb + round_up(d_out, 4))", "(const int8_t *)(sb + d_out)"),
 }
 
 CHECKS = [
@@ -39,6 +47,8 @@ CHECKS = [
     (pins.test_merged_weight_identity, {}),
     (pins.test_zero_cases_leave_y_exactly, {}),
     (pins.test_segments_vs_stable_sort, dict(n=257, slots=9, seed=3)),
+    (pins.test_int8_matches_bf16_twin_exactly, dict(d_in=24, d_out=10, rank=5, rows=6, slots=3)),
+    (pins.test_int8_exact_rational, {}),
 ]
 
 

@@ -219,3 +219,79 @@ def test_segments_vs_stable_sort(n, slots, seed):
         assert np.all(ids[rows_s] == seg.seg_adapter[s])
         assert np.all(np.diff(rows_s) > 0)
         assert len(rows_s) == np.count_nonzero(ids == seg.seg_adapter[s])
+
+
+# ---------------------------------------------------------- int8 factors
+# int8 adapters with one fp32 scale per row ("9. Bottlenecks and Evolution"
+# on "m07 -- Multi-Adapter (LoRA) Serving", item 3).  With power-of-two
+# scales every dequantised value is exactly a bf16 value, so the int8 path
+# must give bit for bit what the (pinned) bf16 path gives on the same values.
+
+def int8_bf16_twins(seed, rows, slots, d_in, d_out, rank, ids):
+    from workloads import gen
+    w8 = bw(seed, rows, slots, d_in, d_out, rank, ids, x_std=1.0, fmt=gen.FMT_INT8_ROWS)
+    wb = bw(seed, rows, slots, d_in, d_out, rank, ids, x_std=1.0)
+    rng = np.random.default_rng(seed)
+    for a in range(slots):
+        sa, qa = w8.A_q8(a, 0)
+        sb, qb = w8.B_q8(a, 0)
+        sa[:] = 2.0 ** rng.integers(-9, -3, size=sa.shape)
+        sb[:] = 2.0 ** rng.integers(-9, -3, size=sb.shape)
+        wb.A(a, 0)[:] = bf16_bits(sa[:, None] * qa.astype(np.float32))
+        wb.B(a, 0)[:] = bf16_bits(sb[:, None] * qb.astype(np.float32))
+    return w8, wb
+
+
+@pytest.mark.parametrize("d_in,d_out,rank,rows,slots", [(24, 10, 5, 6, 3), (40, 24, 3, 5, 2), (16, 8, 16, 4, 2)])
+def test_int8_matches_bf16_twin_exactly(d_in, d_out, rank, rows, slots):
+    ids = np.random.default_rng(d_in + rank).integers(-1, slots, size=rows)
+    w8, wb = int8_bf16_twins(d_in * 7 + rank, rows, slots, d_in, d_out, rank, ids)
+    r8, rb = oracle.lora_layer(w8)["q"], oracle.lora_layer(wb)["q"]
+    assert np.array_equal(r8.v, rb.v)
+    assert np.array_equal(r8.delta, rb.delta)
+    assert np.array_equal(r8.y, rb.y)
+    assert np.abs(rb.delta).max() > 0
+
+
+def test_int8_exact_rational():
+    from workloads import gen
+    rows, slots, d_in, d_out, rank = 5, 2, 12, 6, 3
+    ids = np.array([0, 1, 1, 0, 1])
+    w = bw(77, rows, slots, d_in, d_out, rank, ids, x_std=1.0, fmt=gen.FMT_INT8_ROWS,
+           scales=np.full((slots, 7), 0.625, np.float32))
+    res = oracle.lora_layer(w)["q"]
+    for b in range(rows):
+        a = int(ids[b])
+        sa, qa = w.A_q8(a, 0)
+        sb, qb = w.B_q8(a, 0)
+        xf = [Fraction(float(t)) for t in bf16_to_f32(w.x["x"][b])]
+        v = [sum(Fraction(float(sa[j])) * int(qa[j, k]) * xf[k] for k in range(d_in)) for j in range(rank)]
+        d = [Fraction(0.625) * sum(Fraction(float(sb[n])) * int(qb[n, j]) * v[j] for j in range(rank))
+             for n in range(d_out)]
+        assert rel_err(res.v[b, :rank], v) < 1e-12
+        assert rel_err(res.delta[b], d) < 1e-12
+
+
+def test_int8_padding_columns_unused():
+    # the bytes of B past the rank in each row are never read
+    from workloads import gen
+    ids = np.array([0, 1, 0, 1])
+    w = bw(5, 4, 2, 32, 16, 5, ids, x_std=1.0, fmt=gen.FMT_INT8_ROWS)
+    before = oracle.lora_layer(w)["q"]
+    raw = w.pool.view(np.uint8)
+    for a in range(2):
+        o = 2 * int(w.b_off[a, 0]) + 4 * 16
+        full = raw[o:o + 16 * gen.ldb8(5)].reshape(16, gen.ldb8(5))
+        full[:, 5:] = 0x7F
+    after = oracle.lora_layer(w)["q"]
+    assert np.array_equal(before.delta, after.delta)
+
+
+def test_int8_quantiser_round_trip():
+    # the generator's per-row quantiser: |v - s q| <= s / 2, and the largest
+    # magnitude of each row maps to +-127
+    from workloads import gen
+    v = np.random.default_rng(3).standard_normal((9, 33)).astype(np.float32) * 0.02
+    s, q = gen.quantize_rows(v)
+    assert np.all(np.abs(v - s[:, None] * q.astype(np.float32)) <= s[:, None] * (0.5 + 1e-6))
+    assert np.all(np.abs(q).max(axis=1) == 127)

@@ -49,7 +49,8 @@ class DeviceWorkload:
         w = self.w
         A = np.where(w.a_off >= 0, base + 2 * w.a_off, 0).astype(np.uint64)
         B = np.where(w.b_off >= 0, base + 2 * w.b_off, 0).astype(np.uint64)
-        return lg.pack_table(A, B, w.ranks if ranks is None else ranks, w.scales if scales is None else scales)
+        return lg.pack_table(A, B, w.ranks if ranks is None else ranks, w.scales if scales is None else scales,
+                             w.fmt)
 
     def upload_table(self, table_host: np.ndarray):
         self.table.copy_(torch.from_numpy(table_host.view(np.uint8).reshape(-1).copy()).to(self.device))

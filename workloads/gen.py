@@ -117,6 +117,11 @@ class Workload:
     scales: np.ndarray               # float32 [num_slots, N_MOD]
     seq_lens: np.ndarray | None = None
     notes: dict = field(default_factory=dict)
+    fmt: np.ndarray | None = None    # int32 [num_slots, N_MOD]: FMT_BF16 or FMT_INT8_ROWS
+
+    def __post_init__(self):
+        if self.fmt is None:
+            self.fmt = np.zeros((self.num_slots, N_MOD), np.int32)
 
     @property
     def module_mask(self) -> int:
@@ -132,6 +137,7 @@ class Workload:
         raise KeyError(name)
 
     def A(self, slot: int, col: int) -> np.ndarray:
+        assert self.fmt[slot, col] == FMT_BF16
         r = int(self.ranks[slot, col])
         d_in = self._spec_col(col).d_in
         o = int(self.a_off[slot, col])
@@ -139,10 +145,33 @@ class Workload:
 
     def B(self, slot: int, col: int) -> np.ndarray:
         """[d_out, rank] view (rows ldb(rank) apart in the pool)."""
+        assert self.fmt[slot, col] == FMT_BF16
         r = int(self.ranks[slot, col])
         d_out = self._spec_col(col).d_out
         o = int(self.b_off[slot, col])
         return self.pool[o:o + d_out * ldb(r)].reshape(d_out, ldb(r))[:, :r]
+
+    def A_q8(self, slot: int, col: int):
+        """int8 A: (row scales float32 [rank], values int8 [rank, d_in])."""
+        assert self.fmt[slot, col] == FMT_INT8_ROWS
+        r = int(self.ranks[slot, col])
+        d_in = self._spec_col(col).d_in
+        raw = self.pool.view(np.uint8)[2 * int(self.a_off[slot, col]):]
+        sa = raw[:4 * r].view(np.float32)
+        q = raw[4 * _align(r, 4):4 * _align(r, 4) + r * d_in].view(np.int8).reshape(r, d_in)
+        return sa, q
+
+    def B_q8(self, slot: int, col: int):
+        """int8 B: (row scales float32 [d_out], values int8 [d_out, rank] view;
+        rows ldb8(rank) bytes apart)."""
+        assert self.fmt[slot, col] == FMT_INT8_ROWS
+        r = int(self.ranks[slot, col])
+        d_out = self._spec_col(col).d_out
+        raw = self.pool.view(np.uint8)[2 * int(self.b_off[slot, col]):]
+        sb = raw[:4 * d_out].view(np.float32)
+        o = 4 * _align(d_out, 4)
+        q = raw[o:o + d_out * ldb8(r)].view(np.int8).reshape(d_out, ldb8(r))[:, :r]
+        return sb, q
 
     def _spec_col(self, col):
         for s in self.modules:
@@ -158,9 +187,9 @@ class Workload:
         return a, b, self.ranks[:, col].copy(), self.scales[:, col].copy()
 
     def adapter_bytes_used(self) -> int:
-        """bf16 bytes of A and B at their ranks (padding not counted)."""
-        return 2 * int(sum(self.ranks[a, s.index] * (s.d_in + s.d_out)
-                           for s in self.modules for a in range(self.num_slots)))
+        """Bytes of A and B at their ranks and formats (padding not counted)."""
+        return int(sum(entry_bytes(int(self.ranks[a, s.index]), s.d_in, s.d_out, int(self.fmt[a, s.index]))
+                       for s in self.modules for a in range(self.num_slots)))
 
 
 def ldb(rank: int) -> int:
@@ -168,17 +197,81 @@ def ldb(rank: int) -> int:
     return (int(rank) + 7) // 8 * 8
 
 
-def _fill_adapters(seed, pool, modules, ranks, a_off, b_off, ab_std, slots):
+# Factor formats of a table entry.  FMT_INT8_ROWS: symmetric int8 with one
+# fp32 scale per row ("9. Bottlenecks and Evolution" on "m07 -- Multi-Adapter
+# (LoRA) Serving", item 3, fixes no scheme; this is the reading taken).  A
+# block: float scales[round_up(rank, 4)], then int8 A[rank][d_in]; B block:
+# float scales[round_up(d_out, 4)], then int8 B[d_out][ldb8(rank)].
+FMT_BF16, FMT_INT8_ROWS = 0, 1
+
+
+def ldb8(rank: int) -> int:
+    """Row stride (bytes) of an int8 B: the rank rounded up to a multiple of 16."""
+    return (int(rank) + 15) // 16 * 16
+
+
+def entry_bytes(rank: int, d_in: int, d_out: int, fmt: int) -> int:
+    """Bytes the method reads for one (adapter, projection) at its rank."""
+    if rank <= 0:
+        return 0
+    if fmt == FMT_INT8_ROWS:
+        return rank * (d_in + d_out) + 4 * (rank + d_out)
+    return 2 * rank * (d_in + d_out)
+
+
+def _block_elems(rank: int, d_in: int, d_out: int, fmt: int):
+    """(A, B) block sizes in uint16 pool elements."""
+    if fmt == FMT_INT8_ROWS:
+        a = 4 * _align(rank, 4) + rank * d_in
+        b = 4 * _align(d_out, 4) + d_out * ldb8(rank)
+        return (a + 1) // 2, (b + 1) // 2
+    return rank * d_in, d_out * ldb(rank)
+
+
+def quantize_rows(v: np.ndarray):
+    """Symmetric int8 per row: scale = max|row| / 127 (float32), q = round(v /
+    scale) (ties to even), clamped to [-127, 127]; rows of zeros get scale 0."""
+    v = np.asarray(v, np.float32)
+    m = np.abs(v).max(axis=1)
+    scale = (m / np.float32(127.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0))
+    q = np.clip(np.rint(v / safe[:, None]), -127, 127).astype(np.int8)
+    return scale, q
+
+
+def _fill_adapters(seed, pool, modules, ranks, a_off, b_off, ab_std, slots, fmt=None):
     jobs = []
     for a in slots:
         for s in modules:
             r = int(ranks[a, s.index])
             if r > 0:
                 jobs.append((a, s, r))
+    raw = pool.view(np.uint8)
+
+    def fill_q8(a, s, r, oa, ob):
+        # the same draws as the bf16 factors, quantised per row
+        av = bf16_to_f32(normal_bf16(seed, (_R_A, a, s.index), r * s.d_in, ab_std)).reshape(r, s.d_in)
+        bv = bf16_to_f32(normal_bf16(seed, (_R_B, a, s.index), s.d_out * r, ab_std)).reshape(s.d_out, r)
+        sa, qa = quantize_rows(av)
+        sb, qb = quantize_rows(bv)
+        o = 2 * oa
+        raw[o:o + 4 * r] = sa.view(np.uint8)
+        o += 4 * _align(r, 4)
+        raw[o:o + r * s.d_in] = qa.reshape(-1).view(np.uint8)
+        o = 2 * ob
+        raw[o:o + 4 * s.d_out] = sb.view(np.uint8)
+        o += 4 * _align(s.d_out, 4)
+        lb = ldb8(r)
+        full = raw[o:o + s.d_out * lb].reshape(s.d_out, lb)
+        full[:, :r] = qb.view(np.uint8)
+        if lb > r:  # padding: random bytes that no computation may use
+            full[:, r:] = _rng(seed, _R_PAD, a, s.index).integers(0, 256, size=(s.d_out, lb - r), dtype=np.uint8)
 
     def fill(job):
         a, s, r = job
         oa, ob = int(a_off[a, s.index]), int(b_off[a, s.index])
+        if fmt is not None and fmt[a, s.index] == FMT_INT8_ROWS:
+            return fill_q8(a, s, r, oa, ob)
         normal_bf16(seed, (_R_A, a, s.index), r * s.d_in, ab_std, out=pool[oa:oa + r * s.d_in])
         lb = ldb(r)
         if lb == r:
@@ -199,7 +292,7 @@ def _align(n, a=64):
 def build_workload(name, seed, num_rows, num_slots, shapes: dict, ids, ranks,
                    x_of=None, x_std=1.0, ab_std=0.02, y_std=1.0, scales=None,
                    paged_capacity_rank=None, placement=None, seq_lens=None,
-                   ab_fill=None, max_rank=None):
+                   ab_fill=None, max_rank=None, fmt=None):
     """Assemble a workload.
 
     shapes: {module name: (d_in, d_out)}; ranks: int array [num_slots, N_MOD]
@@ -207,6 +300,8 @@ def build_workload(name, seed, num_rows, num_slots, shapes: dict, ids, ranks,
     With ``paged_capacity_rank`` every slot is a fixed-size page sized for that
     rank and adapter a lives in page ``placement[a]``.
     ``ab_fill``: optional callable(workload) replacing the random A/B values.
+    ``fmt``: factor format per (slot, column), or one code for all
+    (FMT_BF16 default; FMT_INT8_ROWS quantises the same draws per row).
     """
     modules = [ModuleSpec(n, MODULE_INDEX[n], shapes[n][0], shapes[n][1],
                           (x_of or {}).get(n, "x_" + n)) for n in MODULE_NAMES if n in shapes]
@@ -216,6 +311,7 @@ def build_workload(name, seed, num_rows, num_slots, shapes: dict, ids, ranks,
         max_rank = max(1, int(ranks.max()))
     if scales is None:
         scales = np.ones((num_slots, N_MOD), np.float32)
+    fmt = np.broadcast_to(np.asarray(FMT_BF16 if fmt is None else fmt, np.int32), (num_slots, N_MOD)).copy()
     a_off = np.full((num_slots, N_MOD), -1, np.int64)
     b_off = np.full((num_slots, N_MOD), -1, np.int64)
     if paged_capacity_rank is None:
@@ -224,18 +320,21 @@ def build_workload(name, seed, num_rows, num_slots, shapes: dict, ids, ranks,
             for s in modules:
                 r = int(ranks[a, s.index])
                 if r > 0:
+                    ea, eb = _block_elems(r, s.d_in, s.d_out, int(fmt[a, s.index]))
                     a_off[a, s.index] = pos
-                    pos = _align(pos + r * s.d_in)
+                    pos = _align(pos + ea)
                     b_off[a, s.index] = pos
-                    pos = _align(pos + s.d_out * ldb(r))
+                    pos = _align(pos + eb)
         pool = np.zeros(max(pos, 64), np.uint16)
     else:
         cap = int(paged_capacity_rank)
         region = {}
         page = 0
         for s in modules:
-            region[s.name] = (page, _align(page + cap * s.d_in))
-            page = _align(region[s.name][1] + s.d_out * cap)
+            ea = max(_block_elems(cap, s.d_in, s.d_out, f)[0] for f in (FMT_BF16, FMT_INT8_ROWS))
+            eb = max(_block_elems(cap, s.d_in, s.d_out, f)[1] for f in (FMT_BF16, FMT_INT8_ROWS))
+            region[s.name] = (page, _align(page + ea))
+            page = _align(region[s.name][1] + eb)
         page_elems = page
         pool = np.zeros(page_elems * num_slots, np.uint16)
         for a in range(num_slots):
@@ -247,7 +346,7 @@ def build_workload(name, seed, num_rows, num_slots, shapes: dict, ids, ranks,
     w = Workload(name=name, seed=seed, num_rows=num_rows, num_slots=num_slots, max_rank=max_rank,
                  ids=np.asarray(ids, dtype=np.int32), modules=modules, x={}, y0={}, pool=pool,
                  a_off=a_off, b_off=b_off, ranks=ranks, scales=np.asarray(scales, np.float32),
-                 seq_lens=seq_lens)
+                 seq_lens=seq_lens, fmt=fmt)
     xd = {}
     for s in modules:
         xd.setdefault(s.x_name, s.d_in)
@@ -257,7 +356,7 @@ def build_workload(name, seed, num_rows, num_slots, shapes: dict, ids, ranks,
     for s in modules:
         w.y0[s.name] = normal_bf16(seed, (_R_Y, s.index), num_rows * s.d_out, y_std).reshape(num_rows, s.d_out)
     if ab_fill is None:
-        _fill_adapters(seed, pool, modules, ranks, a_off, b_off, ab_std, range(num_slots))
+        _fill_adapters(seed, pool, modules, ranks, a_off, b_off, ab_std, range(num_slots), fmt)
     else:
         ab_fill(w)
     return w
@@ -285,12 +384,14 @@ def q_proj(seed=2, rank=16, rows=128):
                           ranks, x_of={"q": "x"}, x_std=1.0, ab_std=0.02, y_std=1.0)
 
 
-def full_layer(seed=3, rank=64, rows=128):
-    """70B layer, all seven projections at one rank, one distinct adapter per row."""
+def full_layer(seed=3, rank=64, rows=128, fmt=FMT_BF16):
+    """70B layer, all seven projections at one rank, one distinct adapter per row
+    (fmt=FMT_INT8_ROWS: the same draws quantised to int8 per row)."""
     ids = _rng(seed, _R_IDS).permutation(rows)
     ranks = np.full((rows, N_MOD), rank, np.int32)
-    return build_workload(f"full_layer_r{rank}_b{rows}", seed, rows, rows, SHAPES_70B, ids, ranks,
-                          x_of=X_OF_70B, x_std=1.0, ab_std=0.02, y_std=1.0)
+    tag = "_int8" if fmt == FMT_INT8_ROWS else ""
+    return build_workload(f"full_layer_r{rank}_b{rows}{tag}", seed, rows, rows, SHAPES_70B, ids, ranks,
+                          x_of=X_OF_70B, x_std=1.0, ab_std=0.02, y_std=1.0, fmt=fmt)
 
 
 def zipf_ids(seed, num_rows, num_slots, s=1.1):
@@ -335,7 +436,7 @@ def prefill(seed=5, rank=16, num_seqs=32, lo=128, hi=2048):
 
 
 def build_workload_for_tests(seed, rows, slots, d_in, d_out, rank, ids, ranks=None, scales=None,
-                             x_std=0.02, ab_fill=None, ab_fill_after=None, max_rank=None):
+                             x_std=0.02, ab_fill=None, ab_fill_after=None, max_rank=None, fmt=None):
     """A single-projection ("q", table column 0) workload of any small shape.
 
     ``rank`` gives every slot the same rank unless ``ranks`` [slots, 7] is
@@ -347,7 +448,7 @@ def build_workload_for_tests(seed, rows, slots, d_in, d_out, rank, ids, ranks=No
         ranks[:, 0] = rank
     w = build_workload(f"test_{rows}x{d_in}x{d_out}", seed, rows, slots, {"q": (d_in, d_out)},
                        np.asarray(ids), ranks, x_of={"q": "x"}, x_std=x_std, ab_std=0.02, y_std=1.0,
-                       scales=scales, ab_fill=ab_fill, max_rank=max_rank)
+                       scales=scales, ab_fill=ab_fill, max_rank=max_rank, fmt=fmt)
     if ab_fill_after is not None:
         ab_fill_after(w)
     return w
@@ -360,6 +461,7 @@ WORKLOADS = {
     "zipf_paged": zipf_paged,
     "prefill_r16": lambda seed=5: prefill(seed, rank=16),
     "prefill_r64": lambda seed=5: prefill(seed, rank=64),
+    "full_layer_r64_int8": lambda seed=3: full_layer(seed, fmt=FMT_INT8_ROWS),
 }
 
 
