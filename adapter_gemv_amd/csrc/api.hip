@@ -33,16 +33,17 @@ struct ModuleArgs {
   int32_t col;
 };
 
-// Work decomposition: the n-tile of the decode expand.  An item streams
-// about 128 KiB of B (8192 / LPR outputs at LPR = rank class / 8 lanes per
-// output row), capped at the tile the kernel stages in LDS; batches that
-// would give fewer than 2048 items take smaller tiles (down to one sub-tile
-// of 16 load passes), so the work spreads over the device.
+// Work decomposition: the n-tile of the decode expand.  An item takes the
+// largest tile the kernel stages in LDS (2048 outputs at rank class 64, 4096
+// below: 256 KiB of bf16 B at the class's rank, half that in int8, where the
+// fixed cost of an item weighs more); batches that would give fewer than 2048
+// items take smaller tiles (down to one sub-tile of 16 load passes), so the
+// work spreads over the device.
 int pick_nt(int max_rank, int64_t max_seg, const ModuleArgs *ms, int n) {
   const int cls = max_rank <= 8 ? 8 : max_rank <= 16 ? 16 : max_rank <= 32 ? 32 : 64;
   const int lpr = cls / 8;
   const int sub = 16 * kDecodeThreads / lpr;
-  int nt = 8192 / lpr < decode_expand_tile(lpr) ? 8192 / lpr : decode_expand_tile(lpr);
+  int nt = decode_expand_tile(lpr);
   if (nt < sub) nt = sub;
   while (nt > sub) {
     int64_t items = 0;

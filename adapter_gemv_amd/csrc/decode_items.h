@@ -30,6 +30,8 @@
 //   writer.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace lora {
@@ -38,16 +40,22 @@ namespace lora {
 
 // Wave w owns rows [w*jw, w*jw + jw) of A with jw = ceil(rank / 4) <= JW, so
 // all waves share the stream whatever the entry's rank.  RG rows of x are
-// processed together.
-template <int JW, int RG>
-__device__ __forceinline__ void decode_shrink_rows(const LayerDesc &d, const ModuleDesc &m,
-                                                   const uint16_t *__restrict__ A, int rank, int jw, int pos0,
-                                                   int nrows, int chunk) {
+// processed together.  Q8: A is int8 with one fp32 scale per row; a lane
+// takes 16 values of a row per step (one 16-byte load, widened to bf16 in
+// registers) against two 16-byte pieces of x, and the row scale multiplies
+// the chunk's sum.  int8 rows are padded to 16 bytes, so the load stays in
+// its row; where d_in ends inside it, the second x piece lies past the row
+// of x and reads zero, and the padding bytes (always finite) add nothing.
+template <int JW, int RG, bool Q8>
+__device__ __forceinline__ void decode_shrink_rows(const LayerDesc &d, const ModuleDesc &m, const void *A, int rank,
+                                                   int jw, int pos0, int nrows, int chunk) {
+  constexpr int VPL = Q8 ? 16 : 8;  // k per lane and step
   const int lane = threadIdx.x & 63;
   const int j0 = wave_id() * jw;
   const int k_begin = chunk * d.kc;
   const int k_end = min(k_begin + d.kc, m.d_in);
   const uint32_t row_bytes = (uint32_t)m.d_in * 2;
+  const uint32_t a_row_bytes = Q8 ? lda8_of(m.d_in) : row_bytes;
   rsrc_t rx[RG];
 #pragma unroll
   for (int r = 0; r < RG; ++r) {
@@ -55,39 +63,61 @@ __device__ __forceinline__ void decode_shrink_rows(const LayerDesc &d, const Mod
     const bool ok = (unsigned)b < (unsigned)d.num_rows;  // a stray index reads zeros
     rx[r] = make_rsrc(m.x + (int64_t)(ok ? b : 0) * m.ldx, ok ? row_bytes : 0u);
   }
-  const rsrc_t ra = make_rsrc(A, (uint32_t)rank * row_bytes);
+  const uint8_t *a_vals = static_cast<const uint8_t *>(A) + (Q8 ? q8_values_offset(rank) : 0);
+  const rsrc_t ra = make_rsrc(a_vals, (uint32_t)rank * a_row_bytes);
   float acc[JW * RG];
 #pragma unroll
   for (int i = 0; i < JW * RG; ++i) acc[i] = 0.f;
-  for (int k = k_begin + lane * 8; k < k_end; k += 512) {
+  for (int k = k_begin + lane * VPL; k < k_end; k += 64 * VPL) {
     const uint32_t voff = (uint32_t)k * 2;
     u32x4 xv[RG], av[JW];
 #pragma unroll
     for (int r = 0; r < RG; ++r) xv[r] = r < nrows ? buf_ld16(rx[r], voff, 0) : zero4();
+    if constexpr (Q8) {
+      u32x4 xw[RG];  // x[k + 8, k + 16)
 #pragma unroll
-    for (int jj = 0; jj < JW; ++jj)
-      av[jj] = (jj < jw && j0 + jj < rank) ? buf_ld16_stream(ra, voff, (uint32_t)(j0 + jj) * row_bytes) : zero4();
+      for (int r = 0; r < RG; ++r) xw[r] = r < nrows ? buf_ld16(rx[r], voff + 16, 0) : zero4();
+      u32x4 aq[JW];
 #pragma unroll
-    for (int jj = 0; jj < JW; ++jj)
+      for (int jj = 0; jj < JW; ++jj)
+        aq[jj] = (jj < jw && j0 + jj < rank) ? buf_ld16_stream(ra, (uint32_t)k, (uint32_t)(j0 + jj) * a_row_bytes)
+                                             : zero4();
 #pragma unroll
-      for (int r = 0; r < RG; ++r) acc[jj * RG + r] = dot8_bf16(av[jj], xv[r], acc[jj * RG + r]);
+      for (int jj = 0; jj < JW; ++jj) {
+        const u32x4 lo = i8x8_to_bf16x8(u32x2{aq[jj].x, aq[jj].y});
+        const u32x4 hi = i8x8_to_bf16x8(u32x2{aq[jj].z, aq[jj].w});
+#pragma unroll
+        for (int r = 0; r < RG; ++r) acc[jj * RG + r] = dot8_bf16(hi, xw[r], dot8_bf16(lo, xv[r], acc[jj * RG + r]));
+      }
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < JW; ++jj)
+        av[jj] = (jj < jw && j0 + jj < rank) ? buf_ld16_stream(ra, voff, (uint32_t)(j0 + jj) * row_bytes) : zero4();
+#pragma unroll
+      for (int jj = 0; jj < JW; ++jj)
+#pragma unroll
+        for (int r = 0; r < RG; ++r) acc[jj * RG + r] = dot8_bf16(av[jj], xv[r], acc[jj * RG + r]);
+    }
   }
   reduce_scatter<JW * RG, 64>(acc);
   float *out = d.part + ((int64_t)(m.part_base + chunk) * d.num_rows + pos0) * d.rs;
+  const float *a_scale = static_cast<const float *>(A);
   constexpr int NV = JW * RG;
   if constexpr (NV >= 64) {
 #pragma unroll
     for (int i = 0; i < NV / 64; ++i) {
       const int idx = i + (NV / 64) * lane;
       const int jj = idx / RG, r = idx % RG;
-      if (r < nrows && jj < jw && j0 + jj < rank) out[(int64_t)r * d.rs + j0 + jj] = acc[i];
+      if (r < nrows && jj < jw && j0 + jj < rank)
+        out[(int64_t)r * d.rs + j0 + jj] = Q8 ? acc[i] * a_scale[j0 + jj] : acc[i];
     }
   } else {
     constexpr int GS = 64 / NV;
     if (lane % GS == 0) {
       const int idx = lane / GS;
       const int jj = idx / RG, r = idx % RG;
-      if (r < nrows && jj < jw && j0 + jj < rank) out[(int64_t)r * d.rs + j0 + jj] = acc[0];
+      if (r < nrows && jj < jw && j0 + jj < rank)
+        out[(int64_t)r * d.rs + j0 + jj] = Q8 ? acc[0] * a_scale[j0 + jj] : acc[0];
     }
   }
 }
@@ -107,39 +137,87 @@ __device__ __forceinline__ void decode_shrink_block(const LayerDesc &d, int blk)
   if (len >= d.long_min) return;  // an SGMV item takes this segment
   lora_adapter_entry_t e;
   if (!load_entry(d, a, m.col, chunk == 0, &e)) return;
-  const uint16_t *A = static_cast<const uint16_t *>(e.A);
   const int rank = e.rank;
   const int jw = (rank + 3) >> 2;
-  if (len == 1) {
-    decode_shrink_rows<JW, 1>(d, m, A, rank, jw, pos0, 1, chunk);
-  } else {
-    for (int r0 = 0; r0 < len; r0 += RGM)
-      decode_shrink_rows<JW, RGM>(d, m, A, rank, jw, pos0 + r0, min(RGM, len - r0), chunk);
-  }
+  auto run = [&](auto q8) {
+    constexpr bool Q8 = decltype(q8)::value;
+    if (len == 1) {
+      decode_shrink_rows<JW, 1, Q8>(d, m, e.A, rank, jw, pos0, 1, chunk);
+    } else {
+      for (int r0 = 0; r0 < len; r0 += RGM)
+        decode_shrink_rows<JW, RGM, Q8>(d, m, e.A, rank, jw, pos0 + r0, min(RGM, len - r0), chunk);
+    }
+  };
+  if (e.format == LORA_FORMAT_INT8_ROWS) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 // ---------------------------------------------------------------- expand --
+
+// Start (floats) of two tile-sized LDS regions past the v stage and its
+// reduction space: the one-row expand keeps its sums in the first and the
+// int8 row scales of its tile in the second; the multi-row expand keeps the
+// int8 row scales in the first.
+constexpr int kOneRowDeltaBase = 64 + 1024;
 
 // Row stride of B: the rank rounded up to a multiple of 8, so every row is
 // 16-byte aligned.  Columns in [rank, ldb) are padding with finite values;
 // they meet zeros of v and add nothing.
 __device__ __forceinline__ int b_stride(int rank) { return (rank + 7) & ~7; }
 
-// Eight elements B[n][jq .. jq+8) of a B tile, zero for lanes past the rank
-// and rows past the tile.
-__device__ __forceinline__ u32x4 load_b8(rsrc_t rb, int n, int ldb, int rank, int jq) {
-  return buf_ld16_stream(rb, jq < rank ? ((uint32_t)n * ldb + jq) * 2 : kOutOfRange, 0);
-}
+// The rows [n_tile0, n_tile0 + tile_len) of an entry's B.  bf16 rows are
+// b_stride(rank) * 2 bytes apart; Q8 (int8 with one fp32 scale per row)
+// rows are ldb8_of(rank) bytes apart (a multiple of 16), after the d_out
+// scales.  A lane reads the VPL values [jq, jq + VPL) of a row: 8 bf16 (16
+// bytes), or 8 or 16 int8 (8 or 16 bytes).
+template <bool Q8, int VPL = 8>
+struct BTile {
+  static_assert(VPL == 8 || (Q8 && VPL == 16), "values per lane");
+  using raw_t = typename std::conditional<Q8 && VPL == 8, u32x2, u32x4>::type;
+  rsrc_t r;
+  uint32_t row_bytes;
+  const float *scale;  // Q8: scale of tile row 0
+  __device__ __forceinline__ BTile(const void *B, int rank, int d_out, int n_tile0, uint32_t tile_len) {
+    const uint8_t *base = static_cast<const uint8_t *>(B);
+    if constexpr (Q8) {
+      row_bytes = (uint32_t)ldb8_of(rank);
+      scale = reinterpret_cast<const float *>(base) + n_tile0;
+      base += q8_values_offset(d_out);
+    } else {
+      row_bytes = (uint32_t)b_stride(rank) * 2;
+      scale = nullptr;
+    }
+    r = make_rsrc(base + (int64_t)n_tile0 * row_bytes, tile_len * row_bytes);  // past the tile: zero
+  }
+  __device__ __forceinline__ uint32_t off(int n, int jq) const {
+    return (uint32_t)n * row_bytes + (uint32_t)jq * (Q8 ? 1 : 2);
+  }
+  __device__ __forceinline__ raw_t load(uint32_t voff, uint32_t soff) const {
+    if constexpr (sizeof(raw_t) == 8) return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kNonTemporal);
+    else return buf_ld16_stream(r, voff, soff);
+  }
+  // bf16 values for a tile that several rows use: widened once.
+  static __device__ __forceinline__ u32x4 widen(const raw_t &v) {
+    static_assert(VPL == 8, "widen takes 8 values");
+    if constexpr (Q8) return i8x8_to_bf16x8(v);
+    else return v;
+  }
+  // One use of a load: bf16 against the split v; int8 converted to fp32.
+  static __device__ __forceinline__ float dot(const raw_t &b, const float *vv, const V8Split &vs, float c) {
+    if constexpr (Q8 && VPL == 16) return dot8_i8_f32(u32x2{b.z, b.w}, vv + 8, dot8_i8_f32(u32x2{b.x, b.y}, vv, c));
+    else if constexpr (Q8) return dot8_i8_f32(b, vv, c);
+    else return dot8_bf16_split(b, vs, c);
+  }
+};
 
 // One n-tile of one projection for every row of a multi-row segment (fewer
 // than kLongSegRows rows: longer ones go to the SGMV items).  v of every row
 // is staged once; the B sub-tile is loaded once into registers and used by
 // all rows, and the next sub-tile is requested when the rows are done; y of
 // a few rows is requested together.
-template <int LPR>
-__device__ __forceinline__ void decode_expand_rows(const LayerDesc &d, const ModuleDesc &m,
-                                                   const uint16_t *__restrict__ B, int rank, float scale, int pos0,
-                                                   int len, int tile, float *v_lds) {
+template <int LPR, bool Q8>
+__device__ __forceinline__ void decode_expand_rows(const LayerDesc &d, const ModuleDesc &m, const void *B, int rank,
+                                                   float scale, int pos0, int len, int tile, float *v_lds) {
   static_assert(kLongSegRows <= kExpandRowGroup, "a decode segment is staged in one group");
   constexpr int G = kDecodeThreads / LPR;  // output rows per load pass of the block
   constexpr int P = 16;                    // load passes per sub-tile
@@ -151,8 +229,8 @@ __device__ __forceinline__ void decode_expand_rows(const LayerDesc &d, const Mod
   const int n_tile0 = tile * d.nt;
   const int n_tile1 = min(n_tile0 + d.nt, m.d_out);
   const uint32_t tile_len = (uint32_t)(n_tile1 - n_tile0);
-  const int ldb = b_stride(rank);
-  const rsrc_t rb = make_rsrc(B + (int64_t)n_tile0 * ldb, tile_len * ldb * 2);  // past the tile: zero
+  const BTile<Q8> bt(B, rank, m.d_out, n_tile0, tile_len);
+  auto load_b = [&](int n) { return bt.load(jq < rank ? bt.off(n, jq) : kOutOfRange, 0); };
   auto y_rsrc = [&](int i) {
     const int b = i < nr ? uniform(d.perm[pos0 + i]) : -1;
     const bool ok = (unsigned)b < (unsigned)d.num_rows;  // a stray index touches nothing
@@ -160,11 +238,24 @@ __device__ __forceinline__ void decode_expand_rows(const LayerDesc &d, const Mod
   };
   VStage<kExpandRowGroup> vst;
   vst.issue(d, m, pos0, nr, rank);  // before the B stream: waiting for v does not wait for B
-  u32x4 bv[P];
+  typename BTile<Q8>::raw_t bv[P];
 #pragma unroll
-  for (int p = 0; p < P; ++p) bv[p] = load_b8(rb, p * G + g, ldb, rank, jq);
+  for (int p = 0; p < P; ++p) bv[p] = load_b(p * G + g);
+  float *b_scale = v_lds + kOneRowDeltaBase;  // Q8: [NT] row scales of the tile, published by finish()
+  if constexpr (Q8) {
+    constexpr int NT = decode_expand_tile(LPR);  // the host tiles with the same constant
+    const rsrc_t rs = make_rsrc(bt.scale, tile_len * 4);
+#pragma unroll
+    for (int i = 0; i < NT / (kDecodeThreads * 4); ++i) {
+      const int n = (i * kDecodeThreads + t) * 4;
+      *(f32x4_t *)(b_scale + n) = __builtin_bit_cast(f32x4_t, buf_ld16(rs, (uint32_t)n * 4, 0));
+    }
+  }
   vst.finish(d, m, scale, v_lds);
   for (int n0 = 0; n0 < (int)tile_len; n0 += SUB) {
+    u32x4 wb[P];  // the sub-tile as bf16, shared by the rows
+#pragma unroll
+    for (int p = 0; p < P; ++p) wb[p] = BTile<Q8>::widen(bv[p]);
     for (int i0 = 0; i0 < nr; i0 += YR) {
       rsrc_t ry[YR];
       uint16_t yv[YR][PL];
@@ -184,18 +275,21 @@ __device__ __forceinline__ void decode_expand_rows(const LayerDesc &d, const Mod
         const V8Split vs = split_v8(vv);
         float acc[P];
 #pragma unroll
-        for (int p = 0; p < P; ++p) acc[p] = dot8_bf16_split(bv[p], vs, 0.f);
+        for (int p = 0; p < P; ++p) acc[p] = dot8_bf16_split(wb[p], vs, 0.f);
         reduce_scatter<P, LPR>(acc);
+        int sn0 = n0;
+        if constexpr (Q8) asm volatile("" : "+v"(sn0));  // scales read per row, not held across the rows
 #pragma unroll
         for (int ii = 0; ii < PL; ++ii) {
           const uint32_t off = (uint32_t)(n0 + (ii + PL * q) * G + g) * 2;
-          buf_st_u16(ry[u], off, f32_to_bf16(bf16_to_f32(yv[u][ii]) + acc[ii]));
+          const float dlt = Q8 ? acc[ii] * b_scale[sn0 + (ii + PL * q) * G + g] : acc[ii];
+          buf_st_u16(ry[u], off, f32_to_bf16(bf16_to_f32(yv[u][ii]) + dlt));
         }
         __builtin_amdgcn_sched_barrier(0);  // one row's sums live at a time
       }
     }
 #pragma unroll
-    for (int p = 0; p < P; ++p) bv[p] = load_b8(rb, n0 + SUB + p * G + g, ldb, rank, jq);  // past the tile: zero
+    for (int p = 0; p < P; ++p) bv[p] = load_b(n0 + SUB + p * G + g);  // past the tile: zero
   }
 }
 
@@ -210,32 +304,35 @@ __device__ __forceinline__ void decode_expand_rows(const LayerDesc &d, const Mod
 // the sums of each sub-tile go to LDS, and y is written once, after the
 // last load of B.  (A store in the middle of the stream would hold up the
 // loads issued after it: one counter retires loads and stores in order.)
-constexpr int kOneRowDeltaBase = 64 + 1024;  // after the v stage and its reduction space (floats)
+// Q8: a lane takes 16 int8 values (16 bytes) of a row, so half as many
+// lanes share a row and a load moves as many bytes as in bf16.
 
-template <int LPR>
-__device__ __forceinline__ void decode_expand_one_row(const LayerDesc &d, const ModuleDesc &m,
-                                                      const uint16_t *__restrict__ B, int rank, float scale, int pos0,
-                                                      int tile, int item, float *v_lds) {
-  constexpr int G = kDecodeThreads / LPR;
+template <int LPR, bool Q8>
+__device__ __forceinline__ void decode_expand_one_row(const LayerDesc &d, const ModuleDesc &m, const void *B,
+                                                      int rank, float scale, int pos0, int tile, int item,
+                                                      float *v_lds) {
+  constexpr int VPL = Q8 ? 16 : 8;                  // values per lane and load
+  constexpr int L = Q8 && LPR > 1 ? LPR / 2 : LPR;  // lanes per output row
+  constexpr int G = kDecodeThreads / L;
   constexpr int P = 16;
   constexpr int SUB = P * G;
-  constexpr int PL = P / LPR;
+  constexpr int PL = P / L;
   constexpr int NT = decode_expand_tile(LPR);
   static_assert(NT % SUB == 0 && NT % (kDecodeThreads * 8) == 0, "tile");
   constexpr int YT = NT / (kDecodeThreads * 8);  // 16-byte y pieces per thread
-  const int t = threadIdx.x, g = t / LPR, q = t % LPR, jq = q * 8;
+  using BT = BTile<Q8, VPL>;
+  const int t = threadIdx.x, g = t / L, q = t % L, jq = q * VPL;
   const int n_tile0 = tile * d.nt;
   const int n_tile1 = min(n_tile0 + d.nt, m.d_out);
   const int tile_len = n_tile1 - n_tile0;  // <= NT: the host tiles with the same constant
   const int nsub = (tile_len + SUB - 1) / SUB;
-  const int ldb = b_stride(rank);
-  const rsrc_t rb = make_rsrc(B + (int64_t)n_tile0 * ldb, (uint32_t)tile_len * ldb * 2);
-  const uint32_t lane_off = (uint32_t)(g * ldb + jq) * 2;
-  const uint32_t pass_bytes = (uint32_t)G * ldb * 2;
+  const BT bt(B, rank, m.d_out, n_tile0, (uint32_t)tile_len);
+  const uint32_t lane_off = bt.off(g, jq);
+  const uint32_t pass_bytes = (uint32_t)G * bt.row_bytes;
   const bool lane_on = jq < rank;
   auto b_load = [&](int n0, int p) {  // past the tile (also past the last sub-tile) reads zero
     const bool on = lane_on && n0 + p * G + g < tile_len;
-    return buf_ld16_stream(rb, on ? lane_off + p * pass_bytes : kOutOfRange, (uint32_t)n0 * ldb * 2);
+    return bt.load(on ? lane_off + p * pass_bytes : kOutOfRange, (uint32_t)n0 * bt.row_bytes);
   };
   const int b = uniform(d.perm[pos0]);
   const bool row_ok = (unsigned)b < (unsigned)d.num_rows;
@@ -251,13 +348,23 @@ __device__ __forceinline__ void decode_expand_one_row(const LayerDesc &d, const 
   u32x4 yv[YT];
 #pragma unroll
   for (int i = 0; i < YT; ++i) yv[i] = buf_ld16(ry, y_off(i), 0);
-  u32x4 bv[P];
+  float *b_scale = v_lds + kOneRowDeltaBase + NT;  // Q8: [NT] row scales of the tile
+  if constexpr (Q8) {  // requested before B, published by the barrier that ends finish()
+    const rsrc_t rs = make_rsrc(bt.scale, (uint32_t)tile_len * 4);
+    f32x4_t sl[NT / (kDecodeThreads * 4)];
+#pragma unroll
+    for (int i = 0; i < NT / (kDecodeThreads * 4); ++i)
+      sl[i] = __builtin_bit_cast(f32x4_t, buf_ld16(rs, (uint32_t)(i * kDecodeThreads + t) * 16, 0));
+#pragma unroll
+    for (int i = 0; i < NT / (kDecodeThreads * 4); ++i) *(f32x4_t *)(b_scale + (i * kDecodeThreads + t) * 4) = sl[i];
+  }
+  typename BT::raw_t bv[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) bv[p] = b_load(sub_base(0), p);
   vst.finish(d, m, scale, v_lds);
-  float vv[8];
+  float vv[VPL];  // v past the rank is zero (up to 64)
 #pragma unroll
-  for (int k = 0; k < 8; ++k) vv[k] = v_lds[jq + k];
+  for (int k = 0; k < VPL; ++k) vv[k] = v_lds[jq + k];
   const V8Split vs = split_v8(vv);
   float *delta = v_lds + kOneRowDeltaBase;  // [NT] sums of the tile
   for (int st = 0; st < nsub; ++st) {
@@ -265,22 +372,28 @@ __device__ __forceinline__ void decode_expand_one_row(const LayerDesc &d, const 
     float acc[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      acc[p] = dot8_bf16_split(bv[p], vs, 0.f);
+      acc[p] = BT::dot(bv[p], vv, vs, 0.f);
       bv[p] = b_load(n1, p);  // unconditional: a branch here would copy the tile registers
     }
-    reduce_scatter<P, LPR>(acc);
+    reduce_scatter<P, L>(acc);
 #pragma unroll
     for (int ii = 0; ii < PL; ++ii) delta[n0 + (ii + PL * q) * G + g] = acc[ii];
   }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < YT; ++i) {
-    const float *src = delta + y_col(i);
+    float dl[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dl[e] = delta[y_col(i) + e];
+    if constexpr (Q8) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dl[e] *= b_scale[y_col(i) + e];
+    }
     u32x4 o;
-    o.x = pack_bf16x2(bf16_to_f32(yv[i].x) + src[0], bf16_to_f32(yv[i].x >> 16) + src[1]);
-    o.y = pack_bf16x2(bf16_to_f32(yv[i].y) + src[2], bf16_to_f32(yv[i].y >> 16) + src[3]);
-    o.z = pack_bf16x2(bf16_to_f32(yv[i].z) + src[4], bf16_to_f32(yv[i].z >> 16) + src[5]);
-    o.w = pack_bf16x2(bf16_to_f32(yv[i].w) + src[6], bf16_to_f32(yv[i].w >> 16) + src[7]);
+    o.x = pack_bf16x2(bf16_to_f32(yv[i].x) + dl[0], bf16_to_f32(yv[i].x >> 16) + dl[1]);
+    o.y = pack_bf16x2(bf16_to_f32(yv[i].y) + dl[2], bf16_to_f32(yv[i].y >> 16) + dl[3]);
+    o.z = pack_bf16x2(bf16_to_f32(yv[i].z) + dl[4], bf16_to_f32(yv[i].z >> 16) + dl[5]);
+    o.w = pack_bf16x2(bf16_to_f32(yv[i].w) + dl[6], bf16_to_f32(yv[i].w >> 16) + dl[7]);
     buf_st16<kScopeDevice>(ry, y_off(i), o);
   }
 }
@@ -299,10 +412,13 @@ __device__ __forceinline__ void decode_expand_block(const LayerDesc &d, int blk,
   if (len >= d.long_min) return;  // an SGMV item takes this segment
   lora_adapter_entry_t e;
   if (!load_entry(d, a, m.col, tile == 0, &e)) return;
-  const uint16_t *B = static_cast<const uint16_t *>(e.B);
-  const int rank = e.rank;
-  if (len == 1) decode_expand_one_row<LPR>(d, m, B, rank, e.scale, pos0, tile, blk, v_lds);
-  else decode_expand_rows<LPR>(d, m, B, rank, e.scale, pos0, len, tile, v_lds);
+  auto run = [&](auto q8) {
+    constexpr bool Q8 = decltype(q8)::value;
+    if (len == 1) decode_expand_one_row<LPR, Q8>(d, m, e.B, e.rank, e.scale, pos0, tile, blk, v_lds);
+    else decode_expand_rows<LPR, Q8>(d, m, e.B, e.rank, e.scale, pos0, len, tile, v_lds);
+  };
+  if (e.format == LORA_FORMAT_INT8_ROWS) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 }  // namespace lora

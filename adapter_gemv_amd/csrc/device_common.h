@@ -121,6 +121,34 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
 }
 
+// ---- int8 factors (LORA_FORMAT_INT8_ROWS): a block of fp32 row scales,
+// then the int8 rows.  Integers of magnitude <= 128 are exact in bf16, so
+// converting the values to bf16 keeps every product exact.
+__device__ __forceinline__ int round_up4(int a) { return (a + 3) & ~3; }
+__device__ __forceinline__ int ldb8_of(int rank) { return (rank + 15) & ~15; }
+// Row stride (bytes) of an int8 A: d_in rounded up to a multiple of 16.
+__device__ __forceinline__ uint32_t lda8_of(int d_in) { return (uint32_t)(d_in + 15) & ~15u; }
+// Byte offset of the int8 values after the scales of `rows` rows.
+__device__ __forceinline__ uint32_t q8_values_offset(int rows) { return (uint32_t)round_up4(rows) * 4; }
+// Eight int8 values (one 8-byte load) as eight bf16 values (16 bytes).
+__device__ __forceinline__ u32x4 i8x8_to_bf16x8(u32x2 q) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t wv = i < 2 ? q.x : q.y;
+    const int sh = (i & 1) * 16;
+    o[i] = pack_bf16x2((float)(int8_t)(wv >> sh), (float)(int8_t)(wv >> (sh + 8)));
+  }
+  return u32x4{o[0], o[1], o[2], o[3]};
+}
+// Eight int8 values (one 8-byte load) times eight floats, in fp32: each byte
+// is sign-extended and converted exactly, then multiplied and added.
+__device__ __forceinline__ float dot8_i8_f32(u32x2 q, const float *v, float c) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) c = fmaf((float)(int8_t)((k < 4 ? q.x : q.y) >> (8 * (k & 3))), v[k], c);
+  return c;
+}
+
 // Reduce-scatter of NV per-lane values over aligned groups of NL lanes.
 // Afterwards, if NV >= NL, lane q = lane % NL holds in v[i] (i < NV/NL) the
 // group sum of value index i + (NV/NL)*q; if NV < NL, v[0] holds the sum of
@@ -204,7 +232,8 @@ __device__ __forceinline__ bool load_segment(const LayerDesc &d, int s, bool cou
 
 // Whether a table entry describes a delta this launch can apply.
 __device__ __forceinline__ bool entry_ok(const lora_adapter_entry_t &e, int max_rank) {
-  return e.rank > 0 && e.rank <= max_rank && e.format == LORA_FORMAT_BF16 && e.A != nullptr &&
+  return e.rank > 0 && e.rank <= max_rank && (e.format == LORA_FORMAT_BF16 || e.format == LORA_FORMAT_INT8_ROWS) &&
+         e.A != nullptr &&
          ((uintptr_t)e.A & 15) == 0 && e.B != nullptr && ((uintptr_t)e.B & 15) == 0;
 }
 

@@ -9,12 +9,13 @@
 namespace lora {
 namespace {
 
-// LDS of the expand kernel: the SGMV V tile, or the decode v stage plus two
-// buffers of one sub-tile's sums, whichever is larger (floats).
+// LDS of the expand kernel: the SGMV V tile and the int8 row scales of its
+// n-tile, or the decode v stage plus one tile of sums and one of int8 row
+// scales, whichever is larger (floats).
 template <int LPR>
 constexpr int expand_lds_floats() {
-  constexpr int sgmv = kSgmvExpandRows * 64;
-  constexpr int decode = kOneRowDeltaBase + decode_expand_tile(LPR);
+  constexpr int sgmv = kSgmvExpandRows * 64 + kSgmvExpandCols;
+  constexpr int decode = kOneRowDeltaBase + 2 * decode_expand_tile(LPR);
   return sgmv > decode ? sgmv : decode;
 }
 
@@ -32,8 +33,13 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(LayerDesc d, int decod
   else sgmv_shrink_block<NT>(d, blockIdx.x - decode_blocks, lds);
 }
 
+// Waves per SIMD the expand is compiled for: every path of the kernel (bf16
+// and int8, decode and SGMV) fits 4 for the rank classes up to 16 and 3 for
+// ranks 32 and 64 without spilling; left to itself the compiler can give a
+// class one wave less.
 template <int CLS>
-__global__ __launch_bounds__(256) void lora_expand_kernel(LayerDesc d, int decode_blocks) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CLS <= 1 ? 4 : 3))) void lora_expand_kernel(
+    LayerDesc d, int decode_blocks) {
   constexpr int LPR = 1 << CLS;                          // lanes per output row (decode)
   __shared__ float lds[expand_lds_floats<LPR>()];
   constexpr int KT = CLS <= 2 ? 1 : 2;                   // 32-wide rank steps (SGMV)

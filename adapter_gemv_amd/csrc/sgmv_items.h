@@ -97,22 +97,16 @@ __device__ __forceinline__ uint32_t shrink_lds_off(int row, int piece) {
 // threads per 128-byte row segment (whole lines), two rounds ahead in
 // registers; each wave then reads its matrix operands (32 rows x the whole
 // rank) from LDS, so A is read once per block rather than once per wave.
-template <int NT>
-__device__ __forceinline__ void sgmv_shrink_block(const LayerDesc &d, int blk, uint8_t *lds) {
+// Q8: a piece of A is 8 int8 values (8 bytes), widened to bf16 (exactly) on
+// the way into LDS; the partial of rank row j is multiplied by its scale.
+template <int NT, bool Q8>
+__device__ __forceinline__ void sgmv_shrink_tile(const LayerDesc &d, const ModuleDesc &m,
+                                                 const lora_adapter_entry_t &e, int chunk, int seg0, int len, int rt,
+                                                 uint8_t *lds) {
   constexpr int XL = kSgmvShrinkRows * 8 / 256;  // x pieces per thread per round (4)
   constexpr int AROWS = NT * 16;
   constexpr int AL = AROWS * 8 >= 256 ? AROWS * 8 / 256 : 1;  // A pieces per thread per round
   const int t = threadIdx.x, lane = t & 63, w = wave_id();
-  const int tile = blk / d.items_per_seg;
-  const int it = blk - tile * d.items_per_seg;
-  int s, rt;
-  if (!find_long_tile(d, tile, kSgmvShrinkRows, &s, &rt)) return;
-  const ModuleDesc m = module_of_item(d, it);
-  const int chunk = it - m.item_base;
-  int a, seg0, len;
-  if (!load_segment(d, s, it == 0 && rt == 0, &a, &seg0, &len)) return;
-  lora_adapter_entry_t e;
-  if (!load_entry(d, a, m.col, chunk == 0 && rt == 0, &e)) return;
   const int rank = e.rank;
   const int k_begin = chunk * d.kc;
   const int k_end = min(k_begin + d.kc, m.d_in);
@@ -126,15 +120,20 @@ __device__ __forceinline__ void sgmv_shrink_block(const LayerDesc &d, int blk, u
     const int b = r < len ? d.perm[seg0 + r] : -1;
     xoff[i] = (unsigned)b < (unsigned)d.num_rows ? (uint32_t)((int64_t)b * m.ldx * 2) : kOutOfRange;
   }
-  const rsrc_t ra = make_rsrc(e.A, (uint32_t)rank * m.d_in * 2);
+  constexpr uint32_t AE = Q8 ? 1 : 2;                                           // bytes per A value
+  const uint32_t a_row = Q8 ? lda8_of(m.d_in) : (uint32_t)m.d_in * 2;          // bytes per A row
+  const uint8_t *a_vals = static_cast<const uint8_t *>(e.A) + (Q8 ? q8_values_offset(rank) : 0);
+  const rsrc_t ra = make_rsrc(a_vals, (uint32_t)rank * a_row);
   uint32_t aoff[AL];
 #pragma unroll
   for (int i = 0; i < AL; ++i) {
     const int j = i * 32 + (t >> 3);
-    aoff[i] = j < rank && j < AROWS ? (uint32_t)j * m.d_in * 2 : kOutOfRange;
+    aoff[i] = j < rank && j < AROWS ? (uint32_t)j * a_row : kOutOfRange;
   }
+  using araw_t = typename std::conditional<Q8, u32x2, u32x4>::type;
   struct Stage {
-    u32x4 x[XL], a[AL];
+    u32x4 x[XL];
+    araw_t a[AL];
   };
   auto load = [&](Stage &st, int k0) {  // one round; past the chunk: zero, no traffic
     const int k = k0 + piece * 8;
@@ -143,14 +142,23 @@ __device__ __forceinline__ void sgmv_shrink_block(const LayerDesc &d, int blk, u
 #pragma unroll
     for (int i = 0; i < XL; ++i) st.x[i] = buf_ld16(rx, kon && xoff[i] != kOutOfRange ? xoff[i] + kb : kOutOfRange, 0);
 #pragma unroll
-    for (int i = 0; i < AL; ++i) st.a[i] = buf_ld16(ra, kon && aoff[i] != kOutOfRange ? aoff[i] + kb : kOutOfRange, 0);
+    for (int i = 0; i < AL; ++i) {
+      const uint32_t off = kon && aoff[i] != kOutOfRange ? aoff[i] + (uint32_t)k * AE : kOutOfRange;
+      if constexpr (Q8) st.a[i] = buf_ld8(ra, off);
+      else st.a[i] = buf_ld16(ra, off, 0);
+    }
   };
   auto store = [&](const Stage &st, uint8_t *buf) {
 #pragma unroll
     for (int i = 0; i < XL; ++i) *(u32x4 *)(buf + shrink_lds_off(i * 32 + (t >> 3), piece)) = st.x[i];
 #pragma unroll
     for (int i = 0; i < AL; ++i)
-      if (i * 32 + (t >> 3) < AROWS) *(u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(i * 32 + (t >> 3), piece)) = st.a[i];
+      if (i * 32 + (t >> 3) < AROWS) {
+        u32x4 v;
+        if constexpr (Q8) v = i8x8_to_bf16x8(st.a[i]);
+        else v = st.a[i];
+        *(u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(i * 32 + (t >> 3), piece)) = v;
+      }
   };
   f32x4_t acc[2][NT];
 #pragma unroll
@@ -196,6 +204,12 @@ __device__ __forceinline__ void sgmv_shrink_block(const LayerDesc &d, int blk, u
   }
   // C[4*(l/16) + i][l%16] of tile (mt, nt): row 32w + 16mt + 4*(l/16) + i, column 16nt + l%16.
   float *out = d.part + ((int64_t)(m.part_base + chunk) * d.num_rows + seg0) * d.rs;
+  float sa[NT];  // Q8: scales of this lane's rank columns
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int j = nt * 16 + r_in;
+    sa[nt] = Q8 && j < rank ? static_cast<const float *>(e.A)[j] : 1.f;
+  }
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -205,10 +219,27 @@ __device__ __forceinline__ void sgmv_shrink_block(const LayerDesc &d, int blk, u
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const int j = nt * 16 + r_in;
-          if (j < rank) out[(int64_t)r * d.rs + j] = acc[mt][nt][i];
+          if (j < rank) out[(int64_t)r * d.rs + j] = Q8 ? acc[mt][nt][i] * sa[nt] : acc[mt][nt][i];
         }
       }
     }
+}
+
+// Block `blk` of the SGMV shrink numbering (row tiles x decode items).
+template <int NT>
+__device__ __forceinline__ void sgmv_shrink_block(const LayerDesc &d, int blk, uint8_t *lds) {
+  const int tile = blk / d.items_per_seg;
+  const int it = blk - tile * d.items_per_seg;
+  int s, rt;
+  if (!find_long_tile(d, tile, kSgmvShrinkRows, &s, &rt)) return;
+  const ModuleDesc m = module_of_item(d, it);
+  const int chunk = it - m.item_base;
+  int a, seg0, len;
+  if (!load_segment(d, s, it == 0 && rt == 0, &a, &seg0, &len)) return;
+  lora_adapter_entry_t e;
+  if (!load_entry(d, a, m.col, chunk == 0 && rt == 0, &e)) return;
+  if (e.format == LORA_FORMAT_INT8_ROWS) sgmv_shrink_tile<NT, true>(d, m, e, chunk, seg0, len, rt, lds);
+  else sgmv_shrink_tile<NT, false>(d, m, e, chunk, seg0, len, rt, lds);
 }
 
 // ---------------------------------------------------------------- expand --
@@ -216,9 +247,11 @@ __device__ __forceinline__ void sgmv_shrink_block(const LayerDesc &d, int blk, u
 // KT = 32-wide steps over the rank (1: rank <= 32, 2: rank <= 64).  B rows
 // are a multiple of 8 elements apart, so a lane's 8 values of a B row are one
 // 16-byte load; past the rank they are zero (masked) or padding that meets
-// zeros of V.
-template <int KT>
-__device__ __forceinline__ void sgmv_expand_tile(const LayerDesc &d, const ModuleDesc &m, const uint16_t *B, int rank,
+// zeros of V.  Q8: the 8 values are 8 int8 bytes (rows ldb8 bytes apart),
+// widened to bf16 exactly; the row scales of the n-tile wait in LDS after V
+// and multiply the sums in the y update.
+template <int KT, bool Q8>
+__device__ __forceinline__ void sgmv_expand_tile(const LayerDesc &d, const ModuleDesc &m, const void *B, int rank,
                                                  float scale, int seg0, int len, int rt, int tile, float *v_lds) {
   constexpr int DE = 1;  // 32-column steps per register set (two sets in flight)
   constexpr int NQ = kSgmvExpandRows / 16;  // 16-row tiles per block, all handled by every wave
@@ -238,8 +271,11 @@ __device__ __forceinline__ void sgmv_expand_tile(const LayerDesc &d, const Modul
     const int b = r < len ? d.perm[seg0 + r] : -1;
     yrow[q] = (unsigned)b < (unsigned)d.num_rows ? (uint32_t)(((int64_t)b * m.ldy + n_tile0) * 2) : kOutOfRange;
   }
-  const int ldb = (rank + 7) & ~7;
-  const rsrc_t rb = make_rsrc(B + (int64_t)n_tile0 * ldb, (uint32_t)tile_len * ldb * 2);
+  const uint32_t brow = Q8 ? (uint32_t)ldb8_of(rank) : (uint32_t)((rank + 7) & ~7) * 2;  // bytes per B row
+  constexpr uint32_t BE = Q8 ? 1 : 2;                                                       // bytes per B value
+  const uint8_t *b_vals = static_cast<const uint8_t *>(B) + (Q8 ? q8_values_offset(m.d_out) : 0);
+  const rsrc_t rb = make_rsrc(b_vals + (int64_t)n_tile0 * brow, (uint32_t)tile_len * brow);
+  float *b_scale = v_lds + kSgmvExpandRows * 64;  // Q8: [kSgmvExpandCols] row scales of the tile
   // Wave w takes the 32-column steps w, w+4, w+8, ... of the tile.  Matrix
   // row i of half h stands for column n0 + 8*(i/4) + 4h + i%4, so the results
   // of the two halves give lane l the 8 consecutive columns n0 + 8*(l/16) ..
@@ -252,10 +288,13 @@ __device__ __forceinline__ void sgmv_expand_tile(const LayerDesc &d, const Modul
   auto load_b = [&](int n0, int h, int kt) {  // B[col][32kt + 8g .. +8]; zero past the rank / tile
     const int n = n0 + 8 * (r_in >> 2) + 4 * h + (r_in & 3);
     const int k = kt * 32 + 8 * g;
-    return buf_ld16(rb, k < rank && n < tile_len ? ((uint32_t)n * ldb + k) * 2 : kOutOfRange, 0);
+    const uint32_t off = k < rank && n < tile_len ? (uint32_t)n * brow + (uint32_t)k * BE : kOutOfRange;
+    if constexpr (Q8) return buf_ld8(rb, off);
+    else return buf_ld16(rb, off, 0);
   };
+  using braw_t = typename std::conditional<Q8, u32x2, u32x4>::type;
   struct Set {
-    u32x4 bop[DE][2][KT];
+    braw_t bop[DE][2][KT];
     u32x4 yv[DE][NQ];
   };
   auto issue = [&](Set &st, int step) {  // steps step .. step+DE; past the tile: zero, no traffic
@@ -276,6 +315,11 @@ __device__ __forceinline__ void sgmv_expand_tile(const LayerDesc &d, const Modul
   vst.issue(d, m, seg0 + row0, nrows, rank);
   Set s0, s1;
   issue(s0, 0);
+  if constexpr (Q8) {  // published by the barrier that ends finish()
+    const rsrc_t rs = make_rsrc(static_cast<const float *>(B) + n_tile0, (uint32_t)tile_len * 4);
+    for (int n = t * 4; n < tile_len; n += kDecodeThreads * 4)
+      *(f32x4_t *)(b_scale + n) = __builtin_bit_cast(f32x4_t, buf_ld16(rs, (uint32_t)n * 4, 0));
+  }
   vst.finish(d, m, scale, v_lds);
   // All 64 rows as hi/lo bf16 operands: tile q, lane l holds row 16q + l%16,
   // k = 32kt + 8*(l/16) .. +8.
@@ -296,11 +340,23 @@ __device__ __forceinline__ void sgmv_expand_tile(const LayerDesc &d, const Modul
           acc[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt) {
-            const bf16x8_t bo = __builtin_bit_cast(bf16x8_t, st.bop[u][h][kt]);
+            u32x4 bw;
+            if constexpr (Q8) bw = i8x8_to_bf16x8(st.bop[u][h][kt]);
+            else bw = st.bop[u][h][kt];
+            const bf16x8_t bo = __builtin_bit_cast(bf16x8_t, bw);
             acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bo, __builtin_bit_cast(bf16x8_t, vop[q][kt].hi), acc[h],
                                                              0, 0, 0);
             acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bo, __builtin_bit_cast(bf16x8_t, vop[q][kt].lo), acc[h],
                                                              0, 0, 0);
+          }
+        }
+        if constexpr (Q8) {  // columns n0 + 8*(l/16) + 4h + i
+          const int nc = min(n0 + 8 * g, kSgmvExpandCols - 8);  // past the tile: the store is dropped
+          const f32x4_t s0v = *(const f32x4_t *)(b_scale + nc), s1v = *(const f32x4_t *)(b_scale + nc + 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[0][i] *= s0v[i];
+            acc[1][i] *= s1v[i];
           }
         }
         const u32x4 yv = st.yv[u][q];
@@ -337,8 +393,8 @@ __device__ __forceinline__ void sgmv_expand_block(const LayerDesc &d, int blk, f
   if (!load_segment(d, s, it == 0 && rt == 0, &a, &seg0, &len)) return;
   lora_adapter_entry_t e;
   if (!load_entry(d, a, m.col, tile == 0 && rt == 0, &e)) return;
-  const uint16_t *B = static_cast<const uint16_t *>(e.B);
-  sgmv_expand_tile<KT>(d, m, B, e.rank, e.scale, seg0, len, rt, tile, v_lds);
+  if (e.format == LORA_FORMAT_INT8_ROWS) sgmv_expand_tile<KT, true>(d, m, e.B, e.rank, e.scale, seg0, len, rt, tile, v_lds);
+  else sgmv_expand_tile<KT, false>(d, m, e.B, e.rank, e.scale, seg0, len, rt, tile, v_lds);
 }
 
 }  // namespace lora

@@ -31,6 +31,7 @@ DESCRIPTIONS = {
     "zipf_paged": "Zipf(1.1) decode: 512 paged adapters, ranks {8,16,32,64}, 256 rows, q/k/v/o",
     "prefill_r16": "prefill SGMV: 32 sequences, lengths U[128,2048], rank 16, q/o 8192->8192",
     "prefill_r64": "prefill SGMV: 32 sequences, lengths U[128,2048], rank 64, q/o 8192->8192",
+    "full_layer_r64_int8": "70B full layer decode as full_layer_r64, adapters int8 with one fp32 scale per row",
 }
 
 
@@ -344,7 +345,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "int8xbf16" if (w.fmt != 0).any() else "bf16",  # int8 factors: exact in bf16/fp32 products
         "data": "synthetic (seeded, shapes of the pages' 70B workloads)",
         "config": {"workload": DESCRIPTIONS[args.workload], "name": args.workload, "rows": w.num_rows,
                    "distinct_adapters": int(len(np.unique(w.ids[w.ids >= 0]))),

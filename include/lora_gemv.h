@@ -97,10 +97,13 @@ typedef enum lora_status {
  *     scale[row] * q[row][col] ("m07 ...", "9. Bottlenecks and Evolution",
  *     item 3: quantised adapters halve the bytes; symmetric per-row int8 is
  *     this library's reading).  Each factor is one block, 16-byte aligned:
- *       A block: float scale[round_up(rank, 4)], then int8 A[rank][d_in];
+ *       A block: float scale[round_up(rank, 4)], then int8 A[rank][lda8],
+ *                lda8 = d_in rounded up to a multiple of 16 (bytes [d_in,
+ *                lda8) of a row are padding and contribute nothing);
  *       B block: float scale[round_up(d_out, 4)], then int8 B[d_out][ldb8],
  *                ldb8 = rank rounded up to a multiple of 16 (bytes [rank,
  *                ldb8) of a row are padding and contribute nothing).
+ *     Every int8 row starts 16-byte aligned.
  */
 typedef enum lora_factor_format {
   LORA_FORMAT_BF16 = 0,

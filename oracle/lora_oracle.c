@@ -115,8 +115,10 @@ void oracle_expand_row(const double *v, int32_t rank, const uint16_t *B,
  * the page fixes no scheme).  Reading taken: symmetric int8 with one fp32
  * scale per row, value = scale[row] * q[row][col].  A factor block holds the
  * row scales first (their count rounded up to a multiple of 4, so the int8
- * values start 16-byte aligned), then the int8 rows:
- *   A block: float sA[round_up(rank, 4)];  int8 A[rank][d_in]
+ * values start 16-byte aligned), then the int8 rows, each padded to a
+ * multiple of 16 bytes:
+ *   A block: float sA[round_up(rank, 4)];  int8 A[rank][lda8],
+ *            lda8 = round_up(d_in, 16) (columns past d_in never read)
  *   B block: float sB[round_up(d_out, 4)]; int8 B[d_out][ldb8],
  *            ldb8 = round_up(rank, 16) (columns past the rank never read)
  * Each dequantised value scale * q is exact in double, and so is its product
@@ -132,9 +134,10 @@ void oracle_shrink_row_q8(const uint16_t *x, int32_t d_in, const void *A_block,
 {
     const float *sa = (const float *)A_block;
     const int8_t *qa = (const int8_t *)(sa + round_up(rank, 4));
+    const int64_t lda8 = round_up(d_in, 16);
     for (int32_t j = 0; j < rank; ++j) {
         double s = 0.0;
-        const int8_t *a = qa + (int64_t)j * d_in;
+        const int8_t *a = qa + (int64_t)j * lda8;
         for (int32_t k = 0; k < d_in; ++k)
             s += ((double)sa[j] * (double)a[k]) * bf16_value(x[k]);
         v[j] = s;

@@ -1,4 +1,4 @@
-"""GPU parity on the five seeded workloads at their full sizes.
+"""GPU parity on the seeded workloads at their full sizes.
 
 Rows are compared element by element with the oracle: every row where the
 oracle finishes in seconds (decode workloads), and for prefill the first,
@@ -29,7 +29,8 @@ def sample_rows(w):
     return np.unique(rows).astype(np.int32)
 
 
-@pytest.mark.parametrize("name", ["tiny", "q_proj_r16", "full_layer_r64", "zipf_paged", "prefill_r16", "prefill_r64"])
+@pytest.mark.parametrize("name", ["tiny", "q_proj_r16", "full_layer_r64", "full_layer_r64_int8", "zipf_paged",
+                                  "prefill_r16", "prefill_r64"])
 def test_workload_full_size(name):
     note(f"workload {name}: generate")
     w = gen.make_workload(name)

@@ -8,7 +8,8 @@ A skewed id draw gives short segments (decode path) and long ones
 table are mixed in.  The launch-shape choices the host makes from these
 sizes (k-chunks, n-tiles, which segments go to the matrix cores) are all
 exercised; every case is compared with the oracle on the delta alone, on y,
-and on v through the single-projection calls.
+and on v through the single-projection calls.  The mixed-format cases make
+about half the (slot, projection) entries int8 with row scales.
 """
 import numpy as np
 import pytest
@@ -28,7 +29,7 @@ from tests.test_gpu_decode import check_workload  # noqa: E402
 RANK_CHOICES = np.array([0, 1, 3, 8, 13, 16, 24, 32, 40, 57, 64])
 
 
-def random_case(seed: int, big: bool = False):
+def random_case(seed: int, big: bool = False, int8: bool = False):
     rng = np.random.default_rng(7000 + seed)
     names = list(rng.choice(gen.MODULE_NAMES, size=int(rng.integers(1, 4)), replace=False))
     dmax = 160 if big else 400
@@ -50,8 +51,11 @@ def random_case(seed: int, big: bool = False):
     max_rank = max(1, int(ranks.max()))
     if rng.random() < 0.3:
         max_rank = min(64, max_rank + int(rng.integers(1, 16)))  # a launch class above the largest entry
+    fmt = None
+    if int8:  # about half the entries int8 with row scales
+        fmt = np.where(rng.random((slots, gen.N_MOD)) < 0.5, gen.FMT_INT8_ROWS, gen.FMT_BF16).astype(np.int32)
     w = gen.build_workload(f"sweep{seed}", 7000 + seed, rows, slots, shapes, ids, ranks, x_std=1.0, scales=scales,
-                           max_rank=max_rank)
+                           max_rank=max_rank, fmt=fmt)
     return w
 
 
@@ -70,5 +74,14 @@ def test_random_prefill_sized_case(seed):
     w = random_case(100 + seed, big=True)
     runner = ("split", "layer")[seed % 2]
     note(f"sweep big seed {seed}: {w.num_rows} rows, {w.num_slots} slots, "
+         f"{[(m.name, m.d_in, m.d_out) for m in w.modules]}, max_rank {w.max_rank}, runner {runner}")
+    check_workload(w, oracle.lora_layer(w), runner)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_mixed_format_case(seed):
+    w = random_case(200 + seed, big=seed == 5, int8=True)
+    runner = ("split", "layer", "phases")[seed % 3]
+    note(f"sweep int8 seed {seed}: {w.num_rows} rows, {w.num_slots} slots, "
          f"{[(m.name, m.d_in, m.d_out) for m in w.modules]}, max_rank {w.max_rank}, runner {runner}")
     check_workload(w, oracle.lora_layer(w), runner)

@@ -34,6 +34,8 @@ MUTATIONS = {
                              "s += ((double)sb[j] * (double)b[j]) * v[j];"),
     "q8_B_rows_by_rank": ("const int8_t *b = qb + (int64_t)n * ldb8;",
                           "const int8_t *b = qb + (int64_t)n * rank; (void)ldb8;"),
+    "q8_A_rows_by_d_in": ("const int8_t *a = qa + (int64_t)j * lda8;",
+                          "const int8_t *a = qa + (int64_t)j * d_in; (void)lda8;"),
     "q8_A_values_after_rank_scales": ("(const int8_t *)(sa + round_up(rank, 4))", "(const int8_t *)(sa + rank)"),
     "q8_B_values_after_d_out_scales": ("(const int8_t *)(sb + round_up(d_out, 4))", "(const int8_t *)(sb + d_out)"),
 }

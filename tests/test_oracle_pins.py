@@ -273,18 +273,25 @@ def test_int8_exact_rational():
 
 
 def test_int8_padding_columns_unused():
-    # the bytes of B past the rank in each row are never read
+    # the bytes of A past d_in and of B past the rank in each row are never
+    # read, and the rows sit lda8 / ldb8 bytes apart
     from workloads import gen
     ids = np.array([0, 1, 0, 1])
-    w = bw(5, 4, 2, 32, 16, 5, ids, x_std=1.0, fmt=gen.FMT_INT8_ROWS)
+    d_in, d_out, rank = 40, 16, 5
+    w = bw(5, 4, 2, d_in, d_out, rank, ids, x_std=1.0, fmt=gen.FMT_INT8_ROWS)
     before = oracle.lora_layer(w)["q"]
     raw = w.pool.view(np.uint8)
     for a in range(2):
-        o = 2 * int(w.b_off[a, 0]) + 4 * 16
-        full = raw[o:o + 16 * gen.ldb8(5)].reshape(16, gen.ldb8(5))
-        full[:, 5:] = 0x7F
+        o = 2 * int(w.a_off[a, 0]) + 4 * 8
+        full = raw[o:o + rank * gen.lda8(d_in)].reshape(rank, gen.lda8(d_in))
+        assert gen.lda8(d_in) == 48 and np.array_equal(full[:, :d_in].view(np.int8), w.A_q8(a, 0)[1])
+        full[:, d_in:] = 0x7F
+        o = 2 * int(w.b_off[a, 0]) + 4 * d_out
+        full = raw[o:o + d_out * gen.ldb8(rank)].reshape(d_out, gen.ldb8(rank))
+        full[:, rank:] = 0x7F
     after = oracle.lora_layer(w)["q"]
     assert np.array_equal(before.delta, after.delta)
+    assert np.abs(before.delta).max() > 0
 
 
 def test_int8_quantiser_round_trip():

@@ -152,13 +152,15 @@ class Workload:
         return self.pool[o:o + d_out * ldb(r)].reshape(d_out, ldb(r))[:, :r]
 
     def A_q8(self, slot: int, col: int):
-        """int8 A: (row scales float32 [rank], values int8 [rank, d_in])."""
+        """int8 A: (row scales float32 [rank], values int8 [rank, d_in] view;
+        rows lda8(d_in) bytes apart)."""
         assert self.fmt[slot, col] == FMT_INT8_ROWS
         r = int(self.ranks[slot, col])
         d_in = self._spec_col(col).d_in
         raw = self.pool.view(np.uint8)[2 * int(self.a_off[slot, col]):]
         sa = raw[:4 * r].view(np.float32)
-        q = raw[4 * _align(r, 4):4 * _align(r, 4) + r * d_in].view(np.int8).reshape(r, d_in)
+        o = 4 * _align(r, 4)
+        q = raw[o:o + r * lda8(d_in)].view(np.int8).reshape(r, lda8(d_in))[:, :d_in]
         return sa, q
 
     def B_q8(self, slot: int, col: int):
@@ -200,14 +202,19 @@ def ldb(rank: int) -> int:
 # Factor formats of a table entry.  FMT_INT8_ROWS: symmetric int8 with one
 # fp32 scale per row ("9. Bottlenecks and Evolution" on "m07 -- Multi-Adapter
 # (LoRA) Serving", item 3, fixes no scheme; this is the reading taken).  A
-# block: float scales[round_up(rank, 4)], then int8 A[rank][d_in]; B block:
-# float scales[round_up(d_out, 4)], then int8 B[d_out][ldb8(rank)].
+# block: float scales[round_up(rank, 4)], then int8 A[rank][lda8(d_in)]; B
+# block: float scales[round_up(d_out, 4)], then int8 B[d_out][ldb8(rank)].
 FMT_BF16, FMT_INT8_ROWS = 0, 1
 
 
 def ldb8(rank: int) -> int:
     """Row stride (bytes) of an int8 B: the rank rounded up to a multiple of 16."""
     return (int(rank) + 15) // 16 * 16
+
+
+def lda8(d_in: int) -> int:
+    """Row stride (bytes) of an int8 A: d_in rounded up to a multiple of 16."""
+    return (int(d_in) + 15) // 16 * 16
 
 
 def entry_bytes(rank: int, d_in: int, d_out: int, fmt: int) -> int:
@@ -222,7 +229,7 @@ def entry_bytes(rank: int, d_in: int, d_out: int, fmt: int) -> int:
 def _block_elems(rank: int, d_in: int, d_out: int, fmt: int):
     """(A, B) block sizes in uint16 pool elements."""
     if fmt == FMT_INT8_ROWS:
-        a = 4 * _align(rank, 4) + rank * d_in
+        a = 4 * _align(rank, 4) + rank * lda8(d_in)
         b = 4 * _align(d_out, 4) + d_out * ldb8(rank)
         return (a + 1) // 2, (b + 1) // 2
     return rank * d_in, d_out * ldb(rank)
@@ -257,7 +264,11 @@ def _fill_adapters(seed, pool, modules, ranks, a_off, b_off, ab_std, slots, fmt=
         o = 2 * oa
         raw[o:o + 4 * r] = sa.view(np.uint8)
         o += 4 * _align(r, 4)
-        raw[o:o + r * s.d_in] = qa.reshape(-1).view(np.uint8)
+        la = lda8(s.d_in)
+        fa = raw[o:o + r * la].reshape(r, la)
+        fa[:, :s.d_in] = qa.view(np.uint8)
+        if la > s.d_in:  # padding: random bytes that no computation may use
+            fa[:, s.d_in:] = _rng(seed, _R_PAD, a, s.index, 1).integers(0, 256, size=(r, la - s.d_in), dtype=np.uint8)
         o = 2 * ob
         raw[o:o + 4 * s.d_out] = sb.view(np.uint8)
         o += 4 * _align(s.d_out, 4)
