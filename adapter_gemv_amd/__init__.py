@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.restype = st
             f.argtypes = [ctypes.POINTER(_IO), u32, i32, vp, i32, _Seg, i32, vp, sz, vp]
+        L.lora_form_batch.restype = st
+        L.lora_form_batch.argtypes = [vp, i32, vp, ctypes.c_float, i32, i32, i32, i32, vp, vp]
         _lib = L
     return _lib
 
@@ -235,3 +237,22 @@ def layer_shrink(ios, num_rows, table, num_slots, seg, max_rank, ws, stream=None
 def layer_expand(ios, num_rows, table, num_slots, seg, max_rank, ws, stream=None, module_mask=None):
     _layer(lib().lora_layer_expand, "lora_layer_expand", ios, num_rows, table, num_slots, seg, max_rank, ws, stream,
            module_mask)
+
+
+def form_batch(adapters, max_batch: int, max_distinct: int, min_batch: int = 0, reserved_tail: int = 0,
+               waited_ms=None, max_wait_ms: float = 0.0) -> np.ndarray:
+    """lora_form_batch on host arrays: queue positions of the chosen requests,
+    in batch order.  ``adapters``: int32 adapter slot per waiting request,
+    oldest first (negative = base only); ``waited_ms``: optional float ages."""
+    a = np.ascontiguousarray(adapters, dtype=np.int32)
+    w = None if waited_ms is None else np.ascontiguousarray(waited_ms, dtype=np.float32)
+    if w is not None and w.shape != a.shape:
+        raise LoraError("form_batch: waited_ms must match adapters")
+    out = np.empty(max(1, min(int(max_batch), a.size)), np.int32)
+    count = ctypes.c_int32(0)
+    code = lib().lora_form_batch(a.ctypes.data_as(ctypes.c_void_p), a.size,
+                                 None if w is None else w.ctypes.data_as(ctypes.c_void_p), float(max_wait_ms),
+                                 int(max_batch), int(max_distinct), int(min_batch), int(reserved_tail),
+                                 out.ctypes.data_as(ctypes.c_void_p), ctypes.byref(count))
+    _check(code, "form_batch")
+    return out[:count.value].copy()

@@ -14,7 +14,7 @@ LIB = os.path.join(HERE, "liblora_gemv.so")
 INCLUDE = os.path.join(ROOT, "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "segments.hip", "kernels.hip"]
+SOURCES = ["api.hip", "segments.hip", "kernels.hip", "batch_former.cpp"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

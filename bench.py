@@ -32,7 +32,28 @@ DESCRIPTIONS = {
     "prefill_r16": "prefill SGMV: 32 sequences, lengths U[128,2048], rank 16, q/o 8192->8192",
     "prefill_r64": "prefill SGMV: 32 sequences, lengths U[128,2048], rank 64, q/o 8192->8192",
     "full_layer_r64_int8": "70B full layer decode as full_layer_r64, adapters int8 with one fp32 scale per row",
+    "zipf_formed": "Zipf(1.1) decode over zipf_paged's 512 paged adapters: 256 rows chosen from a 512-request queue "
+                   "by the adapter-aware batch former (cap 32 adapters, 4 tail slots, at least 128 rows)",
 }
+
+
+def formed_workload(gen):
+    """The rows the library's batch former picks from the Zipf queue, and a
+    report of the former: its choice and its host time per call."""
+    import numpy as np
+    import adapter_gemv_amd as lg
+    q = gen.zipf_queue()
+    sel = lg.form_batch(q, **gen.ZIPF_FORMER)
+    calls = 200
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        lg.form_batch(q, **gen.ZIPF_FORMER)
+    us = (time.perf_counter() - t0) / calls * 1e6
+    fifo = q[:gen.ZIPF_FORMER["max_batch"]]
+    report = {"queue": int(q.size), **gen.ZIPF_FORMER, "chosen": int(sel.size),
+              "distinct_adapters": int(np.unique(q[sel]).size), "fifo_distinct_adapters": int(np.unique(fifo).size),
+              "host_us_per_call": round(us, 2)}
+    return gen.zipf_paged(ids=q[sel], name="zipf_formed"), report
 
 
 def algorithmic(w):
@@ -270,7 +291,11 @@ def main():
     from workloads.device import DeviceWorkload
 
     print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
-    w = gen.make_workload(args.workload)
+    former = None
+    if args.workload == "zipf_formed":
+        w, former = formed_workload(gen)
+    else:
+        w = gen.make_workload(args.workload)
     traffic = algorithmic(w)
     adapters_bytes = traffic["adapters"]
     reps = args.replicas or max(1, int(np.ceil(1.0e9 / max(adapters_bytes, 1))))
@@ -363,6 +388,8 @@ def main():
                      "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 2),
                      "traffic_source": counted["source"] if counted else None},
     }
+    if former is not None:
+        out["batch_former"] = former
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w)

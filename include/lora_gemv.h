@@ -33,8 +33,9 @@
  * Conventions for every call:
  *  - bf16 tensors are raw 16-bit bfloat16 values, row-major.
  *  - Every pointer argument marked "device" is device memory owned by the
- *    caller.  The library allocates nothing, keeps no pointer after a call
- *    returns and has no global state; it is reentrant.
+ *    caller.  The library allocates no device memory, keeps no pointer after
+ *    a call returns and has no global state; it is reentrant.  (The host-only
+ *    lora_form_batch uses temporary host memory, freed before it returns.)
  *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
  *    enqueues work on it and returns; nothing synchronises the host.  Buffers
  *    must stay alive until the stream has passed the call.  No call
@@ -287,6 +288,52 @@ lora_status_t lora_layer_expand(const lora_module_io_t *io, uint32_t module_mask
                                 int32_t num_slots, lora_segments_t seg,
                                 int32_t max_rank, void *ws, size_t ws_bytes,
                                 void *stream);
+
+/*
+ * lora_form_batch -- choose the requests of the next step from a waiting
+ * queue so that the batch shares adapters (host code; no device work, no
+ * stream).  Source: "m07 -- Multi-Adapter (LoRA) Serving", "6. Deep Dive A",
+ * "The adapter-aware scheduler" (group the queue by adapter, biggest groups
+ * first and whole where possible, and admit no new adapter once the batch
+ * holds max_distinct adapters and at least min_batch requests) and "The
+ * fairness cost, which must be stated" (an age override); "The Revision", R1
+ * (slots reserved for the long tail); "12. Adapter Serving and Multi-Tenant
+ * Customization", "Batching across adapters" (base-only requests are a group
+ * of their own).  The batch, in order:
+ *   1. urgent: every request with waited_ms[i] > max_wait_ms, oldest first
+ *      (skipped when waited_ms is NULL);
+ *   2. tail: the oldest requests (at most min(reserved_tail, max_distinct))
+ *      whose adapter has no other request among those not yet taken;
+ *      base-only requests never take a tail slot;
+ *   3. grouped fill of the rest: groups by adapter (all base-only requests
+ *      form one group), in descending size, equal sizes in the order of their
+ *      oldest request, members oldest first, a group cut only where the batch
+ *      fills.  Before each group: stop if the batch is full, or if the fill has
+ *      admitted (max_distinct - tail) adapter groups and the whole batch holds
+ *      at least min_batch requests.  The base-only group counts against no
+ *      budget.  Whenever min_batch <= max_distinct, steps 2 and 3 together
+ *      admit at most max_distinct adapters.
+ *
+ *   adapters       host int32 [queue_len]: adapter slot of each waiting
+ *                  request, oldest first; negative = base only
+ *   queue_len      >= 0
+ *   waited_ms      host float [queue_len] or NULL; max_wait_ms its deadline
+ *   max_batch      >= 1: most requests chosen
+ *   max_distinct   >= 0: adapter budget of steps 2 and 3
+ *   min_batch      >= 0
+ *   reserved_tail  >= 0
+ *   out_index      host int32 [min(max_batch, queue_len)] (at least 1):
+ *                  queue positions of the chosen requests, in batch order
+ *   out_count      host int32 *: number chosen
+ *
+ * Errors: LORA_ERR_NULL (a needed pointer is NULL), LORA_ERR_SHAPE (a count
+ * out of range); nothing is written then.
+ */
+lora_status_t lora_form_batch(const int32_t *adapters, int32_t queue_len,
+                              const float *waited_ms, float max_wait_ms,
+                              int32_t max_batch, int32_t max_distinct,
+                              int32_t min_batch, int32_t reserved_tail,
+                              int32_t *out_index, int32_t *out_count);
 
 /* A static, human-readable name for a status code. */
 const char *lora_status_string(lora_status_t status);

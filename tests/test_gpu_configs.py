@@ -29,11 +29,23 @@ def sample_rows(w):
     return np.unique(rows).astype(np.int32)
 
 
+def make(name):
+    if name != "zipf_formed":
+        return gen.make_workload(name)
+    # the rows the batch former picks from the Zipf queue: the oracle's choice,
+    # which the library's former must match exactly
+    import oracle.batch_former as bf
+    q = gen.zipf_queue()
+    sel = bf.form_batch(list(q), **gen.ZIPF_FORMER)
+    assert list(lg.form_batch(q, **gen.ZIPF_FORMER)) == sel
+    return gen.zipf_paged(ids=q[sel], name=name)
+
+
 @pytest.mark.parametrize("name", ["tiny", "q_proj_r16", "full_layer_r64", "full_layer_r64_int8", "zipf_paged",
-                                  "prefill_r16", "prefill_r64"])
+                                  "zipf_formed", "prefill_r16", "prefill_r64"])
 def test_workload_full_size(name):
     note(f"workload {name}: generate")
-    w = gen.make_workload(name)
+    w = make(name)
     rows = sample_rows(w)
     ref = oracle.lora_layer(w, rows=rows)
     note(f"workload {name}: {w.num_rows} rows, {w.num_slots} slots, modules {[m.name for m in w.modules]}")

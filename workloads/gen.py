@@ -418,19 +418,34 @@ def zipf_ids(seed, num_rows, num_slots, s=1.1):
     return to_slot[rank_idx].astype(np.int32)
 
 
-def zipf_paged(seed=4, num_slots=512, rows=256, s=1.1):
+def zipf_paged(seed=4, num_slots=512, rows=256, s=1.1, ids=None, name=None):
     """512 adapters in fixed pages sized for rank 64, ranks drawn from
-    {8,16,32,64}, 256 rows with Zipf(1.1) ids, attention q/k/v/o shapes."""
-    ids = zipf_ids(seed, rows, num_slots, s)
+    {8,16,32,64}, 256 rows with Zipf(1.1) ids, attention q/k/v/o shapes.
+    ``ids`` replaces the drawn row ids (a batch chosen from a queue)."""
+    ids = zipf_ids(seed, rows, num_slots, s) if ids is None else np.asarray(ids, np.int32)
+    rows = int(ids.size)
     rk = _rng(seed, _R_RANK).choice(np.array([8, 16, 32, 64]), size=num_slots)
     ranks = np.zeros((num_slots, N_MOD), np.int32)
     for n in ("q", "k", "v", "o"):
         ranks[:, MODULE_INDEX[n]] = rk
     placement = _rng(seed, _R_PLACE).permutation(num_slots)
     shapes = {n: SHAPES_70B[n] for n in ("q", "k", "v", "o")}
-    return build_workload(f"zipf_paged_{num_slots}x{rows}", seed, rows, num_slots, shapes, ids, ranks,
+    return build_workload(name or f"zipf_paged_{num_slots}x{rows}", seed, rows, num_slots, shapes, ids, ranks,
                           x_of=X_OF_70B, x_std=1.0, ab_std=0.02, y_std=1.0,
                           paged_capacity_rank=64, placement=placement)
+
+
+# The waiting queue the batch former chooses from: requests in arrival order,
+# Zipf(1.1) over the same 512 paged adapters, twice the batch.
+ZIPF_QUEUE = dict(seed=6, num_rows=512, num_slots=512, s=1.1)
+# The former's settings for it ("6. Deep Dive A": cap 32; "The Revision", R1:
+# 4 of the 32 held for the tail): a batch of 256 rows, at least 128.
+ZIPF_FORMER = dict(max_batch=256, max_distinct=32, min_batch=128, reserved_tail=4)
+
+
+def zipf_queue():
+    """Adapter slot of each waiting request, oldest first."""
+    return zipf_ids(**ZIPF_QUEUE)
 
 
 def prefill(seed=5, rank=16, num_seqs=32, lo=128, hi=2048):
