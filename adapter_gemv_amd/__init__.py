@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.restype = st
             f.argtypes = [ctypes.POINTER(_IO), u32, i32, vp, i32, _Seg, i32, vp, sz, vp]
+        L.lora_apply_layer_stacked.restype = st
+        L.lora_apply_layer_stacked.argtypes = [ctypes.POINTER(_IO), u32, i32, vp, i32, vp, i32, _Seg, i32, vp, sz, vp]
         L.lora_form_batch.restype = st
         L.lora_form_batch.argtypes = [vp, i32, vp, ctypes.c_float, i32, i32, i32, i32, vp, vp]
         _lib = L
@@ -237,6 +239,23 @@ def layer_shrink(ios, num_rows, table, num_slots, seg, max_rank, ws, stream=None
 def layer_expand(ios, num_rows, table, num_slots, seg, max_rank, ws, stream=None, module_mask=None):
     _layer(lib().lora_layer_expand, "lora_layer_expand", ios, num_rows, table, num_slots, seg, max_rank, ws, stream,
            module_mask)
+
+
+def apply_layer_stacked(ios, num_rows, row_adapters, table, num_slots, seg, max_rank, ws, stream=None,
+                        module_mask=None):
+    """Several adapters per row (``row_adapters``: device int32 [num_rows, depth],
+    -1 pads); see lora_apply_layer_stacked."""
+    import torch
+    _need(row_adapters, torch.int32, "row_adapters", 2)
+    if row_adapters.shape[0] < num_rows or not row_adapters.is_contiguous():
+        raise ValueError("row_adapters: a contiguous [num_rows, depth] tensor")
+    arr, mask = _ios(ios, num_rows)
+    if module_mask is None:
+        module_mask = mask
+    _check(lib().lora_apply_layer_stacked(arr, module_mask, num_rows, _ptr(row_adapters), row_adapters.shape[1],
+                                          _ptr(table), num_slots, seg.c(), max_rank, _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(stream)),
+           "lora_apply_layer_stacked")
 
 
 def form_batch(adapters, max_batch: int, max_distinct: int, min_batch: int = 0, reserved_tail: int = 0,

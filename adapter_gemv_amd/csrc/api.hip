@@ -84,7 +84,7 @@ void fill_desc(LayerDesc &d, const ModuleArgs *ms, int n, bool shrink, int num_r
   d = LayerDesc{};
   d.kc = pick_kc(num_rows, max_rank, num_rows < num_slots ? num_rows : num_slots, ms, n);
   d.nt = pick_nt(max_rank, num_rows < num_slots ? num_rows : num_slots, ms, n);
-  d.sg_nt = kSgmvExpandCols;
+  d.sg_nt = num_rows >= kPrefillRows ? kSgmvExpandCols : kSgmvExpandColsSmall;
   int item = 0, chunk = 0, sg = 0;
   for (int i = 0; i < n; ++i) {
     ModuleDesc &m = d.mod[i];
@@ -230,7 +230,8 @@ lora_status_t lora_build_segments(const int32_t *row_adapter, int32_t num_rows, 
   if (need > 0 && !ws) return LORA_ERR_NULL;
   if (need > 0 && !aligned16(ws)) return LORA_ERR_ALIGN;
   if (ws_bytes < need) return LORA_ERR_WORKSPACE;
-  return launched(launch_build_segments(row_adapter, num_rows, num_slots, seg, ws, static_cast<hipStream_t>(stream)));
+  return launched(
+      launch_build_segments(row_adapter, 1, num_rows, num_slots, false, seg, ws, static_cast<hipStream_t>(stream)));
 }
 
 lora_status_t lora_shrink(const void *x, int64_t ldx, int32_t num_rows, int32_t d_in,
@@ -297,6 +298,36 @@ lora_status_t lora_apply_layer(const lora_module_io_t *io, uint32_t module_mask,
                                const lora_adapter_entry_t *table, int32_t num_slots, lora_segments_t seg,
                                int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
   return layer_phase(true, true, io, module_mask, num_rows, table, num_slots, seg, max_rank, ws, ws_bytes, stream);
+}
+
+// One pass per position of the rows' adapter lists: the segments of that
+// column, then the layer's shrink and expand, each pass adding its delta to y
+// in stream order (a row is in one segment per pass, so no two blocks of a
+// launch touch the same y).
+lora_status_t lora_apply_layer_stacked(const lora_module_io_t *io, uint32_t module_mask, int32_t num_rows,
+                                       const int32_t *row_adapters, int32_t depth,
+                                       const lora_adapter_entry_t *table, int32_t num_slots, lora_segments_t seg,
+                                       int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
+  ModuleArgs ms[LORA_NUM_MODULES];
+  int n = 0;
+  lora_status_t st = check_layer(io, module_mask, num_rows, table, num_slots, seg, max_rank, ws, ws_bytes, ms, &n);
+  if (st != LORA_OK) return st;
+  if (depth < 1 || depth > LORA_MAX_STACK) return LORA_ERR_SHAPE;
+  if (num_rows > 0 && !row_adapters) return LORA_ERR_NULL;
+  const size_t need = segments_ws_bytes(num_rows, num_slots);
+  if (need > 0 && !ws) return LORA_ERR_NULL;
+  if (need > 0 && !aligned16(ws)) return LORA_ERR_ALIGN;
+  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int t = 0; t < depth; ++t) {
+    st = launched(launch_build_segments(row_adapters + t, depth, num_rows, num_slots, t > 0, seg, ws, s));
+    if (st != LORA_OK || num_rows == 0) return st;  // no rows: the first pass only resets the segments
+    st = launch_phase(true, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
+    if (st != LORA_OK) return st;
+    st = launch_phase(false, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
+    if (st != LORA_OK) return st;
+  }
+  return LORA_OK;
 }
 
 }  // extern "C"

@@ -23,8 +23,12 @@ constexpr int kMaxModules = LORA_NUM_MODULES;
 constexpr int kLongSegRows = 8;
 // Batches of at least this many rows use a larger shrink k-chunk.
 constexpr int kPrefillRows = 2048;
-// Output columns per SGMV expand block.
+// Output columns per SGMV expand block (the most a block stages for): in
+// batches of fewer than kPrefillRows rows, whose long segments give few row
+// tiles, a quarter of that, so the launch has more blocks (measured 13-19%
+// faster on the expand of 256-row Zipf batches; the same at 256 columns).
 constexpr int kSgmvExpandCols = 2048;
+constexpr int kSgmvExpandColsSmall = 512;
 
 // Threads per block of the decode kernels: 4 waves of 64.
 constexpr int kDecodeThreads = 256;
@@ -87,9 +91,10 @@ inline int partial_row_stride(int max_rank) { return round_up(max_rank, 8); }
 size_t segments_ws_bytes(int num_rows, int num_slots);
 size_t partials_ws_bytes(int num_rows, int max_rank, int64_t sum_d_in);
 
-hipError_t launch_build_segments(const int32_t *ids, int n, int num_slots,
-                                 const lora_segments_t &seg, void *ws,
-                                 hipStream_t stream);
+// Row b's id is ids[b * stride]; add_status adds the bad ids to the status
+// word instead of setting it.
+hipError_t launch_build_segments(const int32_t *ids, int stride, int n, int num_slots, bool add_status,
+                                 const lora_segments_t &seg, void *ws, hipStream_t stream);
 hipError_t launch_shrink_reduce(const LayerDesc &d, hipStream_t stream);
 // One launch per phase: blocks [0, decode_blocks) take decode items, the
 // rest SGMV row tiles.

@@ -1,4 +1,7 @@
-// Segment builder: group the rows of a batch by adapter slot.
+// Segment builder: group the rows of a batch by adapter slot.  Row b's id is
+// ids[b * stride] (stride > 1: one column of a row's adapter list); the status
+// word gets the rows with an id >= num_slots, or has them added (a later pass
+// over another column of the same list).
 //
 // "m07 -- Multi-Adapter (LoRA) Serving", "6. Deep Dive A": the batched kernel
 // receives an index vector mapping each sequence to an adapter slot.
@@ -80,8 +83,9 @@ constexpr int kSegLdsSlots = 8192;
 // value count rows and the high 16 bits count non-empty slots (n <= 1024,
 // so neither overflows), so one scan gives row offsets and segment indices.
 template <int THREADS>
-__global__ __launch_bounds__(THREADS) void seg_small_kernel(const int32_t *__restrict__ ids, int n, int num_slots,
-                                                            lora_segments_t seg, int32_t *__restrict__ ws_counts) {
+__global__ __launch_bounds__(THREADS) void seg_small_kernel(const int32_t *__restrict__ ids, int stride, int n,
+                                                            int num_slots, bool add_status, lora_segments_t seg,
+                                                            int32_t *__restrict__ ws_counts) {
   __shared__ __align__(16) int s_ids[THREADS];
   __shared__ int s_counts[kSegLdsSlots];
   __shared__ int s_w[THREADS / 64 + 1];
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(THREADS) void seg_small_kernel(const int32_t *__res
   const int t = threadIdx.x;
   int id = -1, bad = 0;
   if (t < n) {
-    const int r = ids[t];
+    const int r = ids[(int64_t)t * stride];
     if (r >= num_slots) bad = 1;
     else if (r >= 0) id = r;
   }
@@ -120,7 +124,7 @@ __global__ __launch_bounds__(THREADS) void seg_small_kernel(const int32_t *__res
   if (t == 0) {
     seg.seg_offsets[carry >> 16] = carry & 0xffff;
     *seg.num_segments = carry >> 16;
-    *seg.status = nbad;
+    *seg.status = add_status ? *seg.status + nbad : nbad;
   }
   __syncthreads();
   if (id >= 0) seg.perm[counts[id] + before] = t;
@@ -129,8 +133,8 @@ __global__ __launch_bounds__(THREADS) void seg_small_kernel(const int32_t *__res
 // Chunk c of kSegChunk rows: hist[a * nchunks + c] = rows of slot a in the
 // chunk (slot-major), lrank[row] = earlier rows of the same slot in the
 // chunk, badc[c] = rows with an id >= num_slots.
-__global__ __launch_bounds__(kSegChunk) void seg_chunk_kernel(const int32_t *__restrict__ ids, int n, int num_slots,
-                                                              int nchunks, int32_t *__restrict__ hist,
+__global__ __launch_bounds__(kSegChunk) void seg_chunk_kernel(const int32_t *__restrict__ ids, int stride, int n,
+                                                              int num_slots, int nchunks, int32_t *__restrict__ hist,
                                                               int32_t *__restrict__ lrank,
                                                               int32_t *__restrict__ badc) {
   __shared__ __align__(16) int s_ids[kSegChunk];
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(kSegChunk) void seg_chunk_kernel(const int32_t *__r
   const int len = min(kSegChunk, n - c * kSegChunk);
   int id = -1, bad = 0;
   if (t < len) {
-    const int r = ids[row];
+    const int r = ids[(int64_t)row * stride];
     if (r >= num_slots) bad = 1;
     else if (r >= 0) id = r;
   }
@@ -162,7 +166,8 @@ constexpr int kScanPer = 8;  // consecutive elements per thread and pass
 // One block: exclusive scan of hist in slot-major order (the first output
 // position of each (slot, chunk)), then the segments: slot a opens one at
 // hist[a * nchunks] when its rows are non-zero.
-__global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(int num_slots, int nchunks, lora_segments_t seg,
+__global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(int num_slots, int nchunks, bool add_status,
+                                                                lora_segments_t seg,
                                                                 int32_t *__restrict__ hist,
                                                                 const int32_t *__restrict__ badc) {
   __shared__ int s_w[kScanThreads / 64 + 1];
@@ -213,19 +218,19 @@ __global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(int num_slots, i
   if (t == 0) {
     seg.seg_offsets[segs] = carry;
     *seg.num_segments = segs;
-    *seg.status = nbad;
+    *seg.status = add_status ? *seg.status + nbad : nbad;
   }
 }
 
 // Chunk c: every valid row goes to its slot's position for this chunk plus
 // its rank inside the chunk.
-__global__ __launch_bounds__(kSegChunk) void seg_scatter_kernel(const int32_t *__restrict__ ids, int n, int num_slots,
-                                                                int nchunks, lora_segments_t seg,
+__global__ __launch_bounds__(kSegChunk) void seg_scatter_kernel(const int32_t *__restrict__ ids, int stride, int n,
+                                                                int num_slots, int nchunks, lora_segments_t seg,
                                                                 const int32_t *__restrict__ hist,
                                                                 const int32_t *__restrict__ lrank) {
   const int row = blockIdx.x * kSegChunk + threadIdx.x;
   if (row >= n) return;
-  const int id = ids[row];
+  const int id = ids[(int64_t)row * stride];
   if (id >= 0 && id < num_slots) seg.perm[hist[(size_t)id * nchunks + blockIdx.x] + lrank[row]] = row;
 }
 
@@ -239,15 +244,16 @@ size_t segments_ws_bytes(int num_rows, int num_slots) {
   return align256((size_t)num_rows * 4) + align256(nchunks * 4) + align256(nchunks * (size_t)num_slots * 4);
 }
 
-hipError_t launch_build_segments(const int32_t *ids, int n, int num_slots, const lora_segments_t &seg, void *ws,
-                                 hipStream_t stream) {
+hipError_t launch_build_segments(const int32_t *ids, int stride, int n, int num_slots, bool add_status,
+                                 const lora_segments_t &seg, void *ws, hipStream_t stream) {
   char *w = static_cast<char *>(ws);
   if (n <= 256) {
-    seg_small_kernel<256><<<1, 256, 0, stream>>>(ids, n, num_slots, seg, reinterpret_cast<int32_t *>(w));
+    seg_small_kernel<256><<<1, 256, 0, stream>>>(ids, stride, n, num_slots, add_status, seg,
+                                                 reinterpret_cast<int32_t *>(w));
     return hipGetLastError();
   }
   if (n <= kSegSmallMax) {
-    seg_small_kernel<kSegSmallMax><<<1, kSegSmallMax, 0, stream>>>(ids, n, num_slots, seg,
+    seg_small_kernel<kSegSmallMax><<<1, kSegSmallMax, 0, stream>>>(ids, stride, n, num_slots, add_status, seg,
                                                                   reinterpret_cast<int32_t *>(w));
     return hipGetLastError();
   }
@@ -257,13 +263,13 @@ hipError_t launch_build_segments(const int32_t *ids, int n, int num_slots, const
   int32_t *badc = reinterpret_cast<int32_t *>(w);
   w += align256((size_t)nchunks * 4);
   int32_t *hist = reinterpret_cast<int32_t *>(w);
-  seg_chunk_kernel<<<nchunks, kSegChunk, 0, stream>>>(ids, n, num_slots, nchunks, hist, lrank, badc);
+  seg_chunk_kernel<<<nchunks, kSegChunk, 0, stream>>>(ids, stride, n, num_slots, nchunks, hist, lrank, badc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  seg_scan_kernel<<<1, kScanThreads, 0, stream>>>(num_slots, nchunks, seg, hist, badc);
+  seg_scan_kernel<<<1, kScanThreads, 0, stream>>>(num_slots, nchunks, add_status, seg, hist, badc);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  seg_scatter_kernel<<<nchunks, kSegChunk, 0, stream>>>(ids, n, num_slots, nchunks, seg, hist, lrank);
+  seg_scatter_kernel<<<nchunks, kSegChunk, 0, stream>>>(ids, stride, n, num_slots, nchunks, seg, hist, lrank);
   return hipGetLastError();
 }
 

@@ -289,6 +289,43 @@ lora_status_t lora_layer_expand(const lora_module_io_t *io, uint32_t module_mask
                                 int32_t max_rank, void *ws, size_t ws_bytes,
                                 void *stream);
 
+/* Most adapters one row may carry in lora_apply_layer_stacked. */
+#define LORA_MAX_STACK 8
+
+/*
+ * lora_apply_layer_stacked -- several adapters on one row: y += sum over the
+ * row's list of scale_a * B_a . (A_a . x) for every projection in
+ * module_mask.  Source: "m07 -- Multi-Adapter (LoRA) Serving", "9.
+ * Bottlenecks and Evolution", item 5 (multi-adapter composition: two
+ * adapters on one request, each one more read and one more kernel pass).
+ * Pass t = 0 .. depth-1, in stream order: the segments of column t of
+ * row_adapters (as lora_build_segments), then the shrink and the expand of
+ * lora_apply_layer.  Each distinct adapter of a column is read once in its
+ * pass.  y is rounded to bf16 after each pass (as by depth calls of
+ * lora_apply_layer), so the delta of pass t is added to the rounded result of
+ * the passes before it.
+ *
+ *   row_adapters  device int32 [num_rows][depth]: the adapter slots of each
+ *                 row, in pass order; negative entries add nothing (a row
+ *                 with fewer adapters pads its list with -1)
+ *   depth         1 .. LORA_MAX_STACK
+ *   seg           device segments as for lora_build_segments; on return they
+ *                 describe the last pass.  *seg.status sums the bad ids of
+ *                 every pass and the delta calls' additions.
+ *   ws, ws_bytes  at least lora_workspace_bytes(num_rows, num_slots,
+ *                 max_rank, sum of the masked d_in); shared by the passes
+ *   other arguments as for lora_apply_layer.
+ *
+ * Errors: those of lora_apply_layer and lora_build_segments, and
+ * LORA_ERR_SHAPE for a depth outside [1, LORA_MAX_STACK].
+ */
+lora_status_t lora_apply_layer_stacked(const lora_module_io_t *io, uint32_t module_mask,
+                                       int32_t num_rows, const int32_t *row_adapters,
+                                       int32_t depth, const lora_adapter_entry_t *table,
+                                       int32_t num_slots, lora_segments_t seg,
+                                       int32_t max_rank, void *ws, size_t ws_bytes,
+                                       void *stream);
+
 /*
  * lora_form_batch -- choose the requests of the next step from a waiting
  * queue so that the batch shares adapters (host code; no device work, no

@@ -23,6 +23,11 @@ Functions and the passages they follow:
 * int8 factors ("9. Bottlenecks and Evolution" on "m07", item 3: quantised
   adapters) -- dequantised exactly (one fp32 scale per row), then the same
   sums.
+* ``lora_layer_stacked`` -- several adapters on one row (same section, item
+  5: multi-adapter composition): each projection's delta is the sum of the
+  single-adapter deltas of the row's list, y = y0 + that sum.
+* ``batch_former.form_batch`` -- the adapter-aware batch former ("6. Deep
+  Dive A", "The adapter-aware scheduler"; "The Revision", R1).
 """
 from __future__ import annotations
 
@@ -182,4 +187,33 @@ def lora_layer(workload, rows=None, modules=None) -> dict:
         out[m.name] = lora_module(workload.x[m.x_name], workload.y0[m.name], workload.ids,
                                   A_ptrs, B_ptrs, ranks, scales, workload.max_rank, rows=rows,
                                   fmts=workload.fmt[:, m.index])
+    return out
+
+
+def lora_layer_stacked(workload, row_adapters, rows=None, modules=None) -> dict:
+    """Several adapters per row: ``row_adapters`` int32 [num_rows, depth]
+    (negative entries add nothing).  For every projection, delta = sum over t
+    of the single-adapter delta of column t, in fp64; y = y0 + delta.
+
+    Returns {module_name: ModuleResult}; ``v`` is [depth, n_sel, max_rank]
+    and ``num_bad_rank`` the sum over the passes.
+    """
+    ra = np.ascontiguousarray(row_adapters, dtype=np.int32)
+    assert ra.ndim == 2 and ra.shape[0] == workload.num_rows
+    out = {}
+    for m in workload.modules:
+        if modules is not None and m.name not in modules:
+            continue
+        A_ptrs, B_ptrs, ranks, scales = workload.host_table(m.index)
+        passes = [lora_module(workload.x[m.x_name], workload.y0[m.name], ra[:, t], A_ptrs, B_ptrs, ranks, scales,
+                              workload.max_rank, rows=rows, fmts=workload.fmt[:, m.index])
+                  for t in range(ra.shape[1])]
+        delta = passes[0].delta.copy()
+        for p in passes[1:]:
+            delta += p.delta
+        sel = np.arange(workload.num_rows) if rows is None else np.asarray(rows)
+        y0 = workload.y0[m.name][sel, :m.d_out]
+        y0 = (y0.astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # bf16 bits, decoded exactly
+        out[m.name] = ModuleResult(np.stack([p.v for p in passes]), delta, y0 + delta,
+                                   sum(p.num_bad_rank for p in passes))
     return out
