@@ -76,7 +76,8 @@ def lib() -> ctypes.CDLL:
             f.restype = st
             f.argtypes = [ctypes.POINTER(_IO), u32, i32, vp, i32, _Seg, i32, vp, sz, vp]
         L.lora_apply_layer_stacked.restype = st
-        L.lora_apply_layer_stacked.argtypes = [ctypes.POINTER(_IO), u32, i32, vp, i32, vp, i32, _Seg, i32, vp, sz, vp]
+        L.lora_apply_layer_stacked.argtypes = [ctypes.POINTER(_IO), u32, i32, vp, i32, vp, vp, i32, _Seg, i32, vp, sz,
+                                               vp]
         L.lora_form_batch.restype = st
         L.lora_form_batch.argtypes = [vp, i32, vp, ctypes.c_float, i32, i32, i32, i32, vp, vp]
         _lib = L
@@ -242,17 +243,25 @@ def layer_expand(ios, num_rows, table, num_slots, seg, max_rank, ws, stream=None
 
 
 def apply_layer_stacked(ios, num_rows, row_adapters, table, num_slots, seg, max_rank, ws, stream=None,
-                        module_mask=None):
+                        module_mask=None, pass_max_rank=None):
     """Several adapters per row (``row_adapters``: device int32 [num_rows, depth],
-    -1 pads); see lora_apply_layer_stacked."""
+    -1 pads; ``pass_max_rank``: optional largest rank of each column); see
+    lora_apply_layer_stacked."""
     import torch
     _need(row_adapters, torch.int32, "row_adapters", 2)
     if row_adapters.shape[0] < num_rows or not row_adapters.is_contiguous():
         raise ValueError("row_adapters: a contiguous [num_rows, depth] tensor")
+    depth = row_adapters.shape[1]
+    pr = None
+    if pass_max_rank is not None:
+        pr = np.ascontiguousarray(pass_max_rank, dtype=np.int32)
+        if pr.shape != (depth,):
+            raise ValueError("pass_max_rank: one rank per column")
     arr, mask = _ios(ios, num_rows)
     if module_mask is None:
         module_mask = mask
-    _check(lib().lora_apply_layer_stacked(arr, module_mask, num_rows, _ptr(row_adapters), row_adapters.shape[1],
+    _check(lib().lora_apply_layer_stacked(arr, module_mask, num_rows, _ptr(row_adapters), depth,
+                                          None if pr is None else pr.ctypes.data_as(ctypes.c_void_p),
                                           _ptr(table), num_slots, seg.c(), max_rank, _ptr(ws),
                                           ws.numel() * ws.element_size(), _stream(stream)),
            "lora_apply_layer_stacked")

@@ -305,7 +305,7 @@ lora_status_t lora_apply_layer(const lora_module_io_t *io, uint32_t module_mask,
 // in stream order (a row is in one segment per pass, so no two blocks of a
 // launch touch the same y).
 lora_status_t lora_apply_layer_stacked(const lora_module_io_t *io, uint32_t module_mask, int32_t num_rows,
-                                       const int32_t *row_adapters, int32_t depth,
+                                       const int32_t *row_adapters, int32_t depth, const int32_t *pass_max_rank,
                                        const lora_adapter_entry_t *table, int32_t num_slots, lora_segments_t seg,
                                        int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
   ModuleArgs ms[LORA_NUM_MODULES];
@@ -314,6 +314,9 @@ lora_status_t lora_apply_layer_stacked(const lora_module_io_t *io, uint32_t modu
   if (st != LORA_OK) return st;
   if (depth < 1 || depth > LORA_MAX_STACK) return LORA_ERR_SHAPE;
   if (num_rows > 0 && !row_adapters) return LORA_ERR_NULL;
+  if (pass_max_rank)
+    for (int t = 0; t < depth; ++t)
+      if (pass_max_rank[t] < 1 || pass_max_rank[t] > max_rank) return LORA_ERR_RANK;
   const size_t need = segments_ws_bytes(num_rows, num_slots);
   if (need > 0 && !ws) return LORA_ERR_NULL;
   if (need > 0 && !aligned16(ws)) return LORA_ERR_ALIGN;
@@ -322,9 +325,10 @@ lora_status_t lora_apply_layer_stacked(const lora_module_io_t *io, uint32_t modu
   for (int t = 0; t < depth; ++t) {
     st = launched(launch_build_segments(row_adapters + t, depth, num_rows, num_slots, t > 0, seg, ws, s));
     if (st != LORA_OK || num_rows == 0) return st;  // no rows: the first pass only resets the segments
-    st = launch_phase(true, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
+    const int r = pass_max_rank ? pass_max_rank[t] : max_rank;  // the pass's launch class
+    st = launch_phase(true, ms, n, num_rows, num_slots, r, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
     if (st != LORA_OK) return st;
-    st = launch_phase(false, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
+    st = launch_phase(false, ms, n, num_rows, num_slots, r, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
     if (st != LORA_OK) return st;
   }
   return LORA_OK;

@@ -34,6 +34,8 @@ DESCRIPTIONS = {
     "full_layer_r64_int8": "70B full layer decode as full_layer_r64, adapters int8 with one fp32 scale per row",
     "zipf_formed": "Zipf(1.1) decode over zipf_paged's 512 paged adapters: 256 rows chosen from a 512-request queue "
                    "by the adapter-aware batch former (cap 32 adapters, 4 tail slots, at least 128 rows)",
+    "stacked_layer": "70B full layer decode, two adapters per row: one of 4 shared domain adapters (rank 64) and a "
+                     "style adapter of its own (rank 16), all 7 projections, 128 rows; one pass per adapter",
 }
 
 
@@ -56,13 +58,14 @@ def formed_workload(gen):
     return gen.zipf_paged(ids=q[sel], name="zipf_formed"), report
 
 
-def algorithmic(w):
-    """Bytes and FLOPs the method must move per step: each distinct adapter
-    once at its own rank, each input tensor once, y read and written once;
-    split into the shrink side (A, x) and the expand side (B, y)."""
+def algorithmic(w, ids=None):
+    """Bytes and FLOPs the method must move per step (per pass with ``ids``):
+    each distinct adapter once at its own rank, each input tensor once, y read
+    and written once; split into the shrink side (A, x) and the expand side
+    (B, y)."""
     from adapter_gemv_amd.traffic import step_traffic
-    return step_traffic(w.ids, w.num_slots, [(m.name, m.index, m.d_in, m.d_out, m.x_name) for m in w.modules],
-                        w.ranks, w.fmt)
+    return step_traffic(w.ids if ids is None else ids, w.num_slots,
+                        [(m.name, m.index, m.d_in, m.d_out, m.x_name) for m in w.modules], w.ranks, w.fmt)
 
 
 def cpu_baseline(w, min_seconds=10.0, max_passes=64):
@@ -81,8 +84,13 @@ def cpu_baseline(w, min_seconds=10.0, max_passes=64):
     t0 = time.perf_counter()
     passes = 0
     while True:
-        oracle.build_segments(w.ids, w.num_slots)
-        oracle.lora_layer(w, rows=rows)
+        if w.stack is None:
+            oracle.build_segments(w.ids, w.num_slots)
+            oracle.lora_layer(w, rows=rows)
+        else:
+            for t in range(w.stack.shape[1]):
+                oracle.build_segments(w.stack[:, t], w.num_slots)
+            oracle.lora_layer_stacked(w, w.stack, rows=rows)
         passes += 1
         el = time.perf_counter() - t0
         if el >= min_seconds or passes >= max_passes:
@@ -296,7 +304,12 @@ def main():
         w, former = formed_workload(gen)
     else:
         w = gen.make_workload(args.workload)
-    traffic = algorithmic(w)
+    if w.stack is None:
+        traffic = algorithmic(w)
+        passes = [traffic]
+    else:  # one pass per column: each reads its adapters, x and y again
+        passes = [algorithmic(w, w.stack[:, t]) for t in range(w.stack.shape[1])]
+        traffic = {k: sum(p[k] for p in passes) for k in passes[0]}
     adapters_bytes = traffic["adapters"]
     reps = args.replicas or max(1, int(np.ceil(1.0e9 / max(adapters_bytes, 1))))
     reps = min(reps, 64)
@@ -309,8 +322,18 @@ def main():
     # Every launch and every event goes on one stream of default priority.
     stream = torch.cuda.Stream()
 
+    stack = None if w.stack is None else torch.from_numpy(np.ascontiguousarray(w.stack)).cuda()
+    # each pass's launch class: the largest rank among its column's adapters (the caller knows it)
+    pass_rank = [w.max_rank] if stack is None else [
+        max(1, int(w.ranks[w.stack[:, t][(w.stack[:, t] >= 0) & (w.stack[:, t] < w.num_slots)]].max(initial=1)))
+        for t in range(w.stack.shape[1])]
+
     def launch(i):
         d = dws[i % reps]
+        if stack is not None:
+            lg.apply_layer_stacked(d.ios, w.num_rows, stack, d.table, w.num_slots, d.seg, w.max_rank, d.ws, stream,
+                                   pass_max_rank=pass_rank)
+            return
         d.build_segments(stream)
         lg.layer_shrink(d.ios, w.num_rows, d.table, w.num_slots, d.seg, w.max_rank, d.ws, stream)
         lg.layer_expand(d.ios, w.num_rows, d.table, w.num_slots, d.seg, w.max_rank, d.ws, stream)
@@ -346,17 +369,33 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / args.steps * 1e3
 
-    seg_us = phase_us(lambda d: d.build_segments(stream))
-    shr_us = phase_us(lambda d: lg.layer_shrink(d.ios, w.num_rows, d.table, w.num_slots, d.seg, w.max_rank, d.ws,
-                                                stream))
-    exp_us = phase_us(lambda d: lg.layer_expand(d.ios, w.num_rows, d.table, w.num_slots, d.seg, w.max_rank, d.ws,
-                                                stream))
-    phases = {"segments": (seg_us, 0), "shrink": (shr_us, traffic["shrink_bytes"]),
-              "expand": (exp_us, traffic["expand_bytes"])}
-    dom = max(("shrink", "expand"), key=lambda k: phases[k][0])
-    dom_us, dom_bytes = phases[dom]
-    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    kernel_name = f"lora_{dom}_kernel<{rank_class(w.max_rank)}>"
+    # A stacked step runs the kernels once per pass (one column of the adapter
+    # lists each, in that column's rank class); a kernel's figures sum over
+    # its launches in a step.
+    cols = [None] if stack is None else [stack[:, t].contiguous() for t in range(stack.shape[1])]
+    per_pass = []
+    kernels = {}  # name -> [launches, us, algorithmic bytes] per step
+    for t, col in enumerate(cols):
+        r = pass_rank[t]
+        if col is None:
+            seg_us = phase_us(lambda d: d.build_segments(stream))
+        else:
+            seg_us = phase_us(lambda d: lg.build_segments(col, w.num_slots, d.seg, d.ws, stream))
+        shr_us = phase_us(lambda d: lg.layer_shrink(d.ios, w.num_rows, d.table, w.num_slots, d.seg, r, d.ws, stream))
+        exp_us = phase_us(lambda d: lg.layer_expand(d.ios, w.num_rows, d.table, w.num_slots, d.seg, r, d.ws, stream))
+        per_pass.append({"segments": seg_us, "shrink": shr_us, "expand": exp_us})
+        for ph, us in (("shrink", shr_us), ("expand", exp_us)):
+            k = kernels.setdefault(f"lora_{ph}_kernel<{rank_class(r)}>", [0, 0.0, 0])
+            k[0] += 1
+            k[1] += us
+            k[2] += passes[t][ph + "_bytes"]
+    phases = {"segments": (sum(p["segments"] for p in per_pass), 0),
+              "shrink": (sum(p["shrink"] for p in per_pass), traffic["shrink_bytes"]),
+              "expand": (sum(p["expand"] for p in per_pass), traffic["expand_bytes"])}
+    kernel_name = max(kernels, key=lambda k: kernels[k][1])
+    n_launch, tot_us, tot_bytes = kernels[kernel_name]
+    achieved = tot_bytes / (tot_us * 1e-6) / 1e9
+    dom_us, dom_bytes = tot_us / n_launch, int(round(tot_bytes / n_launch))  # per launch
     counted = counter_traffic(args.workload, kernel_name)
 
     out = {
@@ -390,6 +429,12 @@ def main():
     }
     if former is not None:
         out["batch_former"] = former
+    if stack is not None:
+        out["stacked"] = {"depth": len(per_pass), "pass_max_rank": pass_rank,
+                          "passes_us": [{k: round(v, 2) for k, v in p.items()} for p in per_pass],
+                          "algorithmic_bytes_per_pass": [p["total"] for p in passes],
+                          "distinct_adapters_per_pass": [int(np.unique(w.stack[:, t]).size) for t in
+                                                         range(len(per_pass))]}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w)

@@ -309,6 +309,12 @@ lora_status_t lora_layer_expand(const lora_module_io_t *io, uint32_t module_mask
  *                 row, in pass order; negative entries add nothing (a row
  *                 with fewer adapters pads its list with -1)
  *   depth         1 .. LORA_MAX_STACK
+ *   pass_max_rank host int32 [depth] or NULL: the largest rank of the
+ *                 adapters in each column, 1 .. max_rank (NULL: max_rank for
+ *                 every pass).  Each pass is sized for its own rank class, so
+ *                 a column of low-rank adapters does not run in the class of
+ *                 the highest rank; an entry above its pass's rank is a
+ *                 device-data error, as a rank above max_rank is.
  *   seg           device segments as for lora_build_segments; on return they
  *                 describe the last pass.  *seg.status sums the bad ids of
  *                 every pass and the delta calls' additions.
@@ -316,12 +322,14 @@ lora_status_t lora_layer_expand(const lora_module_io_t *io, uint32_t module_mask
  *                 max_rank, sum of the masked d_in); shared by the passes
  *   other arguments as for lora_apply_layer.
  *
- * Errors: those of lora_apply_layer and lora_build_segments, and
- * LORA_ERR_SHAPE for a depth outside [1, LORA_MAX_STACK].
+ * Errors: those of lora_apply_layer and lora_build_segments,
+ * LORA_ERR_SHAPE for a depth outside [1, LORA_MAX_STACK], and LORA_ERR_RANK
+ * for a pass_max_rank entry outside [1, max_rank].
  */
 lora_status_t lora_apply_layer_stacked(const lora_module_io_t *io, uint32_t module_mask,
                                        int32_t num_rows, const int32_t *row_adapters,
-                                       int32_t depth, const lora_adapter_entry_t *table,
+                                       int32_t depth, const int32_t *pass_max_rank,
+                                       const lora_adapter_entry_t *table,
                                        int32_t num_slots, lora_segments_t seg,
                                        int32_t max_rank, void *ws, size_t ws_bytes,
                                        void *stream);

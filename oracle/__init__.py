@@ -190,10 +190,12 @@ def lora_layer(workload, rows=None, modules=None) -> dict:
     return out
 
 
-def lora_layer_stacked(workload, row_adapters, rows=None, modules=None) -> dict:
+def lora_layer_stacked(workload, row_adapters, rows=None, modules=None, pass_max_rank=None) -> dict:
     """Several adapters per row: ``row_adapters`` int32 [num_rows, depth]
     (negative entries add nothing).  For every projection, delta = sum over t
     of the single-adapter delta of column t, in fp64; y = y0 + delta.
+    ``pass_max_rank`` [depth]: the largest rank column t admits (entries above
+    it are skipped as bad); default the workload's max_rank.
 
     Returns {module_name: ModuleResult}; ``v`` is [depth, n_sel, max_rank]
     and ``num_bad_rank`` the sum over the passes.
@@ -205,8 +207,9 @@ def lora_layer_stacked(workload, row_adapters, rows=None, modules=None) -> dict:
         if modules is not None and m.name not in modules:
             continue
         A_ptrs, B_ptrs, ranks, scales = workload.host_table(m.index)
+        mr = [workload.max_rank] * ra.shape[1] if pass_max_rank is None else [int(r) for r in pass_max_rank]
         passes = [lora_module(workload.x[m.x_name], workload.y0[m.name], ra[:, t], A_ptrs, B_ptrs, ranks, scales,
-                              workload.max_rank, rows=rows, fmts=workload.fmt[:, m.index])
+                              mr[t], rows=rows, fmts=workload.fmt[:, m.index])
                   for t in range(ra.shape[1])]
         delta = passes[0].delta.copy()
         for p in passes[1:]:
@@ -214,6 +217,8 @@ def lora_layer_stacked(workload, row_adapters, rows=None, modules=None) -> dict:
         sel = np.arange(workload.num_rows) if rows is None else np.asarray(rows)
         y0 = workload.y0[m.name][sel, :m.d_out]
         y0 = (y0.astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # bf16 bits, decoded exactly
-        out[m.name] = ModuleResult(np.stack([p.v for p in passes]), delta, y0 + delta,
-                                   sum(p.num_bad_rank for p in passes))
+        v = np.zeros((len(passes), delta.shape[0], max([workload.max_rank] + mr)), np.float64)
+        for t, p in enumerate(passes):
+            v[t, :, :p.v.shape[1]] = p.v  # each pass's v is as wide as its own max rank
+        out[m.name] = ModuleResult(v, delta, y0 + delta, sum(p.num_bad_rank for p in passes))
     return out

@@ -25,22 +25,22 @@ def _name_case(request):
     note(request.node.nodeid)
 
 
-def run_stacked(dw, ra):
+def run_stacked(dw, ra, pass_max_rank=None):
     w = dw.w
     lg.apply_layer_stacked(dw.ios, w.num_rows, torch.from_numpy(np.ascontiguousarray(ra, np.int32)).cuda(),
-                           dw.table, w.num_slots, dw.seg, w.max_rank, dw.ws)
+                           dw.table, w.num_slots, dw.seg, w.max_rank, dw.ws, pass_max_rank=pass_max_rank)
     torch.cuda.synchronize()
 
 
-def check_stacked(w, ra):
-    ref = oracle.lora_layer_stacked(w, ra)
+def check_stacked(w, ra, pass_max_rank=None):
+    ref = oracle.lora_layer_stacked(w, ra, pass_max_rank=pass_max_rank)
     dw = DeviceWorkload(w)
     dw.reset_y(zero=True)
-    run_stacked(dw, ra)
+    run_stacked(dw, ra, pass_max_rank)
     for m in w.modules:
         check_rows(bf16_host(dw.y[m.name]), ref[m.name].delta, f"{w.name}/{m.name} stacked delta")
     dw.reset_y()
-    run_stacked(dw, ra)
+    run_stacked(dw, ra, pass_max_rank)
     for m in w.modules:
         check_rows(bf16_host(dw.y[m.name]), ref[m.name].y, f"{w.name}/{m.name} stacked y")
     return dw
@@ -56,7 +56,8 @@ def test_depth_one_is_the_layer_call_bit_for_bit():
     assert np.array_equal(bf16_host(a.y["q"]), bf16_host(b.y["q"]))
 
 
-def test_two_adapters_per_decode_row():
+@pytest.mark.parametrize("pass_max_rank", [None, (64, 24)])
+def test_two_adapters_per_decode_row(pass_max_rank):
     # a domain adapter (few, shared) and a style adapter (one per row, some rows without)
     rng = np.random.default_rng(2)
     rows, n_dom, n_sty = 96, 3, 96
@@ -68,7 +69,25 @@ def test_two_adapters_per_decode_row():
     ra = np.stack([rng.integers(0, n_dom, size=rows), n_dom + rng.permutation(rows)], 1).astype(np.int32)
     ra[rng.random(rows) < 0.2, 1] = -1
     w = bw(62, rows, n_dom + n_sty, 4096, 2056, None, ra[:, 0], ranks=ranks, scales=scales, x_std=1.0)
-    check_stacked(w, ra)
+    check_stacked(w, ra, pass_max_rank)
+
+
+def test_entries_above_their_pass_rank_are_skipped_and_counted():
+    # style ranks 8..24 under a pass rank of 16: the 24s are device-data errors
+    rng = np.random.default_rng(5)
+    rows, n_dom, n_sty = 64, 2, 64
+    ranks = np.zeros((n_dom + n_sty, 7), np.int32)
+    ranks[:n_dom, 0] = 32
+    ranks[n_dom:, 0] = rng.choice([8, 16, 24], size=n_sty)
+    ra = np.stack([rng.integers(0, n_dom, size=rows), n_dom + rng.permutation(rows)], 1).astype(np.int32)
+    w = bw(65, rows, n_dom + n_sty, 2048, 1024, None, ra[:, 0], ranks=ranks, x_std=1.0)
+    dw = check_stacked(w, ra, (32, 16))
+    *_, status = dw.seg.host()
+    assert status > 0
+    with pytest.raises(lg.LoraError, match="LORA_ERR_RANK"):
+        run_stacked(dw, ra, (65, 16))
+    with pytest.raises(lg.LoraError, match="LORA_ERR_RANK"):
+        run_stacked(dw, ra, (32, 0))
 
 
 @pytest.mark.parametrize("seed", range(3))
@@ -115,3 +134,9 @@ def test_zero_rows_resets_the_segments():
     torch.cuda.synchronize()
     _, offs, _, status = dw.seg.host()
     assert status == 0
+
+
+def test_stacked_layer_full_size():
+    # the bench's workload: 70B layer, 128 rows, a shared domain adapter (r64) and a style adapter (r16) per row
+    w = gen.make_workload("stacked_layer")
+    check_stacked(w, w.stack, (64, 16))

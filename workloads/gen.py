@@ -118,6 +118,7 @@ class Workload:
     seq_lens: np.ndarray | None = None
     notes: dict = field(default_factory=dict)
     fmt: np.ndarray | None = None    # int32 [num_slots, N_MOD]: FMT_BF16 or FMT_INT8_ROWS
+    stack: np.ndarray | None = None  # int32 [num_rows, depth]: several adapters per row (ids = column 0)
 
     def __post_init__(self):
         if self.fmt is None:
@@ -405,6 +406,23 @@ def full_layer(seed=3, rank=64, rows=128, fmt=FMT_BF16):
                           x_of=X_OF_70B, x_std=1.0, ab_std=0.02, y_std=1.0, fmt=fmt)
 
 
+def stacked_layer(seed=7, rows=128, n_domain=4, domain_rank=64, style_rank=16):
+    """70B layer, all seven projections, two adapters per row: one of
+    ``n_domain`` shared domain adapters (rank 64) and a style adapter of its own
+    (rank 16), the "domain + style" composition of "9. Bottlenecks and
+    Evolution", item 5, on "m07 -- Multi-Adapter (LoRA) Serving".  Slots
+    [0, n_domain) hold the domain adapters, the next ``rows`` the styles."""
+    g = _rng(seed, _R_IDS)
+    stack = np.stack([g.integers(0, n_domain, size=rows), n_domain + g.permutation(rows)], 1).astype(np.int32)
+    slots = n_domain + rows
+    ranks = np.full((slots, N_MOD), style_rank, np.int32)
+    ranks[:n_domain] = domain_rank
+    w = build_workload(f"stacked_layer_{n_domain}x{domain_rank}_{rows}x{style_rank}", seed, rows, slots, SHAPES_70B,
+                       stack[:, 0], ranks, x_of=X_OF_70B, x_std=1.0, ab_std=0.02, y_std=1.0)
+    w.stack = stack
+    return w
+
+
 def zipf_ids(seed, num_rows, num_slots, s=1.1):
     """Finite Zipf(s) over num_slots popularity ranks by inverse CDF, mapped to
     slot ids through a seeded permutation."""
@@ -488,6 +506,7 @@ WORKLOADS = {
     "prefill_r16": lambda seed=5: prefill(seed, rank=16),
     "prefill_r64": lambda seed=5: prefill(seed, rank=64),
     "full_layer_r64_int8": lambda seed=3: full_layer(seed, fmt=FMT_INT8_ROWS),
+    "stacked_layer": stacked_layer,
 }
 
 
