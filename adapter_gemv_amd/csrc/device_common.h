@@ -265,12 +265,12 @@ __device__ __forceinline__ bool load_entry(const LayerDesc &d, int a, int col, b
 // LDS, so the wait for v does not wait for the caller's stream.  With few
 // rows the chunks are also split across threads and combined in LDS (v_lds
 // needs 64*ROWS + 1024 floats then).  finish() ends with a block barrier.
-template <int ROWS>
+template <int ROWS, int UR = 0>
 struct VStage {
   static constexpr int PAIRS = ROWS * 16;  // (row, 4-column group) pairs
   static constexpr int PER = PAIRS >= kDecodeThreads ? PAIRS / kDecodeThreads : 1;
   static constexpr int SPLIT = PAIRS >= kDecodeThreads ? 1 : kDecodeThreads / PAIRS;  // threads per pair
-  static constexpr int U = PER >= 4 ? 2 : SPLIT > 1 ? 2 : 8;                           // chunks per round
+  static constexpr int U = UR > 0 ? UR : PER >= 4 ? 2 : SPLIT > 1 ? 2 : 8;             // chunks per round
   static_assert(PAIRS % kDecodeThreads == 0 || kDecodeThreads % PAIRS == 0, "rows per stage");
 
   int p0, nr, rank, part;

@@ -43,8 +43,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CLS <= 1 ? 
   constexpr int LPR = 1 << CLS;                          // lanes per output row (decode)
   __shared__ float lds[expand_lds_floats<LPR>()];
   constexpr int KT = CLS <= 2 ? 1 : 2;                   // 32-wide rank steps (SGMV)
+  // k-chunk partials per round of the SGMV V staging: 4 where the register
+  // bound leaves room (ranks 32 and 64), else 2
+  constexpr int VU = CLS >= 2 ? 4 : 2;
   if ((int)blockIdx.x < decode_blocks) decode_expand_block<LPR>(d, blockIdx.x, lds);
-  else sgmv_expand_block<KT>(d, blockIdx.x - decode_blocks, lds);
+  else sgmv_expand_block<KT, VU>(d, blockIdx.x - decode_blocks, lds);
 }
 
 // lora_shrink: sum the k-chunk partials of each row in a segment into

@@ -249,8 +249,9 @@ __device__ __forceinline__ void sgmv_shrink_block(const LayerDesc &d, int blk, u
 // 16-byte load; past the rank they are zero (masked) or padding that meets
 // zeros of V.  Q8: the 8 values are 8 int8 bytes (rows ldb8 bytes apart),
 // widened to bf16 exactly; the row scales of the n-tile wait in LDS after V
-// and multiply the sums in the y update.
-template <int KT, bool Q8>
+// and multiply the sums in the y update.  VU = k-chunk partials summed per
+// round of V staging (each round waits for the one before).
+template <int KT, bool Q8, int VU>
 __device__ __forceinline__ void sgmv_expand_tile(const LayerDesc &d, const ModuleDesc &m, const void *B, int rank,
                                                  float scale, int seg0, int len, int rt, int tile, float *v_lds) {
   constexpr int DE = 1;  // 32-column steps per register set (two sets in flight)
@@ -311,7 +312,7 @@ __device__ __forceinline__ void sgmv_expand_tile(const LayerDesc &d, const Modul
   };
   // V rows of the tile (times scale) into LDS, [64][64] fp32; the first
   // round of its loads goes out before the first register set.
-  VStage<kSgmvExpandRows> vst;
+  VStage<kSgmvExpandRows, VU> vst;
   vst.issue(d, m, seg0 + row0, nrows, rank);
   Set s0, s1;
   issue(s0, 0);
@@ -381,7 +382,7 @@ __device__ __forceinline__ void sgmv_expand_tile(const LayerDesc &d, const Modul
 }
 
 // Block `blk` of the SGMV expand numbering (row tiles x sg_items).
-template <int KT>
+template <int KT, int VU>
 __device__ __forceinline__ void sgmv_expand_block(const LayerDesc &d, int blk, float *v_lds) {
   const int tile_idx = blk / d.sg_items;
   const int it = blk - tile_idx * d.sg_items;
@@ -393,8 +394,10 @@ __device__ __forceinline__ void sgmv_expand_block(const LayerDesc &d, int blk, f
   if (!load_segment(d, s, it == 0 && rt == 0, &a, &seg0, &len)) return;
   lora_adapter_entry_t e;
   if (!load_entry(d, a, m.col, tile == 0 && rt == 0, &e)) return;
-  if (e.format == LORA_FORMAT_INT8_ROWS) sgmv_expand_tile<KT, true>(d, m, e.B, e.rank, e.scale, seg0, len, rt, tile, v_lds);
-  else sgmv_expand_tile<KT, false>(d, m, e.B, e.rank, e.scale, seg0, len, rt, tile, v_lds);
+  if (e.format == LORA_FORMAT_INT8_ROWS)
+    sgmv_expand_tile<KT, true, VU>(d, m, e.B, e.rank, e.scale, seg0, len, rt, tile, v_lds);
+  else
+    sgmv_expand_tile<KT, false, VU>(d, m, e.B, e.rank, e.scale, seg0, len, rt, tile, v_lds);
 }
 
 }  // namespace lora
