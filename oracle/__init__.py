@@ -28,6 +28,10 @@ Functions and the passages they follow:
   single-adapter deltas of the row's list, y = y0 + that sum.
 * ``batch_former.form_batch`` -- the adapter-aware batch former ("6. Deep
   Dive A", "The adapter-aware scheduler"; "The Revision", R1).
+* ``linear_layer`` -- base projection and adapter delta together, y = W.x +
+  delta (same page, "6. Deep Dive A": y = Wx + (BA)x(alpha/r)), the result
+  a fused base + delta kernel produces.  W.x is a numpy matmul over the
+  exactly decoded bf16 values, in fp64.
 """
 from __future__ import annotations
 
@@ -221,4 +225,36 @@ def lora_layer_stacked(workload, row_adapters, rows=None, modules=None, pass_max
         for t, p in enumerate(passes):
             v[t, :, :p.v.shape[1]] = p.v  # each pass's v is as wide as its own max rank
         out[m.name] = ModuleResult(v, delta, y0 + delta, sum(p.num_bad_rank for p in passes))
+    return out
+
+
+def _bf16_f64(bits: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(bits).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def base_projection(W: np.ndarray, x: np.ndarray, rows=None, block: int = 2048) -> np.ndarray:
+    """W.x for the selected rows in fp64: W uint16 (bf16) [d_out, d_in], x
+    uint16 [num_rows, >= d_in].  Each product of two bf16 values is exact in
+    fp64; W is decoded a block of rows at a time."""
+    d_out, d_in = W.shape
+    xs = _bf16_f64(x[:, :d_in] if rows is None else x[np.asarray(rows), :d_in])
+    out = np.empty((xs.shape[0], d_out), np.float64)
+    for n0 in range(0, d_out, block):
+        out[:, n0:n0 + block] = xs @ _bf16_f64(W[n0:n0 + block]).T
+    return out
+
+
+def linear_layer(workload, rows=None, modules=None) -> dict:
+    """Base projection plus adapter delta for every projection of a workload
+    with base weights: {module_name: ModuleResult} with y = W.x + delta (the
+    base output replaces y0)."""
+    out = {}
+    for m in workload.modules:
+        if modules is not None and m.name not in modules:
+            continue
+        A_ptrs, B_ptrs, ranks, scales = workload.host_table(m.index)
+        r = lora_module(workload.x[m.x_name], workload.y0[m.name], workload.ids, A_ptrs, B_ptrs, ranks, scales,
+                        workload.max_rank, rows=rows, fmts=workload.fmt[:, m.index])
+        base = base_projection(workload.W[m.name], workload.x[m.x_name], rows)
+        out[m.name] = ModuleResult(r.v, r.delta, base + r.delta, r.num_bad_rank)
     return out

@@ -41,7 +41,7 @@ _CHUNK = 1 << 22
 _THREADS = max(1, min(16, os.cpu_count() or 1))
 
 # Roles of the independent draws.
-_R_IDS, _R_RANK, _R_PLACE, _R_X, _R_Y, _R_A, _R_B, _R_LEN, _R_PAD = range(9)
+_R_IDS, _R_RANK, _R_PLACE, _R_X, _R_Y, _R_A, _R_B, _R_LEN, _R_PAD, _R_W = range(10)
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -119,6 +119,7 @@ class Workload:
     notes: dict = field(default_factory=dict)
     fmt: np.ndarray | None = None    # int32 [num_slots, N_MOD]: FMT_BF16 or FMT_INT8_ROWS
     stack: np.ndarray | None = None  # int32 [num_rows, depth]: several adapters per row (ids = column 0)
+    W: dict | None = None            # module name -> uint16 [d_out, d_in]: base weights (fused workloads)
 
     def __post_init__(self):
         if self.fmt is None:
@@ -423,6 +424,26 @@ def stacked_layer(seed=7, rows=128, n_domain=4, domain_rank=64, style_rank=16):
     return w
 
 
+def add_base_weights(w: Workload) -> Workload:
+    """Base weights W [d_out, d_in] (bf16, row-major like a linear layer's
+    weight) for every projection, N(0, 1/d_in), so W.x has unit variance like
+    the y0 of the other workloads."""
+    w.W = {}
+    for s in w.modules:
+        w.W[s.name] = normal_bf16(w.seed, (_R_W, s.index), s.d_out * s.d_in,
+                                  1.0 / np.sqrt(s.d_in)).reshape(s.d_out, s.d_in)
+    return w
+
+
+def fused_layer(seed=8, rank=64, rows=128):
+    """The full 70B layer of full_layer_r64 with its base weights: base
+    projection and adapter delta together (1.63 GB of W and 2.65 GB of
+    adapters per step)."""
+    w = full_layer(seed, rank, rows)
+    w.name = f"fused_layer_r{rank}_b{rows}"
+    return add_base_weights(w)
+
+
 def zipf_ids(seed, num_rows, num_slots, s=1.1):
     """Finite Zipf(s) over num_slots popularity ranks by inverse CDF, mapped to
     slot ids through a seeded permutation."""
@@ -507,6 +528,7 @@ WORKLOADS = {
     "prefill_r64": lambda seed=5: prefill(seed, rank=64),
     "full_layer_r64_int8": lambda seed=3: full_layer(seed, fmt=FMT_INT8_ROWS),
     "stacked_layer": stacked_layer,
+    "fused_layer_r64": fused_layer,
 }
 
 
