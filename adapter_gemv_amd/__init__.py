@@ -48,6 +48,11 @@ class _IO(ctypes.Structure):
                 ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32)]
 
 
+class _LinIO(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("ldx", ctypes.c_int64), ("W", ctypes.c_void_p), ("ldw", ctypes.c_int64),
+                ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64), ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -78,6 +83,10 @@ def lib() -> ctypes.CDLL:
         L.lora_apply_layer_stacked.restype = st
         L.lora_apply_layer_stacked.argtypes = [ctypes.POINTER(_IO), u32, i32, vp, i32, vp, vp, i32, _Seg, i32, vp, sz,
                                                vp]
+        L.lora_linear_workspace_bytes.restype = sz
+        L.lora_linear_workspace_bytes.argtypes = [i32, i32, i32, i64, i32]
+        L.lora_linear_layer.restype = st
+        L.lora_linear_layer.argtypes = [ctypes.POINTER(_LinIO), u32, i32, vp, vp, i32, _Seg, i32, vp, sz, vp]
         L.lora_form_batch.restype = st
         L.lora_form_batch.argtypes = [vp, i32, vp, ctypes.c_float, i32, i32, i32, i32, vp, vp]
         _lib = L
@@ -154,6 +163,43 @@ class ModuleIO:
 
 def workspace_bytes(num_rows: int, num_slots: int, max_rank: int, sum_d_in: int) -> int:
     return int(lib().lora_workspace_bytes(num_rows, num_slots, max_rank, sum_d_in))
+
+
+class LinearIO:
+    """One projection for linear_layer: x [rows, >= d_in], W [d_out, >= d_in]
+    (the base weight), y [rows, >= d_out] (written), bf16."""
+
+    def __init__(self, x, W, y, d_in=None, d_out=None):
+        self.x, self.W, self.y = x, W, y
+        self.d_in = int(x.shape[1] if d_in is None else d_in)
+        self.d_out = int(W.shape[0] if d_out is None else d_out)
+
+
+def linear_workspace_bytes(num_rows: int, num_slots: int, max_rank: int, sum_d_in: int, n_modules: int) -> int:
+    return int(lib().lora_linear_workspace_bytes(num_rows, num_slots, max_rank, sum_d_in, n_modules))
+
+
+def linear_layer(ios, num_rows, row_adapter, table, num_slots, seg, max_rank, ws, stream=None, module_mask=None):
+    """Base projection + delta of every projection in ``ios`` ({name:
+    LinearIO}); see lora_linear_layer."""
+    import torch
+    _need(row_adapter, torch.int32, "row_adapter", 1)
+    arr = (_LinIO * 7)()
+    mask = 0
+    for i, name in enumerate(MODULES):
+        io = ios.get(name)
+        if io is None:
+            continue
+        for t, what in ((io.x, "x"), (io.W, "W"), (io.y, "y")):
+            _need(t, torch.bfloat16, f"{name}.{what}", 2)
+        if io.x.shape[0] < num_rows or io.y.shape[0] < num_rows:
+            raise ValueError(f"{name}: fewer rows than num_rows")
+        arr[i] = _LinIO(io.x.data_ptr(), io.x.stride(0), io.W.data_ptr(), io.W.stride(0), io.y.data_ptr(),
+                        io.y.stride(0), io.d_in, io.d_out)
+        mask |= 1 << i
+    _check(lib().lora_linear_layer(arr, mask if module_mask is None else module_mask, num_rows, _ptr(row_adapter),
+                                   _ptr(table), num_slots, seg.c(), max_rank, _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)), "lora_linear_layer")
 
 
 def pack_table(A_ptrs, B_ptrs, ranks, scales, formats=None) -> np.ndarray:

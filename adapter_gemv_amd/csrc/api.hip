@@ -206,6 +206,20 @@ size_t lora_workspace_bytes(int32_t num_rows, int32_t num_slots, int32_t max_ran
   return ws_need(num_rows, num_slots, max_rank, sum_d_in);
 }
 
+// The fused layer's workspace: the shrink's partials, then one v plane
+// [num_rows][rs] per projection (256-byte aligned); at least the segment
+// builder's.
+size_t lora_linear_workspace_bytes(int32_t num_rows, int32_t num_slots, int32_t max_rank, int64_t sum_d_in,
+                                   int32_t n_modules) {
+  if (num_rows < 0 || num_slots < 1 || max_rank < 1 || max_rank > LORA_MAX_RANK || sum_d_in < 0 || n_modules < 1 ||
+      n_modules > LORA_NUM_MODULES)
+    return 0;
+  const size_t part = (partials_ws_bytes(num_rows, max_rank, sum_d_in) + 255) & ~(size_t)255;
+  const size_t vplanes = (size_t)n_modules * num_rows * partial_row_stride(max_rank) * 4;
+  const size_t seg = segments_ws_bytes(num_rows, num_slots);
+  return part + vplanes > seg ? part + vplanes : seg;
+}
+
 const char *lora_status_string(lora_status_t status) {
   switch (status) {
     case LORA_OK: return "LORA_OK";
@@ -298,6 +312,88 @@ lora_status_t lora_apply_layer(const lora_module_io_t *io, uint32_t module_mask,
                                const lora_adapter_entry_t *table, int32_t num_slots, lora_segments_t seg,
                                int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
   return layer_phase(true, true, io, module_mask, num_rows, table, num_slots, seg, max_rank, ws, ws_bytes, stream);
+}
+
+// Base projection + delta: the grouped shrink, the partials summed into one v
+// plane per projection (original row order), then the fused kernel.
+lora_status_t lora_linear_layer(const lora_linear_io_t *io, uint32_t module_mask, int32_t num_rows,
+                                const int32_t *row_adapter, const lora_adapter_entry_t *table, int32_t num_slots,
+                                lora_segments_t seg, int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
+  if (!io || !table) return LORA_ERR_NULL;
+  lora_status_t st = check_segments(seg);
+  if (st != LORA_OK) return st;
+  if (module_mask == 0 || module_mask >= (1u << LORA_NUM_MODULES)) return LORA_ERR_MODULE;
+  if (num_rows < 0 || num_slots < 1) return LORA_ERR_SHAPE;
+  if (max_rank < 1 || max_rank > LORA_MAX_RANK) return LORA_ERR_RANK;
+  if (num_rows > 0 && !row_adapter) return LORA_ERR_NULL;
+  ModuleArgs ms[LORA_NUM_MODULES];
+  int n = 0;
+  int64_t sum_d_in = 0;
+  for (int c = 0; c < LORA_NUM_MODULES; ++c) {
+    if (!(module_mask & (1u << c))) continue;
+    const lora_linear_io_t &m = io[c];
+    if (!m.x || !m.y || !m.W) return LORA_ERR_NULL;
+    if (m.d_in <= 0 || m.d_out <= 0 || m.ldx < m.d_in || m.ldy < m.d_out || m.ldw < m.d_in) return LORA_ERR_SHAPE;
+    if ((m.d_in & 7) || (m.d_out & 7) || (m.ldx & 7) || (m.ldy & 7) || (m.ldw & 7) || !aligned16(m.x) ||
+        !aligned16(m.y) || !aligned16(m.W))
+      return LORA_ERR_ALIGN;
+    if (!fits_u32(num_rows, m.ldx) || !fits_u32(num_rows, m.ldy) || !fits_u32(m.d_out, m.ldw)) return LORA_ERR_SHAPE;
+    ms[n] = ModuleArgs{m.x, m.ldx, m.y, m.ldy, m.d_in, m.d_out, c};
+    sum_d_in += m.d_in;
+    ++n;
+  }
+  const size_t need = lora_linear_workspace_bytes(num_rows, num_slots, max_rank, sum_d_in, n);
+  if (!ws) return LORA_ERR_NULL;
+  if (!aligned16(ws)) return LORA_ERR_ALIGN;
+  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
+  const int rs = partial_row_stride(max_rank);
+  if ((int64_t)num_rows * rs * 4 > (int64_t)0xFFFFFF00) return LORA_ERR_SHAPE;
+  if (num_rows == 0) return LORA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // 1. v partials of every projection (segment-grouped: each adapter's A once)
+  st = launch_phase(true, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
+  if (st != LORA_OK) return st;
+  // 2. one v plane per projection, rows in their original order
+  float *vplanes = reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                             ((partials_ws_bytes(num_rows, max_rank, sum_d_in) + 255) & ~(size_t)255));
+  LayerDesc d;
+  fill_desc(d, ms, n, true, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws);
+  d.v_out = vplanes;
+  d.ldv = rs;
+  st = launched(launch_shrink_reduce(d, s));
+  if (st != LORA_OK) return st;
+  // 3. base projection + delta
+  FusedDesc f{};
+  const int row_tiles = (num_rows + kFusedRows - 1) / kFusedRows;
+  int64_t blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    const lora_linear_io_t &m = io[ms[i].col];
+    FusedModule &fm = f.mod[i];
+    fm.x = static_cast<const uint16_t *>(m.x);
+    fm.ldx = m.ldx;
+    fm.W = static_cast<const uint16_t *>(m.W);
+    fm.ldw = m.ldw;
+    fm.y = static_cast<uint16_t *>(m.y);
+    fm.ldy = m.ldy;
+    fm.v = vplanes + (int64_t)i * num_rows * rs;
+    fm.d_in = m.d_in;
+    fm.d_out = m.d_out;
+    fm.col = ms[i].col;
+    fm.n_tiles = (m.d_out + kFusedCols - 1) / kFusedCols;
+    fm.block_base = (int)blocks;
+    blocks += (int64_t)row_tiles * fm.n_tiles;
+  }
+  if (blocks > 0x7fffffff) return LORA_ERR_SHAPE;
+  f.n_active = n;
+  f.num_rows = num_rows;
+  f.num_slots = num_slots;
+  f.table_cols = LORA_NUM_MODULES;
+  f.max_rank = max_rank;
+  f.rs = rs;
+  f.ids = row_adapter;
+  f.status = seg.status;
+  f.table = table;
+  return launched(launch_fused(f, (int)blocks, s));
 }
 
 // One pass per position of the rows' adapter lists: the segments of that

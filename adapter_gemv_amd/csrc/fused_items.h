@@ -1,0 +1,261 @@
+// Base projection and adapter delta in one pass over the base weight:
+//     y[b] = bf16( W . x[b] + scale_a * B_a . v[b] ),   a = the row's adapter.
+//
+// "m07 -- Multi-Adapter (LoRA) Serving", "6. Deep Dive A": the forward is
+// y = Wx + (B.A)x(alpha/r), the base term shared by the batch and the adapter
+// term per row; "Fused mixed-precision base + delta" on the pages' list of
+// next steps puts the delta into the base product's epilogue with a wide
+// accumulator, so y is written once instead of written and then updated.
+//
+// A block takes kFusedRows rows (in their original order) and kFusedCols
+// output columns of one projection, over the whole d_in:
+//   * main loop: x and W stream through LDS in rounds of 64 k, two rounds in
+//     flight in registers, as in the SGMV shrink (x rows from L2, W rows from
+//     HBM once, nontemporal); wave w turns rows [32w, 32w+32) x the 64
+//     columns into 2 x 4 bf16 matrix-core tiles (16x16x32, fp32 accumulate);
+//   * epilogue: the base tile goes to LDS, then each wave streams the B slice
+//     (the block's 64 rows of B_a, rank values each) of one of its rows per
+//     round, one round ahead, with the row's v (from the grouped shrink);
+//     8 lanes share a B row (8 values each), a reduce-scatter leaves one
+//     output column per lane, and y is written once.
+// The table entries of the block's rows are loaded with the first rounds of
+// the main loop (one row per lane), so the epilogue starts without waiting.
+#pragma once
+
+#include "device_common.h"
+#include "sgmv_items.h"
+
+namespace lora {
+
+// The descriptor of the fused kernel, read from its argument segment (see
+// kernel_desc: indexing the by-value argument copies it to scratch memory).
+__device__ __forceinline__ const FusedDesc &fused_desc() {
+  return *(const FusedDesc *)(const void *)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
+__device__ __forceinline__ FusedModule fused_module_of(const FusedDesc &f, int blk) {
+  int mi = 0;
+#pragma unroll
+  for (int k = 1; k < kMaxModules; ++k)
+    if (k < f.n_active && blk >= f.mod[k].block_base) mi = k;
+  return fused_desc().mod[mi];
+}
+
+constexpr int kFusedBaseStride = kFusedCols + 1;  // floats per row of the base tile in LDS (odd: no bank clash)
+static_assert(kFusedRows * kFusedBaseStride * 4 <= 2 * kShrinkBufBytes, "base tile fits the round buffers");
+
+// One epilogue row: per lane 8 pieces of the B slice (q = 0..7: B row
+// n0 + 8q + lane/8, values 8*(lane%8) .. +8; bf16 16 bytes, or int8 8 bytes
+// in .x/.y) and the 8 values of v they meet.
+struct FusedRowLoads {
+  u32x4 b16[8];
+  u32x2 b8[8];
+  f32x4_t v[2];
+};
+
+__device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t *lds) {
+  constexpr int XL = kFusedRows * 8 / 256;   // x pieces per thread per round (4)
+  constexpr int WL = kFusedCols * 8 / 256;   // W pieces per thread per round (2)
+  constexpr int RPW = kFusedRows / 4;        // epilogue rows per wave (32)
+  const int t = threadIdx.x, lane = t & 63, w = wave_id();
+  const FusedModule m = fused_module_of(f, blk);
+  const int local = blk - m.block_base;
+  const int rt = local / m.n_tiles, tile = local - rt * m.n_tiles;
+  const int row0 = rt * kFusedRows, n0 = tile * kFusedCols;
+
+  // Table entries of this wave's epilogue rows w + 4i, one per lane (i < 32).
+  lora_adapter_entry_t my_e{};
+  bool my_valid = false;
+  if (lane < RPW) {
+    const int b = row0 + w + 4 * lane;
+    const int a = b < f.num_rows ? f.ids[b] : -1;
+    my_valid = (unsigned)a < (unsigned)f.num_slots;
+    if (my_valid) my_e = f.table[(int64_t)a * f.table_cols + m.col];
+  }
+
+  const int piece = t & 7;
+  const rsrc_t rx = make_rsrc(m.x, (uint32_t)((int64_t)f.num_rows * m.ldx * 2));
+  uint32_t xoff[XL];
+#pragma unroll
+  for (int i = 0; i < XL; ++i) {
+    const int r = row0 + i * 32 + (t >> 3);
+    xoff[i] = r < f.num_rows ? (uint32_t)((int64_t)r * m.ldx * 2) : kOutOfRange;
+  }
+  const rsrc_t rw = make_rsrc(m.W, (uint32_t)((int64_t)m.d_out * m.ldw * 2));
+  uint32_t woff[WL];
+#pragma unroll
+  for (int i = 0; i < WL; ++i) {
+    const int n = n0 + i * 32 + (t >> 3);
+    woff[i] = n < m.d_out ? (uint32_t)((int64_t)n * m.ldw * 2) : kOutOfRange;
+  }
+  struct Stage {
+    u32x4 x[XL], wv[WL];
+  };
+  auto load = [&](Stage &st, int k0) {  // one round; past d_in: zero, no traffic
+    const int k = k0 + piece * 8;
+    const bool kon = k < m.d_in;
+    const uint32_t kb = (uint32_t)k * 2;
+#pragma unroll
+    for (int i = 0; i < XL; ++i) st.x[i] = buf_ld16(rx, kon && xoff[i] != kOutOfRange ? xoff[i] + kb : kOutOfRange, 0);
+#pragma unroll
+    for (int i = 0; i < WL; ++i)
+      st.wv[i] = buf_ld16_stream(rw, kon && woff[i] != kOutOfRange ? woff[i] + kb : kOutOfRange, 0);
+  };
+  auto store = [&](const Stage &st, uint8_t *buf) {
+#pragma unroll
+    for (int i = 0; i < XL; ++i) *(u32x4 *)(buf + shrink_lds_off(i * 32 + (t >> 3), piece)) = st.x[i];
+#pragma unroll
+    for (int i = 0; i < WL; ++i) *(u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(i * 32 + (t >> 3), piece)) = st.wv[i];
+  };
+  f32x4_t acc[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int r_in = lane & 15, g = lane >> 4;
+  auto compute = [&](const uint8_t *buf) {
+#pragma unroll
+    for (int ks = 0; ks < kShrinkRound / 32; ++ks) {
+      u32x4 xo[2], wo[4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) xo[mt] = *(const u32x4 *)(buf + shrink_lds_off(w * 32 + mt * 16 + r_in, ks * 4 + g));
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        wo[nt] = *(const u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(nt * 16 + r_in, ks * 4 + g));
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xo[mt]),
+                                                                __builtin_bit_cast(bf16x8_t, wo[nt]), acc[mt][nt], 0,
+                                                                0, 0);
+    }
+  };
+  // Two rounds in flight; round i goes to buffer i & 1 (see the SGMV shrink).
+  Stage s0, s1;
+  load(s0, 0);
+  load(s1, kShrinkRound);
+  const int rounds = (m.d_in + kShrinkRound - 1) / kShrinkRound;
+  for (int r = 0; r < rounds; r += 2) {
+    uint8_t *b0 = lds, *b1 = lds + kShrinkBufBytes;
+    store(s0, b0);
+    load(s0, (r + 2) * kShrinkRound);
+    __syncthreads();
+    compute(b0);
+    store(s1, b1);
+    load(s1, (r + 3) * kShrinkRound);
+    __syncthreads();
+    compute(b1);
+  }
+  __syncthreads();  // every wave is done with the round buffers
+
+  // Base tile to LDS: C[4*(l/16) + i][l%16] of tile (mt, nt) is row
+  // 32w + 16mt + 4*(l/16) + i, column 16nt + l%16.
+  float *base = reinterpret_cast<float *>(lds);
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        base[(w * 32 + mt * 16 + g * 4 + i) * kFusedBaseStride + nt * 16 + r_in] = acc[mt][nt][i];
+  __syncthreads();
+
+  // Epilogue: row rr = w + 4i of the tile in round i.
+  const int bl = lane >> 3, pc = lane & 7, j0 = pc * 8;
+  const int c = 8 * pc + bl;  // this lane's output column after the reduce-scatter
+  const rsrc_t ry = make_rsrc(m.y, (uint32_t)((int64_t)f.num_rows * m.ldy * 2));
+  const rsrc_t rv = make_rsrc(m.v, (uint32_t)((int64_t)f.num_rows * f.rs * 4));
+  struct RowInfo {
+    int b, rank, fmt;
+    bool ok;
+    float scale;
+    const uint8_t *B;
+  };
+  auto row_info = [&](int i) {  // uniform: the entry held by lane i
+    RowInfo ri;
+    ri.b = row0 + w + 4 * i;
+    const bool valid = __builtin_amdgcn_readlane((int)my_valid, i) != 0;
+    lora_adapter_entry_t e;
+    e.A = (const void *)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                                         (int)(uint32_t)(uintptr_t)my_e.A, i)) |
+                                    ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                                         (int)(uint32_t)((uintptr_t)my_e.A >> 32), i)
+                                     << 32));
+    e.B = (const void *)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                                         (int)(uint32_t)(uintptr_t)my_e.B, i)) |
+                                    ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                                         (int)(uint32_t)((uintptr_t)my_e.B >> 32), i)
+                                     << 32));
+    e.rank = __builtin_amdgcn_readlane(my_e.rank, i);
+    e.scale = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_e.scale), i));
+    e.format = __builtin_amdgcn_readlane(my_e.format, i);
+    ri.ok = valid && ri.b < f.num_rows && entry_ok(e, f.max_rank);
+    if (valid && ri.b < f.num_rows && e.rank != 0 && !ri.ok && tile == 0 && lane == 0)
+      atomicAdd(f.status, 1);  // a malformed entry, counted by the first column tile
+    ri.rank = e.rank;
+    ri.fmt = e.format;
+    ri.scale = e.scale;
+    ri.B = static_cast<const uint8_t *>(e.B);
+    return ri;
+  };
+  auto issue = [&](const RowInfo &ri, FusedRowLoads &L) {
+    const bool on = ri.ok && j0 < ri.rank;
+    const bool q8 = ri.fmt == LORA_FORMAT_INT8_ROWS;
+    const uint32_t row_bytes = q8 ? (uint32_t)ldb8_of(ri.rank) : (uint32_t)((ri.rank + 7) & ~7) * 2;
+    const uint8_t *vals = ri.B + (q8 ? q8_values_offset(m.d_out) : 0);
+    const rsrc_t rb = make_rsrc(ri.ok ? vals : nullptr, ri.ok ? (uint32_t)m.d_out * row_bytes : 0u);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int n = n0 + 8 * q + bl;
+      const bool lon = on && n < m.d_out;
+      const uint32_t off = (uint32_t)n * row_bytes + (uint32_t)j0 * (q8 ? 1 : 2);
+      L.b16[q] = buf_ld16_stream(rb, lon && !q8 ? off : kOutOfRange, 0);
+      L.b8[q] = __builtin_amdgcn_raw_buffer_load_b64(rb, lon && q8 ? off : kOutOfRange, 0, kNonTemporal);
+    }
+    const uint32_t voff = on ? (uint32_t)(((int64_t)ri.b * f.rs + j0) * 4) : kOutOfRange;
+    L.v[0] = __builtin_bit_cast(f32x4_t, buf_ld16(rv, voff, 0));
+    L.v[1] = __builtin_bit_cast(f32x4_t, buf_ld16(rv, voff == kOutOfRange ? kOutOfRange : voff + 16, 0));
+  };
+  auto finish = [&](const RowInfo &ri, const FusedRowLoads &L, int rr) {
+    if (ri.b >= f.num_rows) return;
+    float dl = 0.f;
+    if (ri.ok) {
+      float vv[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        vv[k] = L.v[0][k];
+        vv[4 + k] = L.v[1][k];
+      }
+      float acc8[8];
+      if (ri.fmt == LORA_FORMAT_INT8_ROWS) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc8[q] = dot8_i8_f32(L.b8[q], vv, 0.f);
+      } else {
+        const V8Split vs = split_v8(vv);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc8[q] = dot8_bf16_split(L.b16[q], vs, 0.f);
+      }
+      reduce_scatter<8, 8>(acc8);
+      dl = acc8[0] * ri.scale;
+      if (ri.fmt == LORA_FORMAT_INT8_ROWS && n0 + c < m.d_out)
+        dl *= reinterpret_cast<const float *>(ri.B)[n0 + c];  // the B row's scale
+    }
+    const float yv = base[rr * kFusedBaseStride + c] + dl;
+    buf_st_u16(ry, n0 + c < m.d_out ? (uint32_t)(((int64_t)ri.b * m.ldy + n0 + c) * 2) : kOutOfRange,
+               f32_to_bf16(yv));
+  };
+  FusedRowLoads cur, nxt;
+  RowInfo ci = row_info(0);
+  issue(ci, cur);
+  for (int i = 0; i + 1 < RPW; ++i) {  // row i+1 is requested before row i is finished
+    const RowInfo ni = row_info(i + 1);
+    issue(ni, nxt);
+    finish(ci, cur, w + 4 * i);
+    cur = nxt;
+    ci = ni;
+  }
+  finish(ci, cur, w + 4 * (RPW - 1));
+}
+
+}  // namespace lora

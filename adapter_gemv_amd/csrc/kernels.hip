@@ -4,6 +4,7 @@
 // rank class of the launch (smallest of 8, 16, 32, 64 holding max_rank) fixes
 // the register tiling of both paths.
 #include "decode_items.h"
+#include "fused_items.h"
 #include "sgmv_items.h"
 
 namespace lora {
@@ -50,8 +51,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CLS <= 1 ? 
   else sgmv_expand_block<KT, VU>(d, blockIdx.x - decode_blocks, lds);
 }
 
-// lora_shrink: sum the k-chunk partials of each row in a segment into
-// v[b][0..max_rank) (zero past the entry's rank).
+// Sum the k-chunk partials of each row in a segment into v[b][0..max_rank)
+// (zero past the entry's rank), for module blockIdx.y into the plane
+// v_out + blockIdx.y * num_rows * ldv (lora_shrink: one module, the caller's
+// v; the fused layer: every module, planes in the workspace).
 __global__ __launch_bounds__(256) void shrink_reduce_kernel(LayerDesc d) {
   const int nseg = min(*d.num_segments, min(d.num_rows, d.num_slots));
   if (nseg <= 0) return;
@@ -66,7 +69,8 @@ __global__ __launch_bounds__(256) void shrink_reduce_kernel(LayerDesc d) {
     if (d.seg_offsets[mid] <= p) lo = mid;
     else hi = mid - 1;
   }
-  const ModuleDesc &m = d.mod[0];
+  const ModuleDesc m = kernel_desc().mod[blockIdx.y];
+  float *v_out = d.v_out + (int64_t)blockIdx.y * d.num_rows * d.ldv;
   const int a = d.seg_adapter[lo];
   if ((unsigned)a >= (unsigned)d.num_slots) return;
   const lora_adapter_entry_t e = d.table[(int64_t)a * d.table_cols + m.col];  // varies per lane
@@ -75,7 +79,13 @@ __global__ __launch_bounds__(256) void shrink_reduce_kernel(LayerDesc d) {
   if (ok && j < e.rank)
     for (int c = 0; c < m.n_chunks; ++c) sum += d.part[((int64_t)(m.part_base + c) * d.num_rows + p) * d.rs + j];
   const int b = d.perm[p];
-  if ((unsigned)b < (unsigned)d.num_rows) d.v_out[(int64_t)b * d.ldv + j] = sum;
+  if ((unsigned)b < (unsigned)d.num_rows) v_out[(int64_t)b * d.ldv + j] = sum;
+}
+
+// Base projection + delta (fused_items.h).
+__global__ __launch_bounds__(256) void lora_fused_kernel(FusedDesc f) {
+  __shared__ __align__(16) uint8_t lds[kShrinkLdsBytes];
+  fused_block(f, blockIdx.x, lds);
 }
 
 int rank_class(int max_rank) { return max_rank <= 8 ? 0 : max_rank <= 16 ? 1 : max_rank <= 32 ? 2 : 3; }
@@ -114,7 +124,13 @@ hipError_t launch_expand(const LayerDesc &d, int decode_blocks, int grid, hipStr
 hipError_t launch_shrink_reduce(const LayerDesc &d, hipStream_t stream) {
   const int64_t total = (int64_t)d.num_rows * d.max_rank;
   if (total <= 0) return hipSuccess;
-  shrink_reduce_kernel<<<(int)((total + 255) / 256), 256, 0, stream>>>(d);
+  shrink_reduce_kernel<<<dim3((unsigned)((total + 255) / 256), (unsigned)d.n_active), 256, 0, stream>>>(d);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused(const FusedDesc &f, int blocks, hipStream_t stream) {
+  if (blocks <= 0) return hipSuccess;
+  lora_fused_kernel<<<blocks, 256, 0, stream>>>(f);
   return hipGetLastError();
 }
 

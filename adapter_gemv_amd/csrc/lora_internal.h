@@ -85,6 +85,41 @@ struct LayerDesc {
   float *v_out;
 };
 
+// Fused base projection + delta: a block computes y for kFusedRows rows and
+// kFusedCols output columns of one projection.
+constexpr int kFusedRows = 128;
+constexpr int kFusedCols = 64;
+
+struct FusedModule {
+  const uint16_t *x;  // [num_rows][ldx]
+  int64_t ldx;
+  const uint16_t *W;  // [d_out][ldw], bf16 base weight
+  int64_t ldw;
+  uint16_t *y;        // [num_rows][ldy], written
+  int64_t ldy;
+  const float *v;     // [num_rows][rs]: the row's unscaled rank-r vector
+  int32_t d_in;
+  int32_t d_out;
+  int32_t col;         // table column
+  int32_t block_base;  // first block of this module
+  int32_t n_tiles;     // column tiles of kFusedCols
+};
+
+struct FusedDesc {
+  FusedModule mod[kMaxModules];
+  int32_t n_active;
+  int32_t num_rows;
+  int32_t num_slots;
+  int32_t table_cols;
+  int32_t max_rank;
+  int32_t rs;          // floats per row of v
+  const int32_t *ids;  // the rows' adapter slots, original order
+  int32_t *status;
+  const lora_adapter_entry_t *table;
+};
+
+hipError_t launch_fused(const FusedDesc &f, int blocks, hipStream_t stream);
+
 inline int round_up(int a, int b) { return (a + b - 1) / b * b; }
 inline int partial_row_stride(int max_rank) { return round_up(max_rank, 8); }
 

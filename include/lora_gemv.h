@@ -289,6 +289,61 @@ lora_status_t lora_layer_expand(const lora_module_io_t *io, uint32_t module_mask
                                 int32_t max_rank, void *ws, size_t ws_bytes,
                                 void *stream);
 
+/* One projection of a layer for lora_linear_layer: input, base weight and
+ * output (which the call writes). */
+typedef struct lora_linear_io {
+  const void *x; /* device, bf16 [num_rows][ldx]                             */
+  int64_t ldx;
+  const void *W; /* device, bf16 [d_out][ldw]: the base weight, row n holds  */
+  int64_t ldw;   /* the d_in weights of output n (a linear layer's weight)   */
+  void *y;       /* device, bf16 [num_rows][ldy]: written, W.x + delta       */
+  int64_t ldy;
+  int32_t d_in;
+  int32_t d_out;
+} lora_linear_io_t;
+
+/*
+ * lora_linear_workspace_bytes -- workspace of lora_linear_layer for n_modules
+ * projections whose d_in sum to sum_d_in (also enough for
+ * lora_build_segments with the same rows and slots).  0 for bad arguments.
+ */
+size_t lora_linear_workspace_bytes(int32_t num_rows, int32_t num_slots,
+                                   int32_t max_rank, int64_t sum_d_in,
+                                   int32_t n_modules);
+
+/*
+ * lora_linear_layer -- base projection and adapter delta together:
+ *     y[b] = bf16_rne( W . x[b] + scale_a * B_a . (A_a . x[b]) )
+ * for every projection whose bit is set in module_mask, a = row_adapter[b]
+ * (rows whose id is negative or >= num_slots get the base term only).
+ * Source: "m07 -- Multi-Adapter (LoRA) Serving", "6. Deep Dive A" (y = Wx +
+ * (B.A)x(alpha/r): the base term shared by the batch, the adapter term per
+ * row) and the fused base + delta on the pages' list of next steps (the
+ * delta in the base product's epilogue with a wide accumulator, so y is
+ * written once, never read).  Three launches on `stream`: the grouped shrink
+ * of lora_layer_shrink (each distinct adapter's A read once), a sum of its
+ * partials into one v per row and projection, and one fused kernel that
+ * streams W once (bf16 matrix cores, fp32 accumulate) and adds each row's
+ * delta before the single bf16 rounding.
+ *
+ *   io           array of LORA_NUM_MODULES entries, read where module_mask
+ *                has a bit: x, W, y 16-byte aligned; d_in, d_out, ldx, ldw,
+ *                ldy multiples of 8; W below 4 GiB
+ *   row_adapter  device int32 [num_rows]: the ids the segments were built
+ *                from (lora_build_segments on the same stream before)
+ *   seg          those segments; *seg.status counts as for lora_apply_layer
+ *   ws, ws_bytes at least lora_linear_workspace_bytes(...)
+ *   other arguments as for lora_apply_layer.  Factors in either format.
+ *
+ * Errors: those of lora_apply_layer; LORA_ERR_NULL for a null W or
+ * row_adapter, LORA_ERR_SHAPE for ldw < d_in or a W of 4 GiB or more.
+ */
+lora_status_t lora_linear_layer(const lora_linear_io_t *io, uint32_t module_mask,
+                                int32_t num_rows, const int32_t *row_adapter,
+                                const lora_adapter_entry_t *table, int32_t num_slots,
+                                lora_segments_t seg, int32_t max_rank, void *ws,
+                                size_t ws_bytes, void *stream);
+
 /* Most adapters one row may carry in lora_apply_layer_stacked. */
 #define LORA_MAX_STACK 8
 
