@@ -85,8 +85,10 @@ def lib() -> ctypes.CDLL:
                                                vp]
         L.lora_linear_workspace_bytes.restype = sz
         L.lora_linear_workspace_bytes.argtypes = [i32, i32, i32, i64, i32]
-        L.lora_linear_layer.restype = st
-        L.lora_linear_layer.argtypes = [ctypes.POINTER(_LinIO), u32, i32, vp, vp, i32, _Seg, i32, vp, sz, vp]
+        for name in ("lora_linear_layer", "lora_linear_shrink", "lora_linear_expand"):
+            f = getattr(L, name)
+            f.restype = st
+            f.argtypes = [ctypes.POINTER(_LinIO), u32, i32, vp, vp, i32, _Seg, i32, vp, sz, vp]
         L.lora_form_batch.restype = st
         L.lora_form_batch.argtypes = [vp, i32, vp, ctypes.c_float, i32, i32, i32, i32, vp, vp]
         _lib = L
@@ -179,7 +181,8 @@ def linear_workspace_bytes(num_rows: int, num_slots: int, max_rank: int, sum_d_i
     return int(lib().lora_linear_workspace_bytes(num_rows, num_slots, max_rank, sum_d_in, n_modules))
 
 
-def linear_layer(ios, num_rows, row_adapter, table, num_slots, seg, max_rank, ws, stream=None, module_mask=None):
+def linear_layer(ios, num_rows, row_adapter, table, num_slots, seg, max_rank, ws, stream=None, module_mask=None,
+                 _fn="lora_linear_layer"):
     """Base projection + delta of every projection in ``ios`` ({name:
     LinearIO}); see lora_linear_layer."""
     import torch
@@ -197,9 +200,19 @@ def linear_layer(ios, num_rows, row_adapter, table, num_slots, seg, max_rank, ws
         arr[i] = _LinIO(io.x.data_ptr(), io.x.stride(0), io.W.data_ptr(), io.W.stride(0), io.y.data_ptr(),
                         io.y.stride(0), io.d_in, io.d_out)
         mask |= 1 << i
-    _check(lib().lora_linear_layer(arr, mask if module_mask is None else module_mask, num_rows, _ptr(row_adapter),
-                                   _ptr(table), num_slots, seg.c(), max_rank, _ptr(ws),
-                                   ws.numel() * ws.element_size(), _stream(stream)), "lora_linear_layer")
+    _check(getattr(lib(), _fn)(arr, mask if module_mask is None else module_mask, num_rows, _ptr(row_adapter),
+                               _ptr(table), num_slots, seg.c(), max_rank, _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(stream)), _fn)
+
+
+def linear_shrink(*args, **kw):
+    """The shrink part of linear_layer (v per row and projection into ws)."""
+    linear_layer(*args, _fn="lora_linear_shrink", **kw)
+
+
+def linear_expand(*args, **kw):
+    """The fused part of linear_layer (W.x + delta into y), after linear_shrink."""
+    linear_layer(*args, _fn="lora_linear_expand", **kw)
 
 
 def pack_table(A_ptrs, B_ptrs, ranks, scales, formats=None) -> np.ndarray:

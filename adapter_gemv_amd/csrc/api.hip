@@ -314,11 +314,51 @@ lora_status_t lora_apply_layer(const lora_module_io_t *io, uint32_t module_mask,
   return layer_phase(true, true, io, module_mask, num_rows, table, num_slots, seg, max_rank, ws, ws_bytes, stream);
 }
 
-// Base projection + delta: the grouped shrink, the partials summed into one v
-// plane per projection (original row order), then the fused kernel.
-lora_status_t lora_linear_layer(const lora_linear_io_t *io, uint32_t module_mask, int32_t num_rows,
-                                const int32_t *row_adapter, const lora_adapter_entry_t *table, int32_t num_slots,
-                                lora_segments_t seg, int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
+// One pass per position of the rows' adapter lists: the segments of that
+// column, then the layer's shrink and expand, each pass adding its delta to y
+// in stream order (a row is in one segment per pass, so no two blocks of a
+// launch touch the same y).
+lora_status_t lora_apply_layer_stacked(const lora_module_io_t *io, uint32_t module_mask, int32_t num_rows,
+                                       const int32_t *row_adapters, int32_t depth, const int32_t *pass_max_rank,
+                                       const lora_adapter_entry_t *table, int32_t num_slots, lora_segments_t seg,
+                                       int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
+  ModuleArgs ms[LORA_NUM_MODULES];
+  int n = 0;
+  lora_status_t st = check_layer(io, module_mask, num_rows, table, num_slots, seg, max_rank, ws, ws_bytes, ms, &n);
+  if (st != LORA_OK) return st;
+  if (depth < 1 || depth > LORA_MAX_STACK) return LORA_ERR_SHAPE;
+  if (num_rows > 0 && !row_adapters) return LORA_ERR_NULL;
+  if (pass_max_rank)
+    for (int t = 0; t < depth; ++t)
+      if (pass_max_rank[t] < 1 || pass_max_rank[t] > max_rank) return LORA_ERR_RANK;
+  const size_t need = segments_ws_bytes(num_rows, num_slots);
+  if (need > 0 && !ws) return LORA_ERR_NULL;
+  if (need > 0 && !aligned16(ws)) return LORA_ERR_ALIGN;
+  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int t = 0; t < depth; ++t) {
+    st = launched(launch_build_segments(row_adapters + t, depth, num_rows, num_slots, t > 0, seg, ws, s));
+    if (st != LORA_OK || num_rows == 0) return st;  // no rows: the first pass only resets the segments
+    const int r = pass_max_rank ? pass_max_rank[t] : max_rank;  // the pass's launch class
+    st = launch_phase(true, ms, n, num_rows, num_slots, r, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
+    if (st != LORA_OK) return st;
+    st = launch_phase(false, ms, n, num_rows, num_slots, r, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
+    if (st != LORA_OK) return st;
+  }
+  return LORA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Base projection + delta: the grouped shrink and the partials summed into one
+// v plane per projection (original row order) (do_shrink), then the fused
+// kernel (do_fused).
+lora_status_t linear_phase(bool do_shrink, bool do_fused, const lora_linear_io_t *io, uint32_t module_mask,
+                           int32_t num_rows, const int32_t *row_adapter, const lora_adapter_entry_t *table,
+                           int32_t num_slots, lora_segments_t seg, int32_t max_rank, void *ws, size_t ws_bytes,
+                           void *stream) {
   if (!io || !table) return LORA_ERR_NULL;
   lora_status_t st = check_segments(seg);
   if (st != LORA_OK) return st;
@@ -350,18 +390,21 @@ lora_status_t lora_linear_layer(const lora_linear_io_t *io, uint32_t module_mask
   if ((int64_t)num_rows * rs * 4 > (int64_t)0xFFFFFF00) return LORA_ERR_SHAPE;
   if (num_rows == 0) return LORA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // 1. v partials of every projection (segment-grouped: each adapter's A once)
-  st = launch_phase(true, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
-  if (st != LORA_OK) return st;
-  // 2. one v plane per projection, rows in their original order
   float *vplanes = reinterpret_cast<float *>(static_cast<char *>(ws) +
                                              ((partials_ws_bytes(num_rows, max_rank, sum_d_in) + 255) & ~(size_t)255));
-  LayerDesc d;
-  fill_desc(d, ms, n, true, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws);
-  d.v_out = vplanes;
-  d.ldv = rs;
-  st = launched(launch_shrink_reduce(d, s));
-  if (st != LORA_OK) return st;
+  if (do_shrink) {
+    // 1. v partials of every projection (segment-grouped: each adapter's A once)
+    st = launch_phase(true, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
+    if (st != LORA_OK) return st;
+    // 2. one v plane per projection, rows in their original order
+    LayerDesc d;
+    fill_desc(d, ms, n, true, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws);
+    d.v_out = vplanes;
+    d.ldv = rs;
+    st = launched(launch_shrink_reduce(d, s));
+    if (st != LORA_OK) return st;
+  }
+  if (!do_fused) return LORA_OK;
   // 3. base projection + delta
   FusedDesc f{};
   const int row_tiles = (num_rows + kFusedRows - 1) / kFusedRows;
@@ -396,38 +439,29 @@ lora_status_t lora_linear_layer(const lora_linear_io_t *io, uint32_t module_mask
   return launched(launch_fused(f, (int)blocks, s));
 }
 
-// One pass per position of the rows' adapter lists: the segments of that
-// column, then the layer's shrink and expand, each pass adding its delta to y
-// in stream order (a row is in one segment per pass, so no two blocks of a
-// launch touch the same y).
-lora_status_t lora_apply_layer_stacked(const lora_module_io_t *io, uint32_t module_mask, int32_t num_rows,
-                                       const int32_t *row_adapters, int32_t depth, const int32_t *pass_max_rank,
-                                       const lora_adapter_entry_t *table, int32_t num_slots, lora_segments_t seg,
-                                       int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
-  ModuleArgs ms[LORA_NUM_MODULES];
-  int n = 0;
-  lora_status_t st = check_layer(io, module_mask, num_rows, table, num_slots, seg, max_rank, ws, ws_bytes, ms, &n);
-  if (st != LORA_OK) return st;
-  if (depth < 1 || depth > LORA_MAX_STACK) return LORA_ERR_SHAPE;
-  if (num_rows > 0 && !row_adapters) return LORA_ERR_NULL;
-  if (pass_max_rank)
-    for (int t = 0; t < depth; ++t)
-      if (pass_max_rank[t] < 1 || pass_max_rank[t] > max_rank) return LORA_ERR_RANK;
-  const size_t need = segments_ws_bytes(num_rows, num_slots);
-  if (need > 0 && !ws) return LORA_ERR_NULL;
-  if (need > 0 && !aligned16(ws)) return LORA_ERR_ALIGN;
-  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  for (int t = 0; t < depth; ++t) {
-    st = launched(launch_build_segments(row_adapters + t, depth, num_rows, num_slots, t > 0, seg, ws, s));
-    if (st != LORA_OK || num_rows == 0) return st;  // no rows: the first pass only resets the segments
-    const int r = pass_max_rank ? pass_max_rank[t] : max_rank;  // the pass's launch class
-    st = launch_phase(true, ms, n, num_rows, num_slots, r, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
-    if (st != LORA_OK) return st;
-    st = launch_phase(false, ms, n, num_rows, num_slots, r, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
-    if (st != LORA_OK) return st;
-  }
-  return LORA_OK;
+}  // namespace
+
+extern "C" {
+
+lora_status_t lora_linear_layer(const lora_linear_io_t *io, uint32_t module_mask, int32_t num_rows,
+                                const int32_t *row_adapter, const lora_adapter_entry_t *table, int32_t num_slots,
+                                lora_segments_t seg, int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
+  return linear_phase(true, true, io, module_mask, num_rows, row_adapter, table, num_slots, seg, max_rank, ws,
+                      ws_bytes, stream);
+}
+
+lora_status_t lora_linear_shrink(const lora_linear_io_t *io, uint32_t module_mask, int32_t num_rows,
+                                 const int32_t *row_adapter, const lora_adapter_entry_t *table, int32_t num_slots,
+                                 lora_segments_t seg, int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
+  return linear_phase(true, false, io, module_mask, num_rows, row_adapter, table, num_slots, seg, max_rank, ws,
+                      ws_bytes, stream);
+}
+
+lora_status_t lora_linear_expand(const lora_linear_io_t *io, uint32_t module_mask, int32_t num_rows,
+                                 const int32_t *row_adapter, const lora_adapter_entry_t *table, int32_t num_slots,
+                                 lora_segments_t seg, int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
+  return linear_phase(false, true, io, module_mask, num_rows, row_adapter, table, num_slots, seg, max_rank, ws,
+                      ws_bytes, stream);
 }
 
 }  // extern "C"

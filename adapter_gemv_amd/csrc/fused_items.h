@@ -11,8 +11,13 @@
 // output columns of one projection, over the whole d_in:
 //   * main loop: x and W stream through LDS in rounds of 64 k, two rounds in
 //     flight in registers, as in the SGMV shrink (x rows from L2, W rows from
-//     HBM once, nontemporal); wave w turns rows [32w, 32w+32) x the 64
-//     columns into 2 x 4 bf16 matrix-core tiles (16x16x32, fp32 accumulate);
+//     HBM once, nontemporal, 128-byte line pieces); wave w turns rows
+//     [32w, 32w+32) x the 64 columns into 2 x 4 bf16 matrix-core tiles
+//     (16x16x32, fp32 accumulate).  Loading W straight into the matrix-core
+//     operand layout (16 rows x 64 bytes per instruction) with each wave
+//     owning 16 or 32 columns measured slower, and so did one register set
+//     for both B formats in the epilogue (a branch per row around the loads
+//     makes the compiler wait for all of them);
 //   * epilogue: the base tile goes to LDS, then each wave streams the B slice
 //     (the block's 64 rows of B_a, rank values each) of one of its rows per
 //     round, one round ahead, with the row's v (from the grouped shrink);
@@ -43,6 +48,7 @@ __device__ __forceinline__ FusedModule fused_module_of(const FusedDesc &f, int b
 
 constexpr int kFusedBaseStride = kFusedCols + 1;  // floats per row of the base tile in LDS (odd: no bank clash)
 static_assert(kFusedRows * kFusedBaseStride * 4 <= 2 * kShrinkBufBytes, "base tile fits the round buffers");
+constexpr int kFusedLdsBytes = kShrinkLdsBytes;  // two round buffers of x and W, later the base tile
 
 // One epilogue row: per lane 8 pieces of the B slice (q = 0..7: B row
 // n0 + 8q + lane/8, values 8*(lane%8) .. +8; bf16 16 bytes, or int8 8 bytes
@@ -221,11 +227,11 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
     if (ri.b >= f.num_rows) return;
     float dl = 0.f;
     if (ri.ok) {
-      float vv[8];
+      float vv[8];  // v past the rank is not part of the row's vector: zero
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        vv[k] = L.v[0][k];
-        vv[4 + k] = L.v[1][k];
+        vv[k] = j0 + k < ri.rank ? L.v[0][k] : 0.f;
+        vv[4 + k] = j0 + 4 + k < ri.rank ? L.v[1][k] : 0.f;
       }
       float acc8[8];
       if (ri.fmt == LORA_FORMAT_INT8_ROWS) {

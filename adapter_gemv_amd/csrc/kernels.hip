@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void shrink_reduce_kernel(LayerDesc d) {
 
 // Base projection + delta (fused_items.h).
 __global__ __launch_bounds__(256) void lora_fused_kernel(FusedDesc f) {
-  __shared__ __align__(16) uint8_t lds[kShrinkLdsBytes];
+  __shared__ __align__(16) uint8_t lds[kFusedLdsBytes];
   fused_block(f, blockIdx.x, lds);
 }
 

@@ -36,6 +36,8 @@ DESCRIPTIONS = {
                    "by the adapter-aware batch former (cap 32 adapters, 4 tail slots, at least 128 rows)",
     "stacked_layer": "70B full layer decode, two adapters per row: one of 4 shared domain adapters (rank 64) and a "
                      "style adapter of its own (rank 16), all 7 projections, 128 rows; one pass per adapter",
+    "fused_layer_r64": "70B full layer decode, base projection + delta fused: bf16 W of all 7 projections (1.63 GB) "
+                       "and 128 distinct rank-64 adapters, 128 rows; y written once",
 }
 
 
@@ -80,11 +82,16 @@ def cpu_baseline(w, min_seconds=10.0, max_passes=64):
     rows = None
     if w.seq_lens is not None:  # prefill: a bounded sample of rows
         rows = np.arange(0, w.num_rows, max(1, w.num_rows // 256), dtype=np.int32)
+    if w.W is not None:  # base projection in fp64 on one core: a sample of 8 rows
+        rows = np.arange(0, w.num_rows, max(1, w.num_rows // 8), dtype=np.int32)
     n_rows = w.num_rows if rows is None else rows.size
     t0 = time.perf_counter()
     passes = 0
     while True:
-        if w.stack is None:
+        if w.W is not None:
+            oracle.build_segments(w.ids, w.num_slots)
+            oracle.linear_layer(w, rows=rows)
+        elif w.stack is None:
             oracle.build_segments(w.ids, w.num_slots)
             oracle.lora_layer(w, rows=rows)
         else:
@@ -99,6 +106,42 @@ def cpu_baseline(w, min_seconds=10.0, max_passes=64):
             "sample": f"{passes} pass(es) of {n_rows} rows through every projection of the workload "
                       f"(segments + fp64 shrink/expand), single-threaded C pinned to one core, {el:.1f} s; "
                       f"host {platform.processor() or platform.machine()}, {os.cpu_count()} logical CPUs"}
+
+
+def fused_comparison(w, d, lg, stream, steps, traffic):
+    """The same work unfused, timed like the step: the base product by torch's
+    bf16 GEMM into y, then segments and the delta (y read and written); and the
+    base product alone."""
+    import torch
+    xs = {m.name: d.x[m.x_name][:w.num_rows] for m in w.modules}
+
+    def base():
+        for m in w.modules:
+            torch.mm(xs[m.name], d.W[m.name].t(), out=d.y[m.name])
+
+    def unfused():
+        base()
+        d.build_segments(stream)
+        lg.apply_layer(d.ios, w.num_rows, d.table, w.num_slots, d.seg, w.max_rank, d.ws, stream)
+
+    def timed(fn):
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(steps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    base_ms, unfused_ms = timed(base), timed(unfused)
+    return {"base_weight_bytes": traffic["base_weights"],
+            "unfused_ms_per_step": round(unfused_ms, 5), "base_gemm_ms_per_step": round(base_ms, 5),
+            "base_gemm_gbps": round(traffic["base_weights"] / (base_ms * 1e-3) / 1e9, 1),
+            "unfused": "torch.mm (bf16 GEMM library) into y, then lora_build_segments + lora_apply_layer"}
 
 
 def rank_class(max_rank):
@@ -210,8 +253,10 @@ def summarize_profile(a):
         if k not in write or not k.startswith(("lora_", "seg_", "shrink_")):
             continue
         b = (fetch[k] * f_scale + write[k] * w_scale) * 1024.0
-        phase = "shrink" if "shrink" in k else "expand" if "expand" in k else None
-        alg_b = alg.get(phase) if phase else None
+        phase = ("shrink" if k.startswith("lora_shrink") else
+                 "expand" if k.startswith(("lora_expand", "lora_fused")) else None)
+        per_kernel = bench.get("kernels_algorithmic_bytes_per_launch", {})
+        alg_b = per_kernel.get(k, alg.get(phase) if phase else None)
         ratio = f"{b / alg_b:.3f}" if alg_b else "-"
         lines.append(f"| `{k}` | {n_fetch[k]} | {fetch[k]:.1f} | {write[k]:.1f} | {b:.4g} | "
                      f"{alg_b if alg_b else '-'} | {ratio} |")
@@ -304,7 +349,16 @@ def main():
         w, former = formed_workload(gen)
     else:
         w = gen.make_workload(args.workload)
-    if w.stack is None:
+    if w.W is not None:  # fused: + the base weights, y written once (not read)
+        traffic = algorithmic(w)
+        w_bytes = sum(2 * m.d_in * m.d_out for m in w.modules)
+        y_write = traffic["y"] // 2
+        b_bytes = traffic["expand_bytes"] - traffic["y"]
+        traffic["total"] = w_bytes + traffic["adapters"] + traffic["x"] + y_write
+        traffic["expand_bytes"] = w_bytes + b_bytes + traffic["x"] + y_write  # the fused kernel
+        traffic["base_weights"] = w_bytes
+        passes = [traffic]
+    elif w.stack is None:
         traffic = algorithmic(w)
         passes = [traffic]
     else:  # one pass per column: each reads its adapters, x and y again
@@ -330,6 +384,10 @@ def main():
 
     def launch(i):
         d = dws[i % reps]
+        if d.W is not None:
+            d.build_segments(stream)
+            lg.linear_layer(d.lin_ios, w.num_rows, d.ids, d.table, w.num_slots, d.seg, w.max_rank, d.ws, stream)
+            return
         if stack is not None:
             lg.apply_layer_stacked(d.ios, w.num_rows, stack, d.table, w.num_slots, d.seg, w.max_rank, d.ws, stream,
                                    pass_max_rank=pass_rank)
@@ -381,11 +439,20 @@ def main():
             seg_us = phase_us(lambda d: d.build_segments(stream))
         else:
             seg_us = phase_us(lambda d: lg.build_segments(col, w.num_slots, d.seg, d.ws, stream))
-        shr_us = phase_us(lambda d: lg.layer_shrink(d.ios, w.num_rows, d.table, w.num_slots, d.seg, r, d.ws, stream))
-        exp_us = phase_us(lambda d: lg.layer_expand(d.ios, w.num_rows, d.table, w.num_slots, d.seg, r, d.ws, stream))
+        if w.W is not None:  # the fused call's two parts: grouped shrink (+ v sums), fused kernel
+            shr_us = phase_us(lambda d: lg.linear_shrink(d.lin_ios, w.num_rows, d.ids, d.table, w.num_slots, d.seg,
+                                                         r, d.ws, stream))
+            exp_us = phase_us(lambda d: lg.linear_expand(d.lin_ios, w.num_rows, d.ids, d.table, w.num_slots, d.seg,
+                                                         r, d.ws, stream))
+        else:
+            shr_us = phase_us(lambda d: lg.layer_shrink(d.ios, w.num_rows, d.table, w.num_slots, d.seg, r, d.ws,
+                                                        stream))
+            exp_us = phase_us(lambda d: lg.layer_expand(d.ios, w.num_rows, d.table, w.num_slots, d.seg, r, d.ws,
+                                                        stream))
         per_pass.append({"segments": seg_us, "shrink": shr_us, "expand": exp_us})
         for ph, us in (("shrink", shr_us), ("expand", exp_us)):
-            k = kernels.setdefault(f"lora_{ph}_kernel<{rank_class(r)}>", [0, 0.0, 0])
+            name = "lora_fused_kernel" if (w.W is not None and ph == "expand") else f"lora_{ph}_kernel<{rank_class(r)}>"
+            k = kernels.setdefault(name, [0, 0.0, 0])
             k[0] += 1
             k[1] += us
             k[2] += passes[t][ph + "_bytes"]
@@ -421,6 +488,7 @@ def main():
                 "achieved_gbps": round(gbps, 1),
                 "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2), "peak_gbps": PEAK_HBM_GBPS},
         "phases_us": {k: round(v[0], 2) for k, v in phases.items()},
+        "kernels_algorithmic_bytes_per_launch": {k: int(round(v[2] / v[0])) for k, v in kernels.items()},
         "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": counted["bytes_per_launch"] if counted else None,
@@ -429,6 +497,8 @@ def main():
     }
     if former is not None:
         out["batch_former"] = former
+    if w.W is not None:
+        out["fused"] = fused_comparison(w, dws[0], lg, stream, args.steps, traffic)
     if stack is not None:
         out["stacked"] = {"depth": len(per_pass), "pass_max_rank": pass_rank,
                           "passes_us": [{k: round(v, 2) for k, v in p.items()} for p in per_pass],

@@ -344,6 +344,24 @@ lora_status_t lora_linear_layer(const lora_linear_io_t *io, uint32_t module_mask
                                 lora_segments_t seg, int32_t max_rank, void *ws,
                                 size_t ws_bytes, void *stream);
 
+/*
+ * The two parts of lora_linear_layer, for callers that interleave other work
+ * or time them apart: lora_linear_shrink leaves one v per row and projection
+ * in the workspace (the grouped shrink and the sum of its partials);
+ * lora_linear_expand, enqueued later on the same stream with the same
+ * arguments and workspace, runs the fused kernel and writes y.
+ */
+lora_status_t lora_linear_shrink(const lora_linear_io_t *io, uint32_t module_mask,
+                                 int32_t num_rows, const int32_t *row_adapter,
+                                 const lora_adapter_entry_t *table, int32_t num_slots,
+                                 lora_segments_t seg, int32_t max_rank, void *ws,
+                                 size_t ws_bytes, void *stream);
+lora_status_t lora_linear_expand(const lora_linear_io_t *io, uint32_t module_mask,
+                                 int32_t num_rows, const int32_t *row_adapter,
+                                 const lora_adapter_entry_t *table, int32_t num_slots,
+                                 lora_segments_t seg, int32_t max_rank, void *ws,
+                                 size_t ws_bytes, void *stream);
+
 /* Most adapters one row may carry in lora_apply_layer_stacked. */
 #define LORA_MAX_STACK 8
 

@@ -15,7 +15,7 @@ if not torch.cuda.is_available():  # pragma: no cover
     pytest.skip("no GPU", allow_module_level=True)
 
 import adapter_gemv_amd as lg  # noqa: E402
-from workloads.device import DeviceWorkload, bf16_tensor  # noqa: E402
+from workloads.device import DeviceWorkload  # noqa: E402
 
 
 @pytest.fixture(autouse=True)
@@ -29,18 +29,18 @@ class FusedRun:
     def __init__(self, w):
         self.w = w
         self.dw = DeviceWorkload(w)
-        self.W = {m.name: bf16_tensor(w.W[m.name]) for m in w.modules}
-        sum_d_in = sum(m.d_in for m in w.modules)
-        nb = lg.linear_workspace_bytes(w.num_rows, w.num_slots, w.max_rank, sum_d_in, len(w.modules))
-        self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
-        self.ios = {m.name: lg.LinearIO(self.dw.x[m.x_name], self.W[m.name], self.dw.y[m.name]) for m in w.modules}
 
-    def run(self):
+    def run(self, phases=False):
         w, dw = self.w, self.dw
         for y in dw.y.values():
             y.fill_(float("nan"))  # every element must be written
-        lg.build_segments(dw.ids, w.num_slots, dw.seg, self.ws)
-        lg.linear_layer(self.ios, w.num_rows, dw.ids, dw.table, w.num_slots, dw.seg, w.max_rank, self.ws)
+        dw.build_segments()
+        args = (dw.lin_ios, w.num_rows, dw.ids, dw.table, w.num_slots, dw.seg, w.max_rank, dw.ws)
+        if phases:
+            lg.linear_shrink(*args)
+            lg.linear_expand(*args)
+        else:
+            lg.linear_layer(*args)
         torch.cuda.synchronize()
         return {m.name: bf16_host(dw.y[m.name]) for m in w.modules}
 
@@ -134,3 +134,27 @@ def test_fused_full_layer_sampled_rows():
     rows = np.random.default_rng(1).choice(w.num_rows, 12, replace=False).astype(np.int32)
     note(f"fused full layer: rows {list(rows)}")
     check_fused(w, rows=rows)
+
+
+def test_phases_equal_the_whole_call():
+    ids = np.random.default_rng(3).integers(-1, 20, size=90)
+    w = gen.add_base_weights(bw(430, 90, 20, 2048, 1040, 32, ids, x_std=1.0))
+    run = FusedRun(w)
+    whole = run.run()["q"]
+    split = run.run(phases=True)["q"]
+    assert np.array_equal(whole, split)
+
+
+@pytest.mark.parametrize("max_rank", [5, 13, 30])
+def test_fused_max_rank_not_a_multiple_of_eight(max_rank):
+    # the v planes hold max_rank values of a rounded-up row: lanes past the rank must read zeros
+    rng = np.random.default_rng(max_rank)
+    rows, slots = 70, 12
+    ids = rng.integers(-1, slots, size=rows)
+    ranks = np.zeros((slots, 7), np.int32)
+    ranks[:, 0] = rng.integers(1, max_rank + 1, size=slots)
+    ranks[0, 0] = max_rank
+    fmt = np.where(rng.random((slots, 7)) < 0.5, gen.FMT_INT8_ROWS, gen.FMT_BF16).astype(np.int32)
+    w = gen.add_base_weights(bw(440 + max_rank, rows, slots, 1024, 528, None, ids, ranks=ranks, x_std=1.0,
+                                max_rank=max_rank, fmt=fmt))
+    check_fused(w)

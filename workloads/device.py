@@ -44,6 +44,15 @@ class DeviceWorkload:
         self.ws_bytes = lg.workspace_bytes(w.num_rows + ws_extra_rows, w.num_slots, w.max_rank, sum_d_in)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
         self.ios = {m.name: lg.ModuleIO(self.x[m.x_name], self.y[m.name]) for m in w.modules}
+        self.W = self.lin_ios = None
+        if w.W is not None:  # base weights: the fused calls, and a workspace for them
+            self.W = {m.name: bf16_tensor(w.W[m.name], device) for m in w.modules}
+            self.lin_ios = {m.name: lg.LinearIO(self.x[m.x_name], self.W[m.name], self.y[m.name]) for m in w.modules}
+            nb = lg.linear_workspace_bytes(w.num_rows + ws_extra_rows, w.num_slots, w.max_rank, sum_d_in,
+                                           len(w.modules))
+            if nb > self.ws_bytes:
+                self.ws_bytes = nb
+                self.ws = torch.empty(nb, dtype=torch.uint8, device=device)
 
     def pack(self, base: int, ranks=None, scales=None) -> np.ndarray:
         w = self.w
