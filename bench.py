@@ -255,8 +255,11 @@ def summarize_profile(a):
         b = (fetch[k] * f_scale + write[k] * w_scale) * 1024.0
         phase = ("shrink" if k.startswith("lora_shrink") else
                  "expand" if k.startswith(("lora_expand", "lora_fused")) else None)
-        per_kernel = bench.get("kernels_algorithmic_bytes_per_launch", {})
-        alg_b = per_kernel.get(k, alg.get(phase) if phase else None)
+        per_kernel = bench.get("kernels_algorithmic_bytes_per_launch")
+        if per_kernel is not None:  # the step's own kernels (a comparison leg's get none)
+            alg_b = per_kernel.get(k)
+        else:
+            alg_b = alg.get(phase) if phase else None
         ratio = f"{b / alg_b:.3f}" if alg_b else "-"
         lines.append(f"| `{k}` | {n_fetch[k]} | {fetch[k]:.1f} | {write[k]:.1f} | {b:.4g} | "
                      f"{alg_b if alg_b else '-'} | {ratio} |")
