@@ -17,7 +17,7 @@ import os
 import numpy as np
 
 __all__ = [
-    "LoraError", "Segments", "ModuleIO", "MODULES", "TABLE_ENTRY_DTYPE", "lib", "workspace_bytes",
+    "LoraError", "Segments", "segment_bound", "ModuleIO", "MODULES", "TABLE_ENTRY_DTYPE", "lib", "workspace_bytes",
     "build_segments", "shrink", "expand", "apply_layer", "layer_shrink", "layer_expand", "pack_table",
     "status_string", "MAX_RANK",
 ]
@@ -40,7 +40,8 @@ class LoraError(RuntimeError):
 
 class _Seg(ctypes.Structure):
     _fields_ = [("perm", ctypes.c_void_p), ("seg_offsets", ctypes.c_void_p), ("seg_adapter", ctypes.c_void_p),
-                ("num_segments", ctypes.c_void_p), ("status", ctypes.c_void_p)]
+                ("num_segments", ctypes.c_void_p), ("tile_counts", ctypes.c_void_p), ("status", ctypes.c_void_p),
+                ("max_segments", ctypes.c_int32)]
 
 
 class _IO(ctypes.Structure):
@@ -129,22 +130,33 @@ def _need(t, dtype, what, ndim=None):
 
 
 class Segments:
-    """Device buffers of lora_segments_t for batches of up to ``num_rows`` rows."""
+    """Device buffers of lora_segments_t for batches of up to ``num_rows`` rows.
 
-    def __init__(self, num_rows: int, device="cuda"):
+    ``max_segments`` (host, 0 = none) bounds the segments of a build: the
+    number of distinct valid adapter ids of the batch, which the host that
+    formed the batch knows (see ``segment_bound``).  The calls size their
+    work items for it; a build with more segments drops those of the highest
+    slots and counts their rows into the status word."""
+
+    def __init__(self, num_rows: int, device="cuda", max_segments: int = 0):
         import torch
         n = max(int(num_rows), 1)
         i32 = dict(dtype=torch.int32, device=device)
         self.num_rows = int(num_rows)
+        self.max_segments = int(max_segments)
         self.perm = torch.zeros(n, **i32)
         self.seg_offsets = torch.zeros(n + 1, **i32)
         self.seg_adapter = torch.zeros(n, **i32)
         self.num_segments = torch.zeros(1, **i32)
+        self.tile_counts = torch.zeros(2, **i32)
         self.status = torch.zeros(1, **i32)
 
     def c(self) -> _Seg:
+        if self.max_segments < 0:
+            raise ValueError("max_segments must be >= 0")
         return _Seg(self.perm.data_ptr(), self.seg_offsets.data_ptr(), self.seg_adapter.data_ptr(),
-                    self.num_segments.data_ptr(), self.status.data_ptr())
+                    self.num_segments.data_ptr(), self.tile_counts.data_ptr(), self.status.data_ptr(),
+                    self.max_segments)
 
     def host(self):
         """(perm, seg_offsets, seg_adapter, status) copied to the host (synchronises)."""
@@ -152,6 +164,19 @@ class Segments:
         offs = self.seg_offsets[:ns + 1].cpu().numpy()
         return (self.perm[:int(offs[-1])].cpu().numpy(), offs, self.seg_adapter[:ns].cpu().numpy(),
                 int(self.status.item()))
+
+
+def segment_bound(row_adapter, num_slots: int) -> int:
+    """Host ids (any int array, one per row; for several adapters per row, a
+    [rows, depth] array: the most over the columns) -> the distinct valid
+    slots, the tightest ``Segments.max_segments`` for a batch (0 when it has
+    none)."""
+    import numpy as np
+    ids = np.asarray(row_adapter)
+    if ids.size == 0:
+        return 0
+    cols = ids.reshape(ids.shape[0], -1).T if ids.ndim > 1 else ids[None]
+    return max((int(np.unique(c[(c >= 0) & (c < num_slots)]).size) for c in cols), default=0)
 
 
 class ModuleIO:

@@ -13,8 +13,18 @@ namespace {
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
 lora_status_t check_segments(const lora_segments_t &seg) {
-  if (!seg.perm || !seg.seg_offsets || !seg.seg_adapter || !seg.num_segments || !seg.status) return LORA_ERR_NULL;
+  if (!seg.perm || !seg.seg_offsets || !seg.seg_adapter || !seg.num_segments || !seg.status || !seg.tile_counts)
+    return LORA_ERR_NULL;
+  if (seg.max_segments < 0) return LORA_ERR_SHAPE;
   return LORA_OK;
+}
+
+// The most segments a batch can have: one per row, one per slot, and the
+// caller's bound when it gives one.
+int segment_bound(int num_rows, int num_slots, const lora_segments_t &seg) {
+  int b = num_rows < num_slots ? num_rows : num_slots;
+  if (seg.max_segments > 0 && seg.max_segments < b) b = seg.max_segments;
+  return b;
 }
 
 size_t ws_need(int num_rows, int num_slots, int max_rank, int64_t sum_d_in) {  // covers every call
@@ -82,8 +92,9 @@ int pick_kc(int num_rows, int max_rank, int64_t max_seg, const ModuleArgs *ms, i
 void fill_desc(LayerDesc &d, const ModuleArgs *ms, int n, bool shrink, int num_rows, int num_slots, int max_rank,
                int table_cols, const lora_adapter_entry_t *table, const lora_segments_t &seg, void *ws) {
   d = LayerDesc{};
-  d.kc = pick_kc(num_rows, max_rank, num_rows < num_slots ? num_rows : num_slots, ms, n);
-  d.nt = pick_nt(max_rank, num_rows < num_slots ? num_rows : num_slots, ms, n);
+  const int max_seg = segment_bound(num_rows, num_slots, seg);
+  d.kc = pick_kc(num_rows, max_rank, max_seg, ms, n);
+  d.nt = pick_nt(max_rank, max_seg, ms, n);
   d.sg_nt = num_rows >= kPrefillRows ? kSgmvExpandCols : kSgmvExpandColsSmall;
   int item = 0, chunk = 0, sg = 0;
   for (int i = 0; i < n; ++i) {
@@ -114,10 +125,12 @@ void fill_desc(LayerDesc &d, const ModuleArgs *ms, int n, bool shrink, int num_r
   d.num_slots = num_slots;
   d.max_rank = max_rank;
   d.long_min = num_rows >= kLongSegRows ? kLongSegRows : 0x7fffffff;
+  d.max_seg = max_seg;
   d.perm = seg.perm;
   d.seg_offsets = seg.seg_offsets;
   d.seg_adapter = seg.seg_adapter;
   d.num_segments = seg.num_segments;
+  d.tile_counts = seg.tile_counts;
   d.status = seg.status;
   d.table = table;
   d.part = static_cast<float *>(ws);
@@ -127,8 +140,9 @@ void fill_desc(LayerDesc &d, const ModuleArgs *ms, int n, bool shrink, int num_r
 bool fits_u32(int64_t rows, int64_t ld) { return rows * ld * 2 <= (int64_t)0xFFFFFF00; }
 
 // Launch one phase (shrink or expand) over every module: decode items for
-// every possible segment, then SGMV items for every row tile that segments
-// of at least kLongSegRows rows can produce.
+// every possible segment and SGMV items for every row tile that segments of
+// at least kLongSegRows rows can produce (the kernels put the tiles the
+// build counted first and let the rest of that room exit).
 lora_status_t launch_phase(bool shrink, const ModuleArgs *ms, int n, int num_rows, int num_slots, int max_rank,
                            int table_cols, const lora_adapter_entry_t *table, const lora_segments_t &seg, void *ws,
                            const float *v_in, int64_t ldv, hipStream_t s) {
@@ -136,11 +150,10 @@ lora_status_t launch_phase(bool shrink, const ModuleArgs *ms, int n, int num_row
   fill_desc(d, ms, n, shrink, num_rows, num_slots, max_rank, table_cols, table, seg, ws);
   d.v = v_in;
   d.ldv = ldv;
-  const int64_t max_seg = num_rows < num_slots ? num_rows : num_slots;
-  const int64_t dec = max_seg * d.items_per_seg;
+  const int64_t dec = (int64_t)d.max_seg * d.items_per_seg;
   int64_t sg = 0;
   if (num_rows >= kLongSegRows)
-    sg = (int64_t)long_tiles_max(num_rows, num_slots, shrink ? sgmv_shrink_rows() : sgmv_expand_rows()) *
+    sg = (int64_t)long_tiles_max(num_rows, d.max_seg, shrink ? sgmv_shrink_rows() : sgmv_expand_rows()) *
          (shrink ? d.items_per_seg : d.sg_items);
   if (dec + sg > 0x7fffffff) return LORA_ERR_SHAPE;
   const hipError_t e = shrink ? launch_shrink(d, (int)dec, (int)(dec + sg), s) : launch_expand(d, (int)dec, (int)(dec + sg), s);
@@ -436,6 +449,9 @@ lora_status_t linear_phase(bool do_shrink, bool do_fused, const lora_linear_io_t
   f.ids = row_adapter;
   f.status = seg.status;
   f.table = table;
+  f.num_segments = seg.num_segments;
+  f.seg_adapter = seg.seg_adapter;
+  f.max_seg = segment_bound(num_rows, num_slots, seg);
   return launched(launch_fused(f, (int)blocks, s));
 }
 

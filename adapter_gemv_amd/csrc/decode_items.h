@@ -122,13 +122,13 @@ __device__ __forceinline__ void decode_shrink_rows(const LayerDesc &d, const Mod
   }
 }
 
-// Block `blk` of the decode shrink numbering.  JW = rows of A per wave at the
-// largest rank of the launch (4*JW).
+// Block `blk` of the decode shrink numbering (nseg: the segments built).  JW
+// = rows of A per wave at the largest rank of the launch (4*JW).
 template <int JW>
-__device__ __forceinline__ void decode_shrink_block(const LayerDesc &d, int blk) {
+__device__ __forceinline__ void decode_shrink_block(const LayerDesc &d, int blk, int nseg) {
   constexpr int RGM = 4;  // rows of x per pass for multi-row segments
   const int s = blk / d.items_per_seg;
-  if (s >= uniform(*d.num_segments)) return;
+  if (s >= nseg) return;
   const int it = blk - s * d.items_per_seg;
   const ModuleDesc m = module_of_item(d, it);
   const int chunk = it - m.item_base;
@@ -398,12 +398,12 @@ __device__ __forceinline__ void decode_expand_one_row(const LayerDesc &d, const 
   }
 }
 
-// Block `blk` of the decode expand numbering.  LPR = lanes per output row at
-// the largest rank of the launch (8*LPR).
+// Block `blk` of the decode expand numbering (nseg: the segments built).  LPR
+// = lanes per output row at the largest rank of the launch (8*LPR).
 template <int LPR>
-__device__ __forceinline__ void decode_expand_block(const LayerDesc &d, int blk, float *v_lds) {
+__device__ __forceinline__ void decode_expand_block(const LayerDesc &d, int blk, int nseg, float *v_lds) {
   const int s = blk / d.items_per_seg;
-  if (s >= uniform(*d.num_segments)) return;
+  if (s >= nseg) return;
   const int it = blk - s * d.items_per_seg;
   const ModuleDesc m = module_of_item(d, it);
   const int tile = it - m.item_base;

@@ -69,13 +69,17 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
   const int rt = local / m.n_tiles, tile = local - rt * m.n_tiles;
   const int row0 = rt * kFusedRows, n0 = tile * kFusedCols;
 
+  // Segments come in ascending slot order, so the slots with a segment in
+  // this build are the valid ones up to the last segment's.
+  const int nseg = min(uniform(*f.num_segments), f.max_seg);
+  const int last_slot = nseg > 0 ? uniform(f.seg_adapter[nseg - 1]) : -1;
   // Table entries of this wave's epilogue rows w + 4i, one per lane (i < 32).
   lora_adapter_entry_t my_e{};
   bool my_valid = false;
   if (lane < RPW) {
     const int b = row0 + w + 4 * lane;
     const int a = b < f.num_rows ? f.ids[b] : -1;
-    my_valid = (unsigned)a < (unsigned)f.num_slots;
+    my_valid = (unsigned)a < (unsigned)f.num_slots && a <= last_slot;
     if (my_valid) my_e = f.table[(int64_t)a * f.table_cols + m.col];
   }
 

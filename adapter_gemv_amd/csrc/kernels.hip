@@ -1,6 +1,7 @@
 // The delta kernels: one launch per phase covers every projection of the
-// call and every segment.  Blocks [0, decode_blocks) take decode items
-// (segments shorter than long_min rows), the rest take SGMV row tiles.  The
+// call and every segment.  The SGMV row tiles (segments of at least long_min
+// rows) come first, then decode_blocks blocks of decode items (shorter
+// segments); the grid's remaining blocks have no work.  The
 // rank class of the launch (smallest of 8, 16, 32, 64 holding max_rank) fixes
 // the register tiling of both paths.
 #include "decode_items.h"
@@ -25,13 +26,28 @@ constexpr int expand_lds_floats() {
 constexpr int kShrinkLdsAlloc = 64 * 1024;
 static_assert(kShrinkLdsBytes <= kShrinkLdsAlloc, "shrink LDS");
 
+// Blocks of the SGMV tiles the build counted (`tiles`, `items` blocks each),
+// at most the room the host left for them (`room` blocks).  They come first:
+// a tile of many rows is the longest work of the launch.  Then the decode
+// items; the unused room ends the grid, where its blocks exit at once.
+// (The order of the branches below changes the code the compiler produces
+// for each path: testing the decode range first measured faster shrinks for
+// batches of single-row segments, by about 2%, but slower matrix-core
+// paths, by 5 to 13%; this order keeps the matrix-core code.)
+__device__ __forceinline__ int sgmv_blocks(int tiles, int items, int room) {
+  return items > 0 ? min(max(tiles, 0), room / items) * items : 0;
+}
+
 template <int CLS>
 __global__ __launch_bounds__(256) void lora_shrink_kernel(LayerDesc d, int decode_blocks) {
   __shared__ __align__(16) uint8_t lds[kShrinkLdsAlloc];
   constexpr int JW = 2 << CLS;                          // A rows per wave (decode)
   constexpr int NT = CLS <= 1 ? 1 : CLS == 2 ? 2 : 4;   // 16-column rank tiles (SGMV)
-  if ((int)blockIdx.x < decode_blocks) decode_shrink_block<JW>(d, blockIdx.x);
-  else sgmv_shrink_block<NT>(d, blockIdx.x - decode_blocks, lds);
+  const int b = blockIdx.x;
+  const int nseg = uniform(*d.num_segments);  // requested with the tile count: one wait for both
+  const int sg = sgmv_blocks(uniform(d.tile_counts[0]), d.items_per_seg, (int)gridDim.x - decode_blocks);
+  if (b < sg) sgmv_shrink_block<NT>(d, b, lds);
+  else if (b < sg + decode_blocks) decode_shrink_block<JW>(d, b - sg, nseg);
 }
 
 // Waves per SIMD the expand is compiled for: every path of the kernel (bf16
@@ -47,8 +63,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CLS <= 1 ? 
   // k-chunk partials per round of the SGMV V staging: 4 where the register
   // bound leaves room (ranks 32 and 64), else 2
   constexpr int VU = CLS >= 2 ? 4 : 2;
-  if ((int)blockIdx.x < decode_blocks) decode_expand_block<LPR>(d, blockIdx.x, lds);
-  else sgmv_expand_block<KT, VU>(d, blockIdx.x - decode_blocks, lds);
+  const int b = blockIdx.x;
+  const int nseg = uniform(*d.num_segments);  // requested with the tile count: one wait for both
+  const int sg = sgmv_blocks(uniform(d.tile_counts[1]), d.sg_items, (int)gridDim.x - decode_blocks);
+  if (b < sg) sgmv_expand_block<KT, VU>(d, b, lds);
+  else if (b < sg + decode_blocks) decode_expand_block<LPR>(d, b - sg, nseg, lds);
 }
 
 // Sum the k-chunk partials of each row in a segment into v[b][0..max_rank)
@@ -56,7 +75,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CLS <= 1 ? 
 // v_out + blockIdx.y * num_rows * ldv (lora_shrink: one module, the caller's
 // v; the fused layer: every module, planes in the workspace).
 __global__ __launch_bounds__(256) void shrink_reduce_kernel(LayerDesc d) {
-  const int nseg = min(*d.num_segments, min(d.num_rows, d.num_slots));
+  const int nseg = min(*d.num_segments, d.max_seg);
   if (nseg <= 0) return;
   const int nvalid = min(d.seg_offsets[nseg], d.num_rows);
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -92,8 +111,8 @@ int rank_class(int max_rank) { return max_rank <= 8 ? 0 : max_rank <= 16 ? 1 : m
 
 }  // namespace
 
-int long_tiles_max(int num_rows, int num_slots, int rows_per_tile) {
-  const int long_segs = min(num_slots, num_rows / kLongSegRows);
+int long_tiles_max(int num_rows, int max_seg, int rows_per_tile) {
+  const int long_segs = min(max_seg, num_rows / kLongSegRows);
   return num_rows / rows_per_tile + long_segs + 1;
 }
 int sgmv_shrink_rows() { return kSgmvShrinkRows; }

@@ -21,6 +21,10 @@ constexpr int kMaxModules = LORA_NUM_MODULES;
 // Segments of at least this many rows go to the matrix-core (SGMV) kernels;
 // shorter ones to the decode kernels.
 constexpr int kLongSegRows = 8;
+// Rows per SGMV block: shrink 4 waves x 2 tiles of 16, expand 4 tiles of 16
+// (all in every wave).  The segment builder counts the tiles of these sizes.
+constexpr int kSgmvShrinkRows = 128;
+constexpr int kSgmvExpandRows = 64;
 // Batches of at least this many rows use a larger shrink k-chunk.
 constexpr int kPrefillRows = 2048;
 // Output columns per SGMV expand block (the most a block stages for): in
@@ -69,12 +73,14 @@ struct LayerDesc {
   int32_t num_slots;
   int32_t max_rank;
   int32_t long_min;       // segments with at least this many rows: SGMV path
+  int32_t max_seg;        // segments the grid covers: min(rows, slots, the caller's bound)
   int32_t sg_items;       // SGMV expand items (n-tiles over all modules) per row tile
   int32_t sg_nt;          // SGMV expand n-tile
   const int32_t *perm;
   const int32_t *seg_offsets;
   const int32_t *seg_adapter;
   const int32_t *num_segments;
+  const int32_t *tile_counts;  // SGMV tiles of the build: [0] shrink, [1] expand
   int32_t *status;
   const lora_adapter_entry_t *table;
   float *part;            // partials [chunks][num_rows][rs]
@@ -116,6 +122,11 @@ struct FusedDesc {
   const int32_t *ids;  // the rows' adapter slots, original order
   int32_t *status;
   const lora_adapter_entry_t *table;
+  // the segments of the build: a row's delta applies only when its slot has
+  // one (the builder may have dropped slots past the caller's bound)
+  const int32_t *num_segments;
+  const int32_t *seg_adapter;
+  int32_t max_seg;
 };
 
 hipError_t launch_fused(const FusedDesc &f, int blocks, hipStream_t stream);
@@ -136,7 +147,7 @@ hipError_t launch_shrink_reduce(const LayerDesc &d, hipStream_t stream);
 hipError_t launch_shrink(const LayerDesc &d, int decode_blocks, int grid, hipStream_t stream);
 hipError_t launch_expand(const LayerDesc &d, int decode_blocks, int grid, hipStream_t stream);
 
-int long_tiles_max(int num_rows, int num_slots, int rows_per_tile);
+int long_tiles_max(int num_rows, int max_seg, int rows_per_tile);
 int sgmv_shrink_rows();
 int sgmv_expand_rows();
 

@@ -26,6 +26,21 @@
 namespace lora {
 namespace {
 
+// The end of a build, by one thread once every segment start is written:
+// segs segments hold `rows` rows.  Past the caller's bound (max_segments)
+// the segments of the highest slots are dropped and their rows counted as
+// bad; the status word gets (or, add_status, has added) the bad rows.
+__device__ void finish_segments(const lora_segments_t &seg, int segs, int rows, bool add_status, int nbad) {
+  if (seg.max_segments > 0 && segs > seg.max_segments) {
+    nbad += rows - seg.seg_offsets[seg.max_segments];  // the kept rows end where segment max_segments starts
+    segs = seg.max_segments;
+  } else {
+    seg.seg_offsets[segs] = rows;
+  }
+  *seg.num_segments = segs;
+  *seg.status = add_status ? *seg.status + nbad : nbad;
+}
+
 // Exclusive scan of one int per thread over a block of THREADS threads;
 // *total gets the sum.  s_w holds THREADS/64 + 1 ints.
 template <int THREADS>
@@ -56,6 +71,38 @@ __device__ int block_excl_scan(int x, int *total, int *s_w) {
   *total = s_w[kWaves];
   __syncthreads();
   return res;
+}
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Segments a build keeps: all, or the caller's bound when there are more.
+__device__ __forceinline__ int kept_segments(const lora_segments_t &seg, int segs) {
+  return seg.max_segments > 0 && segs > seg.max_segments ? seg.max_segments : segs;
+}
+
+// Every thread of the (scan) block, once the kept segments' offsets are
+// written: the SGMV row tiles of those segments (segments of at least kLongSegRows
+// rows, in batches of at least that many rows) for the other calls, in
+// tiles of kSgmvShrinkRows and of kSgmvExpandRows rows.
+template <int THREADS>
+__device__ void count_long_tiles(const lora_segments_t &seg, int n, int segs, int *s_w) {
+  int shr = 0, exp = 0;
+  if (n >= kLongSegRows) {
+    for (int s = threadIdx.x; s < segs; s += THREADS) {
+      const int len = seg.seg_offsets[s + 1] - seg.seg_offsets[s];
+      if (len >= kLongSegRows) {
+        shr += ceil_div(len, kSgmvShrinkRows);
+        exp += ceil_div(len, kSgmvExpandRows);
+      }
+    }
+  }
+  int tot_shr, tot_exp;
+  block_excl_scan<THREADS>(shr, &tot_shr, s_w);
+  block_excl_scan<THREADS>(exp, &tot_exp, s_w);
+  if (threadIdx.x == 0) {
+    seg.tile_counts[0] = tot_shr;
+    seg.tile_counts[1] = tot_exp;
+  }
 }
 
 // Rows of this block with the same id before / after row t.  s_ids holds the
@@ -106,6 +153,7 @@ __global__ __launch_bounds__(THREADS) void seg_small_kernel(const int32_t *__res
   if (id >= 0 && after == 0) counts[id] = before + 1;
   __syncthreads();
   int carry = 0;  // rows | segments << 16 of the slots before this pass
+  int tiles = 0;  // this thread's SGMV tiles of kept segments: expand | shrink << 16 (at most 144 each)
   for (int base = 0; base < num_slots; base += THREADS) {
     const int a = base + t;
     const int c = a < num_slots ? counts[a] : 0;
@@ -117,14 +165,19 @@ __global__ __launch_bounds__(THREADS) void seg_small_kernel(const int32_t *__res
       if (c > 0) {
         seg.seg_offsets[ex >> 16] = ex & 0xffff;
         seg.seg_adapter[ex >> 16] = a;
+        const bool kept = seg.max_segments <= 0 || (ex >> 16) < seg.max_segments;
+        if (kept && n >= kLongSegRows && c >= kLongSegRows)
+          tiles += ceil_div(c, kSgmvExpandRows) | ceil_div(c, kSgmvShrinkRows) << 16;
       }
     }
     carry += tot;
   }
+  int all_tiles;
+  block_excl_scan<THREADS>(tiles, &all_tiles, s_w);  // its barriers also publish every segment start
   if (t == 0) {
-    seg.seg_offsets[carry >> 16] = carry & 0xffff;
-    *seg.num_segments = carry >> 16;
-    *seg.status = add_status ? *seg.status + nbad : nbad;
+    finish_segments(seg, carry >> 16, carry & 0xffff, add_status, nbad);
+    seg.tile_counts[0] = all_tiles >> 16;
+    seg.tile_counts[1] = all_tiles & 0xffff;
   }
   __syncthreads();
   if (id >= 0) seg.perm[counts[id] + before] = t;
@@ -166,7 +219,7 @@ constexpr int kScanPer = 8;  // consecutive elements per thread and pass
 // One block: exclusive scan of hist in slot-major order (the first output
 // position of each (slot, chunk)), then the segments: slot a opens one at
 // hist[a * nchunks] when its rows are non-zero.
-__global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(int num_slots, int nchunks, bool add_status,
+__global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(int n, int num_slots, int nchunks, bool add_status,
                                                                 lora_segments_t seg,
                                                                 int32_t *__restrict__ hist,
                                                                 const int32_t *__restrict__ badc) {
@@ -215,11 +268,10 @@ __global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(int num_slots, i
     }
     segs += tot;
   }
-  if (t == 0) {
-    seg.seg_offsets[segs] = carry;
-    *seg.num_segments = segs;
-    *seg.status = add_status ? *seg.status + nbad : nbad;
-  }
+  __syncthreads();  // every segment start is written
+  if (t == 0) finish_segments(seg, segs, carry, add_status, nbad);
+  __syncthreads();
+  count_long_tiles<kScanThreads>(seg, n, kept_segments(seg, segs), s_w);
 }
 
 // Chunk c: every valid row goes to its slot's position for this chunk plus
@@ -266,7 +318,7 @@ hipError_t launch_build_segments(const int32_t *ids, int stride, int n, int num_
   seg_chunk_kernel<<<nchunks, kSegChunk, 0, stream>>>(ids, stride, n, num_slots, nchunks, hist, lrank, badc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  seg_scan_kernel<<<1, kScanThreads, 0, stream>>>(num_slots, nchunks, add_status, seg, hist, badc);
+  seg_scan_kernel<<<1, kScanThreads, 0, stream>>>(n, num_slots, nchunks, add_status, seg, hist, badc);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   seg_scatter_kernel<<<nchunks, kSegChunk, 0, stream>>>(ids, stride, n, num_slots, nchunks, seg, hist, lrank);

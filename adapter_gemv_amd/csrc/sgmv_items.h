@@ -40,15 +40,13 @@
 
 namespace lora {
 
-constexpr int kSgmvShrinkRows = 128;  // rows per shrink block: 4 waves x 2 tiles of 16
-constexpr int kSgmvExpandRows = 64;   // rows per expand block: 4 tiles of 16, all in every wave
 
 // Tile (segment, row tile) of a block among the segments of at least
 // long_min rows, in segment order, `rows` rows per tile: one wave-wide scan
 // over the segment list.  False when the block has no tile.
 __device__ __forceinline__ bool find_long_tile(const LayerDesc &d, int tile, int rows, int *s_out, int *rt_out) {
   const int lane = threadIdx.x & 63;
-  const int nseg = min(uniform(*d.num_segments), min(d.num_rows, d.num_slots));
+  const int nseg = min(uniform(*d.num_segments), d.max_seg);
   int base = 0;
   for (int s0 = 0; s0 < nseg; s0 += 64) {
     const int s = s0 + lane;

@@ -307,6 +307,9 @@ def main():
     ap.add_argument("--replicas", type=int, default=0,
                     help="independent copies of the adapters to rotate through (0 = enough to exceed 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-segment-bound", action="store_true",
+                    help="give the calls no bound on the segments (max_segments = 0): work items sized for one "
+                         "adapter per row")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (3 times), to scale HBM byte counters")
     ap.add_argument("--summarize-profile", action="store_true",
@@ -371,7 +374,8 @@ def main():
     reps = args.replicas or max(1, int(np.ceil(1.0e9 / max(adapters_bytes, 1))))
     reps = min(reps, 64)
     print(f"[bench] uploading {reps} replica(s)", file=sys.stderr, flush=True)
-    dws = [DeviceWorkload(w) for _ in range(reps)]
+    # The host formed the batch, so it passes the batch's distinct adapter count as the segment bound.
+    dws = [DeviceWorkload(w, bound_segments=not args.no_segment_bound) for _ in range(reps)]
     torch.cuda.synchronize()
 
     import adapter_gemv_amd as lg
@@ -483,6 +487,7 @@ def main():
         "data": "synthetic (seeded, shapes of the pages' 70B workloads)",
         "config": {"workload": DESCRIPTIONS[args.workload], "name": args.workload, "rows": w.num_rows,
                    "distinct_adapters": int(len(np.unique(w.ids[w.ids >= 0]))),
+                   "max_segments": dws[0].seg.max_segments,
                    "modules": [m.name for m in w.modules], "max_rank": w.max_rank,
                    "adapter_replicas": reps, "parallelism": "single GPU"},
         "hbm": {"algorithmic_bytes_per_step": traffic["total"],

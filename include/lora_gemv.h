@@ -149,17 +149,37 @@ typedef struct lora_adapter_entry {
  *                                 [seg_offsets[s], seg_offsets[s+1])
  *   seg_adapter   [num_rows]      adapter slot of segment s
  *   num_segments  [1]             number of segments
+ *   tile_counts   [2]             sizes of the build's work for the other
+ *                                 calls (how many of their row tiles the
+ *                                 segments fill); no meaning to the caller
  *   status        [1]             0, or the number of rows with an id
- *                                 >= num_slots at the last build plus one per
- *                                 (segment, projection) skipped since then
+ *                                 >= num_slots or in a segment past
+ *                                 max_segments at the last build, plus one
+ *                                 per (segment, projection) skipped since then
  * Only the first num_segments (+1) entries are meaningful.
+ * One host value rides along:
+ *   max_segments  0, or a bound on the segments of a build: the number of
+ *                 distinct valid slot ids in the batch, which a host that
+ *                 formed the batch knows ("12. Adapter Serving ...",
+ *                 "Scheduling with adapter awareness": the scheduler groups
+ *                 requests by adapter).  Every call sizes its tiles and grid
+ *                 for min(num_rows, num_slots, max_segments) segments, so a
+ *                 tight bound gives a batch of few adapters short work items
+ *                 instead of items sized for one adapter per row.  A build
+ *                 that finds more segments keeps the first max_segments
+ *                 (lowest slots) and counts the rows of the others into
+ *                 *status (those rows get no delta); the other calls apply at
+ *                 most max_segments segments.  Use one value for a build and
+ *                 the calls that read its segments.  Negative: LORA_ERR_SHAPE.
  */
 typedef struct lora_segments {
   int32_t *perm;
   int32_t *seg_offsets;
   int32_t *seg_adapter;
   int32_t *num_segments;
+  int32_t *tile_counts;
   int32_t *status;
+  int32_t max_segments;
 } lora_segments_t;
 
 /* One projection of a layer for lora_apply_layer. */

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol():
 
 
 def seg(**kw):
-    d = dict(perm=P, seg_offsets=P, seg_adapter=P, num_segments=P, status=P)
+    d = dict(perm=P, seg_offsets=P, seg_adapter=P, num_segments=P, tile_counts=P, status=P)
     d.update(kw)
     return lg._Seg(**d)
 
@@ -64,12 +64,14 @@ def test_workspace_query():
 @pytest.mark.parametrize("args,code", [
     (dict(seg=seg(perm=None)), NULL),
     (dict(seg=seg(status=None)), NULL),
+    (dict(seg=seg(tile_counts=None)), NULL),
     (dict(n=-1), SHAPE),
     (dict(slots=0), SHAPE),
     (dict(ids=None), NULL),
     (dict(n=5000, ws=None), NULL),           # long batches need workspace
     (dict(n=5000, ws_bytes=0), WS),          # long batches need workspace
     (dict(n=128, slots=20000, ws_bytes=0), WS),  # so do very large slot tables
+    (dict(seg=seg(max_segments=-1)), SHAPE),
 ])
 def test_build_segments_rejects(args, code):
     a = dict(ids=P, n=128, slots=16, seg=seg(), ws=P, ws_bytes=BIG)
@@ -84,7 +86,7 @@ SHRINK = dict(x=P, ldx=1024, n=64, d=1024, table=P, slots=8, n_mod=7, module=0, 
 @pytest.mark.parametrize("fn", ["lora_shrink", "lora_expand"])
 @pytest.mark.parametrize("args,code", [
     (dict(x=None), NULL), (dict(table=None), NULL), (dict(v=None), NULL),
-    (dict(seg=seg(seg_adapter=None)), NULL),
+    (dict(seg=seg(seg_adapter=None)), NULL), (dict(seg=seg(max_segments=-3)), SHAPE),
     (dict(n_mod=0), MODULE), (dict(n_mod=8), MODULE), (dict(module=7), MODULE), (dict(module=-1), MODULE),
     (dict(max_rank=0), RANK), (dict(max_rank=65), RANK),
     (dict(n=-1), SHAPE), (dict(slots=0), SHAPE), (dict(d=0), SHAPE), (dict(ldx=1016), SHAPE), (dict(ldv=8), SHAPE),
@@ -126,6 +128,7 @@ def ios(**over):
 @pytest.mark.parametrize("fn", ["lora_apply_layer", "lora_layer_shrink", "lora_layer_expand"])
 @pytest.mark.parametrize("args,code", [
     (dict(io=None), NULL), (dict(table=None), NULL), (dict(ws=None), NULL), (dict(seg=seg(num_segments=None)), NULL),
+    (dict(seg=seg(max_segments=-1)), SHAPE),
     (dict(mask=0), MODULE), (dict(mask=0x80), MODULE),
     (dict(n=-1), SHAPE), (dict(slots=0), SHAPE),
     (dict(max_rank=0), RANK), (dict(max_rank=100), RANK),
@@ -155,3 +158,16 @@ def test_python_binding_rejects_cpu_tensors():
     s = lg.Segments.__new__(lg.Segments)
     with pytest.raises((TypeError, ValueError)):
         lg.build_segments(torch.zeros(4, dtype=torch.int32), 4, s, torch.zeros(16, dtype=torch.uint8))
+
+
+def test_segment_bound_counts_distinct_valid_slots():
+    import numpy as np
+    assert lg.segment_bound(np.array([3, 3, -1, 7, 9, 2, 3]), 8) == 3          # 9 >= slots, -1 base only
+    assert lg.segment_bound(np.zeros(0, np.int32), 8) == 0
+    assert lg.segment_bound(np.array([-1, -2]), 8) == 0
+    # several adapters per row: the most over the columns (one build per column)
+    assert lg.segment_bound(np.array([[0, 1], [0, 2], [0, 3], [5, -1]]), 8) == 3
+    s = lg.Segments.__new__(lg.Segments)  # no buffers: the bound is checked first
+    s.max_segments = -1
+    with pytest.raises(ValueError):
+        s.c()

@@ -49,7 +49,7 @@ def test_workload_full_size(name):
     rows = sample_rows(w)
     ref = oracle.lora_layer(w, rows=rows)
     note(f"workload {name}: {w.num_rows} rows, {w.num_slots} slots, modules {[m.name for m in w.modules]}")
-    dw = DeviceWorkload(w)
+    dw = DeviceWorkload(w, bound_segments=True)  # as the bench runs it
     # delta alone
     dw.reset_y(zero=True)
     dw.step()

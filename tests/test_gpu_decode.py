@@ -41,6 +41,9 @@ def test_segments_bit_exact(n, slots, lo, hi):
     assert np.array_equal(offs, ref.seg_offsets)
     assert np.array_equal(adap, ref.seg_adapter)
     assert status == ref.num_bad_ids
+    lens = np.diff(ref.seg_offsets.astype(np.int64))
+    long = lens[lens >= 8] if n >= 8 else lens[:0]  # the build's SGMV tiles: 128 rows (shrink), 64 (expand)
+    assert seg.tile_counts.cpu().tolist() == [int(((long + 127) // 128).sum()), int(((long + 63) // 64).sum())]
 
 
 def test_segments_sorted_runs():

@@ -26,9 +26,9 @@ def _name_case(request):
 class FusedRun:
     """A workload on the device with its base weights; run() fills y."""
 
-    def __init__(self, w):
+    def __init__(self, w, bound_segments=False):
         self.w = w
-        self.dw = DeviceWorkload(w)
+        self.dw = DeviceWorkload(w, bound_segments=bound_segments)
 
     def run(self, phases=False):
         w, dw = self.w, self.dw
@@ -45,9 +45,9 @@ class FusedRun:
         return {m.name: bf16_host(dw.y[m.name]) for m in w.modules}
 
 
-def check_fused(w, rows=None):
+def check_fused(w, rows=None, bound_segments=False):
     ref = oracle.linear_layer(w, rows=rows)
-    got = FusedRun(w).run()
+    got = FusedRun(w, bound_segments).run()
     for m in w.modules:
         g = got[m.name] if rows is None else got[m.name][rows]
         assert np.isfinite(g).all(), m.name
@@ -133,7 +133,7 @@ def test_fused_full_layer_sampled_rows():
     w = gen.make_workload("fused_layer_r64")
     rows = np.random.default_rng(1).choice(w.num_rows, 12, replace=False).astype(np.int32)
     note(f"fused full layer: rows {list(rows)}")
-    check_fused(w, rows=rows)
+    check_fused(w, rows=rows, bound_segments=True)  # as the bench runs it
 
 
 def test_phases_equal_the_whole_call():

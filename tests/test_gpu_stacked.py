@@ -32,9 +32,9 @@ def run_stacked(dw, ra, pass_max_rank=None):
     torch.cuda.synchronize()
 
 
-def check_stacked(w, ra, pass_max_rank=None):
+def check_stacked(w, ra, pass_max_rank=None, bound_segments=False):
     ref = oracle.lora_layer_stacked(w, ra, pass_max_rank=pass_max_rank)
-    dw = DeviceWorkload(w)
+    dw = DeviceWorkload(w, bound_segments=bound_segments)
     dw.reset_y(zero=True)
     run_stacked(dw, ra, pass_max_rank)
     for m in w.modules:
@@ -139,4 +139,4 @@ def test_zero_rows_resets_the_segments():
 def test_stacked_layer_full_size():
     # the bench's workload: 70B layer, 128 rows, a shared domain adapter (r64) and a style adapter (r16) per row
     w = gen.make_workload("stacked_layer")
-    check_stacked(w, w.stack, (64, 16))
+    check_stacked(w, w.stack, (64, 16), bound_segments=True)  # as the bench runs it

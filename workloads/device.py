@@ -29,7 +29,10 @@ class DeviceWorkload:
     """Device copies of a workload: ids, x, pristine y0, working y, the factor
     pool, the adapter table, segment buffers and a workspace."""
 
-    def __init__(self, w: Workload, device="cuda", ws_extra_rows: int = 0):
+    def __init__(self, w: Workload, device="cuda", ws_extra_rows: int = 0, bound_segments: bool = False):
+        """bound_segments: give the calls the batch's distinct adapter count
+        (of each column of ``w.stack`` when set), as a host that formed the
+        batch would."""
         self.w = w
         self.device = device
         self.ids = torch.from_numpy(np.ascontiguousarray(w.ids, dtype=np.int32)).to(device)
@@ -39,7 +42,8 @@ class DeviceWorkload:
         self.pool = bf16_tensor(w.pool, device)
         self.table_host = self.pack(self.pool.data_ptr())
         self.table = torch.from_numpy(self.table_host.view(np.uint8).reshape(-1).copy()).to(device)
-        self.seg = lg.Segments(w.num_rows + ws_extra_rows, device)
+        bound = lg.segment_bound(w.ids if w.stack is None else w.stack, w.num_slots) if bound_segments else 0
+        self.seg = lg.Segments(w.num_rows + ws_extra_rows, device, max_segments=bound)
         sum_d_in = sum(m.d_in for m in w.modules)
         self.ws_bytes = lg.workspace_bytes(w.num_rows + ws_extra_rows, w.num_slots, w.max_rank, sum_d_in)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
