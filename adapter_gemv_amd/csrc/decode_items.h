@@ -160,6 +160,11 @@ __device__ __forceinline__ void decode_shrink_block(const LayerDesc &d, int blk,
 // int8 row scales in the first.
 constexpr int kOneRowDeltaBase = 64 + 1024;
 
+// Load passes per sub-tile of the decode expand: 16, or fewer where G rows
+// per pass would make a sub-tile longer than the tile capacity NTC (narrow
+// lane widths in a launch of a higher rank class).
+constexpr int expand_passes(int ntc, int g) { return 16 * g <= ntc ? 16 : ntc / g; }
+
 // Row stride of B: the rank rounded up to a multiple of 8, so every row is
 // 16-byte aligned.  Columns in [rank, ldb) are padding with finite values;
 // they meet zeros of v and add nothing.
@@ -215,12 +220,12 @@ struct BTile {
 // is staged once; the B sub-tile is loaded once into registers and used by
 // all rows, and the next sub-tile is requested when the rows are done; y of
 // a few rows is requested together.
-template <int LPR, bool Q8>
+template <int LPR, bool Q8, int NTC>
 __device__ __forceinline__ void decode_expand_rows(const LayerDesc &d, const ModuleDesc &m, const void *B, int rank,
                                                    float scale, int pos0, int len, int tile, float *v_lds) {
   static_assert(kLongSegRows <= kExpandRowGroup, "a decode segment is staged in one group");
   constexpr int G = kDecodeThreads / LPR;  // output rows per load pass of the block
-  constexpr int P = 16;                    // load passes per sub-tile
+  constexpr int P = expand_passes(NTC, G);  // load passes per sub-tile
   constexpr int SUB = P * G;               // outputs per sub-tile
   constexpr int PL = P / LPR;              // outputs per lane per row after the reduce-scatter
   constexpr int YR = PL <= 4 ? 4 : 1;      // rows whose y is requested together
@@ -243,7 +248,7 @@ __device__ __forceinline__ void decode_expand_rows(const LayerDesc &d, const Mod
   for (int p = 0; p < P; ++p) bv[p] = load_b(p * G + g);
   float *b_scale = v_lds + kOneRowDeltaBase;  // Q8: [NT] row scales of the tile, published by finish()
   if constexpr (Q8) {
-    constexpr int NT = decode_expand_tile(LPR);  // the host tiles with the same constant
+    constexpr int NT = NTC;  // the launch's tile capacity: the host tiles with the same constant
     const rsrc_t rs = make_rsrc(bt.scale, tile_len * 4);
 #pragma unroll
     for (int i = 0; i < NT / (kDecodeThreads * 4); ++i) {
@@ -307,17 +312,17 @@ __device__ __forceinline__ void decode_expand_rows(const LayerDesc &d, const Mod
 // Q8: a lane takes 16 int8 values (16 bytes) of a row, so half as many
 // lanes share a row and a load moves as many bytes as in bf16.
 
-template <int LPR, bool Q8>
+template <int LPR, bool Q8, int NTC>
 __device__ __forceinline__ void decode_expand_one_row(const LayerDesc &d, const ModuleDesc &m, const void *B,
                                                       int rank, float scale, int pos0, int tile, int item,
                                                       float *v_lds) {
   constexpr int VPL = Q8 ? 16 : 8;                  // values per lane and load
   constexpr int L = Q8 && LPR > 1 ? LPR / 2 : LPR;  // lanes per output row
   constexpr int G = kDecodeThreads / L;
-  constexpr int P = 16;
+  constexpr int P = expand_passes(NTC, G);
   constexpr int SUB = P * G;
   constexpr int PL = P / L;
-  constexpr int NT = decode_expand_tile(LPR);
+  constexpr int NT = NTC;
   static_assert(NT % SUB == 0 && NT % (kDecodeThreads * 8) == 0, "tile");
   constexpr int YT = NT / (kDecodeThreads * 8);  // 16-byte y pieces per thread
   using BT = BTile<Q8, VPL>;
@@ -400,6 +405,10 @@ __device__ __forceinline__ void decode_expand_one_row(const LayerDesc &d, const 
 
 // Block `blk` of the decode expand numbering (nseg: the segments built).  LPR
 // = lanes per output row at the largest rank of the launch (8*LPR).
+// An item runs at the lane width of its entry's own rank (rank/8 lanes per
+// output row, rounded up to a power of two), not at the launch's: a rank-8
+// entry in a rank-64 launch streams its B tile with every lane busy and one
+// eighth of the load instructions.  The tile and its LDS are the launch's.
 template <int LPR>
 __device__ __forceinline__ void decode_expand_block(const LayerDesc &d, int blk, int nseg, float *v_lds) {
   const int s = blk / d.items_per_seg;
@@ -412,13 +421,23 @@ __device__ __forceinline__ void decode_expand_block(const LayerDesc &d, int blk,
   if (len >= d.long_min) return;  // an SGMV item takes this segment
   lora_adapter_entry_t e;
   if (!load_entry(d, a, m.col, tile == 0, &e)) return;
-  auto run = [&](auto q8) {
+  constexpr int NTC = decode_expand_tile(LPR);
+  auto run = [&](auto q8, auto lw) {
     constexpr bool Q8 = decltype(q8)::value;
-    if (len == 1) decode_expand_one_row<LPR, Q8>(d, m, e.B, e.rank, e.scale, pos0, tile, blk, v_lds);
-    else decode_expand_rows<LPR, Q8>(d, m, e.B, e.rank, e.scale, pos0, len, tile, v_lds);
+    constexpr int LW = decltype(lw)::value;
+    if constexpr (LW <= LPR) {
+      if (len == 1) decode_expand_one_row<LW, Q8, NTC>(d, m, e.B, e.rank, e.scale, pos0, tile, blk, v_lds);
+      else decode_expand_rows<LW, Q8, NTC>(d, m, e.B, e.rank, e.scale, pos0, len, tile, v_lds);
+    }
   };
-  if (e.format == LORA_FORMAT_INT8_ROWS) run(std::true_type{});
-  else run(std::false_type{});
+  auto by_width = [&](auto q8) {  // e.rank <= d.max_rank (load_entry), so the width is at most LPR
+    if (e.rank <= 8) run(q8, std::integral_constant<int, 1>{});
+    else if (e.rank <= 16) run(q8, std::integral_constant<int, 2>{});
+    else if (e.rank <= 32) run(q8, std::integral_constant<int, 4>{});
+    else run(q8, std::integral_constant<int, 8>{});
+  };
+  if (e.format == LORA_FORMAT_INT8_ROWS) by_width(std::true_type{});
+  else by_width(std::false_type{});
 }
 
 }  // namespace lora
