@@ -29,9 +29,12 @@ constexpr int kSgmvExpandRows = 64;
 constexpr int kPrefillRows = 2048;
 // Output columns per SGMV expand block (the most a block stages for): in
 // batches of fewer than kPrefillRows rows, whose long segments give few row
-// tiles, a quarter of that, so the launch has more blocks (measured 13-19%
+// tiles, half of that, so the launch has more blocks (measured 13-19%
 // faster on the expand of 256-row Zipf batches; the same at 256 columns).
-constexpr int kSgmvExpandCols = 2048;
+// Prefill batches: 1024 columns measured 2-5% faster than 2048 (each block
+// re-sums its rows' k-chunk partials, but more blocks per row tile keep more
+// of the y read-modify-write in flight); 512 and 4096 were slower.
+constexpr int kSgmvExpandCols = 1024;
 constexpr int kSgmvExpandColsSmall = 512;
 
 // Threads per block of the decode kernels: 4 waves of 64.
