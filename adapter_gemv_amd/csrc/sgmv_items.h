@@ -85,6 +85,8 @@ constexpr int kShrinkXBytes = kSgmvShrinkRows * kShrinkRound * 2;  // 16 KiB
 constexpr int kShrinkABytes = 64 * kShrinkRound * 2;               // 8 KiB
 constexpr int kShrinkBufBytes = kShrinkXBytes + kShrinkABytes;
 constexpr int kShrinkLdsBytes = 2 * kShrinkBufBytes;
+constexpr int kShrinkStages = 4;  // rounds in flight (even)
+static_assert(kShrinkStages % 2 == 0, "rounds alternate between two LDS buffers");
 
 __device__ __forceinline__ uint32_t shrink_lds_off(int row, int piece) {
   return (uint32_t)row * (kShrinkRound * 2) + (uint32_t)((piece ^ (row & 7)) * 16);
@@ -182,23 +184,25 @@ __device__ __forceinline__ void sgmv_shrink_tile(const LayerDesc &d, const Modul
                                                                 0, 0);
     }
   };
-  // Two rounds in flight in registers; round i is written to buffer i & 1,
-  // one barrier per round.  A buffer is rewritten two rounds after it was
-  // read, and every wave has passed the barrier in between.
-  Stage s0, s1;
-  load(s0, k_begin);
-  load(s1, k_begin + kShrinkRound);
+  // kShrinkStages rounds in flight in registers (a short segment's block
+  // is a chain of rounds, each waiting one memory latency, so its time is
+  // the chunk's rounds over the rounds in flight); round i is written to
+  // LDS buffer i & 1, one barrier per round.  A buffer is rewritten two
+  // rounds after it was read, and every wave has passed the barrier in
+  // between.  Rounds past the chunk load nothing and add zeros.
+  Stage st[kShrinkStages];
+#pragma unroll
+  for (int i = 0; i < kShrinkStages; ++i) load(st[i], k_begin + i * kShrinkRound);
   const int rounds = (k_end - k_begin + kShrinkRound - 1) / kShrinkRound;
-  for (int r = 0; r < rounds; r += 2) {
-    uint8_t *b0 = lds, *b1 = lds + kShrinkBufBytes;
-    store(s0, b0);
-    load(s0, k_begin + (r + 2) * kShrinkRound);
-    __syncthreads();
-    compute(b0);
-    store(s1, b1);
-    load(s1, k_begin + (r + 3) * kShrinkRound);
-    __syncthreads();
-    compute(b1);
+  for (int r = 0; r < rounds; r += kShrinkStages) {
+#pragma unroll
+    for (int i = 0; i < kShrinkStages; ++i) {
+      uint8_t *buf = lds + (i & 1) * kShrinkBufBytes;  // kShrinkStages is even: round r + i has parity i
+      store(st[i], buf);
+      load(st[i], k_begin + (r + i + kShrinkStages) * kShrinkRound);
+      __syncthreads();
+      compute(buf);
+    }
   }
   // C[4*(l/16) + i][l%16] of tile (mt, nt): row 32w + 16mt + 4*(l/16) + i, column 16nt + l%16.
   float *out = d.part + ((int64_t)(m.part_base + chunk) * d.num_rows + seg0) * d.rs;
