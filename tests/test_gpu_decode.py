@@ -15,7 +15,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU-only hosts
     pytest.skip("no GPU", allow_module_level=True)
 
 import adapter_gemv_amd as lg  # noqa: E402  (raises if the HIP library is missing)
-from workloads.device import DeviceWorkload  # noqa: E402
+from workloads.device import DeviceWorkload, to_bits  # noqa: E402
 
 
 @pytest.fixture(autouse=True)
@@ -307,3 +307,28 @@ def test_long_segments_with_short_and_base_rows():
     w = bw(200, ids.size, len(lens), 4096, 2048, None, ids, ranks=ranks, x_std=1.0)
     for runner in ("split", "layer"):
         check_workload(w, oracle_all(w), runner)
+
+
+def test_prefill_phases_expand_twice():
+    # A prefill-sized batch (at least 2048 rows, ragged k-chunks): the layer
+    # expand only reads the shrink's k-chunk partials, so a second expand
+    # after the same shrink gives the same bits.
+    lens = [700, 1, 2, 300, 1, 5, 9, 1100, 1]
+    ids = np.concatenate([np.repeat(np.arange(len(lens)), lens), -np.ones(40, int)])
+    ids = np.random.default_rng(5).permutation(ids)
+    ranks = np.zeros((len(lens), 7), np.int32)
+    ranks[:, 0] = [64, 16, 8, 32, 64, 13, 40, 16, 64]
+    w = bw(300, ids.size, len(lens), 4104, 1032, None, ids, ranks=ranks, x_std=1.0)
+    assert w.num_rows >= 2048
+    ref = oracle_all(w)
+    dw = DeviceWorkload(w)
+    dw.build_segments()
+    lg.layer_shrink(dw.ios, w.num_rows, dw.table, w.num_slots, dw.seg, w.max_rank, dw.ws)
+    outs = []
+    for _ in range(2):
+        dw.reset_y(zero=True)
+        lg.layer_expand(dw.ios, w.num_rows, dw.table, w.num_slots, dw.seg, w.max_rank, dw.ws)
+        torch.cuda.synchronize()
+        outs.append(to_bits(dw.y["q"]))
+    assert np.array_equal(outs[0], outs[1])
+    check_rows(bf16_host(dw.y["q"]), ref["q"].delta, "prefill phases delta")
