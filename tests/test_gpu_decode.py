@@ -332,3 +332,27 @@ def test_prefill_phases_expand_twice():
         outs.append(to_bits(dw.y["q"]))
     assert np.array_equal(outs[0], outs[1])
     check_rows(bf16_host(dw.y["q"]), ref["q"].delta, "prefill phases delta")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "int8", "mixed"])
+def test_entry_lane_width_in_rank64_launch(fmt):
+    # One row per adapter, entries of many ranks in one launch of rank class
+    # 64: each expand item runs at the lane width of its own entry's rank
+    # (1, 2, 4 or 8 lanes per output row, fewer load passes at width 1), over
+    # whole and ragged n-tiles (d_out = 2 * 2048 + 8).
+    ranks_ = np.array([1, 3, 8, 9, 13, 16, 17, 24, 32, 33, 40, 57, 64, 8, 16, 32, 64], np.int32)
+    slots = ranks_.size
+    ids = np.random.default_rng(11).permutation(slots).astype(np.int32)
+    ranks = np.zeros((slots, 7), np.int32)
+    ranks[:, 0] = ranks_
+    if fmt == "bf16":
+        code = gen.FMT_BF16
+    elif fmt == "int8":
+        code = gen.FMT_INT8_ROWS
+    else:
+        code = np.where(np.arange(slots)[:, None] % 2 == 0, gen.FMT_INT8_ROWS, gen.FMT_BF16) * np.ones((1, 7), int)
+        code = code.astype(np.int32)
+    w = bw(400, slots, slots, 2056, 2 * 2048 + 8, None, ids, ranks=ranks, x_std=1.0, max_rank=64, fmt=code)
+    assert w.max_rank == 64
+    for runner in ("layer", "split"):
+        check_workload(w, oracle_all(w), runner)
