@@ -37,6 +37,20 @@ Nothing here is shared with the library's native former.
 from __future__ import annotations
 
 
+def _rank_groups(adapters, taken):
+    """The requests not yet taken, grouped by adapter (every base-only request
+    in the one group keyed -1), as records [size, oldest position, key,
+    members oldest first], ranked biggest first and, among equal sizes, by
+    their oldest member."""
+    members = {}
+    for i, a in enumerate(adapters):
+        if not taken[i]:
+            members.setdefault(a if a >= 0 else -1, []).append(i)
+    records = [[len(m), m[0], key, m] for key, m in members.items()]
+    records.sort(key=lambda r: (-r[0], r[1]))
+    return records
+
+
 def form_batch(adapters, max_batch, max_distinct, min_batch=0, reserved_tail=0,
                waited_ms=None, max_wait_ms=None):
     """Queue positions of the chosen requests, in batch order: urgent ones,
@@ -75,25 +89,24 @@ def form_batch(adapters, max_batch, max_distinct, min_batch=0, reserved_tail=0,
             take(i)
             tail += 1
 
-    # 3. Grouped fill over the rest: group by adapter (groups met in queue
-    #    order, members oldest first), biggest group first.
-    groups = {}
-    for i in range(n):
-        if not taken[i]:
-            key = adapters[i] if adapters[i] >= 0 else -1
-            groups.setdefault(key, []).append(i)
-    order = sorted(groups, key=lambda a: -len(groups[a]))  # stable: ties keep queue order
-    budget = max_distinct - tail
-    distinct = 0
-    for a in order:
-        if len(batch) >= max_batch:
+    # 3. Grouped fill.  Every group is ranked once; then each group in rank
+    #    order is admitted whole (cut only by the batch's capacity) while
+    #    there is room and either the fill still has adapter budget or the
+    #    batch is below its minimum size.  The base-only group spends no
+    #    budget.
+    adapter_budget = max_distinct - tail
+    adapters_admitted = 0
+    for size, oldest, key, members in _rank_groups(adapters, taken):
+        room = max_batch - len(batch)
+        if room <= 0:
             break
-        if distinct >= budget and len(batch) >= min_batch:
-            break  # no new adapters; the batch is big enough
-        for i in groups[a][: max_batch - len(batch)]:
+        budget_spent = adapters_admitted >= adapter_budget
+        big_enough = len(batch) >= min_batch
+        if budget_spent and big_enough:
+            break
+        for i in members[:min(size, room)]:
             take(i)
-        if a >= 0:
-            distinct += 1
+        adapters_admitted += 1 if key >= 0 else 0
     return batch
 
 

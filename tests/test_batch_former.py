@@ -126,12 +126,14 @@ def test_invariants_on_random_queues():
 
 SRC = open(bf.__file__).read()
 MUTATIONS = {
-    "smallest_group_first": ("sorted(groups, key=lambda a: -len(groups[a]))", "sorted(groups, key=lambda a: len(groups[a]))"),
+    "smallest_group_first": ("records.sort(key=lambda r: (-r[0], r[1]))", "records.sort(key=lambda r: (r[0], r[1]))"),
+    "newest_group_first_on_ties": ("records.sort(key=lambda r: (-r[0], r[1]))",
+                                   "records.sort(key=lambda r: (-r[0], -r[1]))"),
     "tail_takes_shared": ("count[adapters[i]] == 1", "count[adapters[i]] >= 1"),
-    "budget_ignores_tail": ("budget = max_distinct - tail", "budget = max_distinct"),
-    "no_min_batch": ("if distinct >= budget and len(batch) >= min_batch:", "if distinct >= budget:"),
-    "newest_first": ("for i in groups[a][: max_batch - len(batch)]:", "for i in groups[a][::-1][: max_batch - len(batch)]:"),
-    "base_only_counts": ("if a >= 0:\n            distinct += 1", "if True:\n            distinct += 1"),
+    "budget_ignores_tail": ("adapter_budget = max_distinct - tail", "adapter_budget = max_distinct"),
+    "no_min_batch": ("big_enough = len(batch) >= min_batch", "big_enough = True"),
+    "newest_first": ("for i in members[:min(size, room)]:", "for i in members[::-1][:min(size, room)]:"),
+    "base_only_counts": ("adapters_admitted += 1 if key >= 0 else 0", "adapters_admitted += 1"),
     "deadline_inclusive": ("if waited_ms[i] > max_wait_ms:", "if waited_ms[i] >= max_wait_ms:"),
     "tail_not_capped": ("if tail >= min(reserved_tail, max_distinct) or", "if tail >= reserved_tail or"),
 }
