@@ -18,13 +18,15 @@ import numpy as np
 
 __all__ = [
     "LoraError", "Segments", "segment_bound", "ModuleIO", "MODULES", "TABLE_ENTRY_DTYPE", "lib", "workspace_bytes",
-    "build_segments", "shrink", "expand", "apply_layer", "layer_shrink", "layer_expand", "pack_table",
+    "build_segments", "shrink", "expand", "apply_layer", "apply_layer_noalloc", "layer_shrink", "layer_expand",
+    "pack_table", "STATIC_SCRATCH_BYTES",
     "status_string", "MAX_RANK",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblora_gemv.so")
 MAX_RANK = 64
+STATIC_SCRATCH_BYTES = 16 << 20  # LORA_STATIC_SCRATCH_BYTES
 MODULES = ("q", "k", "v", "o", "gate", "up", "down")
 
 # lora_adapter_entry_t, 32 bytes
@@ -81,6 +83,8 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.restype = st
             f.argtypes = [ctypes.POINTER(_IO), u32, i32, vp, i32, _Seg, i32, vp, sz, vp]
+        L.lora_apply_layer_noalloc.restype = st
+        L.lora_apply_layer_noalloc.argtypes = [ctypes.POINTER(_IO), u32, i32, vp, i32, _Seg, i32, vp]
         L.lora_apply_layer_stacked.restype = st
         L.lora_apply_layer_stacked.argtypes = [ctypes.POINTER(_IO), u32, i32, vp, i32, vp, vp, i32, _Seg, i32, vp, sz,
                                                vp]
@@ -314,6 +318,16 @@ def apply_layer(ios, num_rows, table, num_slots, seg, max_rank, ws, stream=None,
     """Delta of every projection given in ``ios`` ({name: ModuleIO}); see lora_apply_layer."""
     _layer(lib().lora_apply_layer, "lora_apply_layer", ios, num_rows, table, num_slots, seg, max_rank, ws, stream,
            module_mask)
+
+
+def apply_layer_noalloc(ios, num_rows, table, num_slots, seg, max_rank, stream=None, module_mask=None):
+    """apply_layer with the library's static device scratch instead of a
+    workspace (allocates nothing); see lora_apply_layer_noalloc."""
+    arr, mask = _ios(ios, num_rows)
+    if module_mask is None:
+        module_mask = mask
+    _check(lib().lora_apply_layer_noalloc(arr, module_mask, num_rows, _ptr(table), num_slots, seg.c(), max_rank,
+                                          _stream(stream)), "lora_apply_layer_noalloc")
 
 
 def layer_shrink(ios, num_rows, table, num_slots, seg, max_rank, ws, stream=None, module_mask=None):

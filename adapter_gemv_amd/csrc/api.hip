@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "lora_internal.h"
 
 using namespace lora;
@@ -243,6 +245,8 @@ const char *lora_status_string(lora_status_t status) {
     case LORA_ERR_WORKSPACE: return "LORA_ERR_WORKSPACE: workspace too small";
     case LORA_ERR_MODULE: return "LORA_ERR_MODULE: bad module index, n_mod or module mask";
     case LORA_ERR_LAUNCH: return "LORA_ERR_LAUNCH: kernel launch failed";
+    case LORA_ERR_SCRATCH:
+      return "LORA_ERR_SCRATCH: the call needs more scratch than LORA_STATIC_SCRATCH_BYTES";
   }
   return "unknown lora_status_t";
 }
@@ -481,3 +485,55 @@ lora_status_t lora_linear_expand(const lora_linear_io_t *io, uint32_t module_mas
 }
 
 }  // extern "C"
+
+// ---- lora_apply_layer_noalloc: the k-chunk partials in a static device
+// array instead of a caller's workspace.  Each device that loads the library
+// holds its own copy until the process ends; in host code `scratch` is only
+// a handle, so its device address is looked up once per device and every
+// launch takes that address.
+static __device__ __align__(256) uint8_t scratch[LORA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices];  // device address of `scratch`, per device
+
+// The address of the current device's `scratch` (looked up on the first call
+// on that device, with it current).
+lora_status_t scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LORA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return LORA_ERR_LAUNCH;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" lora_status_t lora_apply_layer_noalloc(const lora_module_io_t *io, uint32_t module_mask,
+                                                  int32_t num_rows, const lora_adapter_entry_t *table,
+                                                  int32_t num_slots, lora_segments_t seg, int32_t max_rank,
+                                                  void *stream) {
+  ModuleArgs ms[LORA_NUM_MODULES];
+  int n = 0;
+  // the argument checks of lora_apply_layer, with the static array as an
+  // aligned workspace of its full size
+  lora_status_t st = check_layer(io, module_mask, num_rows, table, num_slots, seg, max_rank,
+                                 reinterpret_cast<void *>(uintptr_t{256}), LORA_STATIC_SCRATCH_BYTES, ms, &n);
+  if (st == LORA_ERR_WORKSPACE) return LORA_ERR_SCRATCH;
+  if (st != LORA_OK) return st;
+  if (num_rows == 0) return LORA_OK;
+  void *ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != LORA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launch_phase(true, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
+  if (st != LORA_OK) return st;
+  return launch_phase(false, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
+}

@@ -35,7 +35,9 @@
  *  - Every pointer argument marked "device" is device memory owned by the
  *    caller.  The library allocates no device memory, keeps no pointer after
  *    a call returns and has no global state; it is reentrant.  (The host-only
- *    lora_form_batch uses temporary host memory, freed before it returns.)
+ *    lora_form_batch uses temporary host memory, freed before it returns.
+ *    The one exception is lora_apply_layer_noalloc, which works in a static
+ *    device array of the library and caches its address per device.)
  *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
  *    enqueues work on it and returns; nothing synchronises the host.  Buffers
  *    must stay alive until the stream has passed the call.  No call
@@ -88,7 +90,10 @@ typedef enum lora_status {
                               aligned, or a dimension is not a multiple of 8  */
   LORA_ERR_WORKSPACE = 5,  /* ws_bytes < lora_workspace_bytes(...)            */
   LORA_ERR_MODULE = 6,     /* bad module index, n_mod or module mask          */
-  LORA_ERR_LAUNCH = 7      /* the HIP runtime refused a kernel launch         */
+  LORA_ERR_LAUNCH = 7,     /* the HIP runtime refused a kernel launch, or the
+                              device or its static scratch could not be found */
+  LORA_ERR_SCRATCH = 8     /* the call needs more than LORA_STATIC_SCRATCH_BYTES
+                              of scratch (lora_apply_layer_noalloc)           */
 } lora_status_t;
 
 /*
@@ -472,6 +477,34 @@ lora_status_t lora_form_batch(const int32_t *adapters, int32_t queue_len,
                               int32_t max_batch, int32_t max_distinct,
                               int32_t min_batch, int32_t reserved_tail,
                               int32_t *out_index, int32_t *out_count);
+
+/* Size of the static device array that lora_apply_layer_noalloc uses as its
+ * workspace (16 MiB on every device the library runs on, held until the
+ * process ends). */
+#define LORA_STATIC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * lora_apply_layer_noalloc -- lora_apply_layer without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  The
+ * k-chunk partials go to a static device array of LORA_STATIC_SCRATCH_BYTES
+ * instead; the call itself allocates nothing.  Same arguments (less ws and
+ * ws_bytes), same kernels, same results and the same errors as
+ * lora_apply_layer, except that a call whose workspace would exceed
+ * LORA_STATIC_SCRATCH_BYTES (lora_workspace_bytes with these sizes) returns
+ * LORA_ERR_SCRATCH and enqueues nothing.  At 128 rows and rank 64 the array
+ * holds every projection of the 70B layer (2.7 MB).
+ * The array is per device and shared by every call on that device: calls
+ * that may overlap on one device (other streams, other host threads) race
+ * on it and must be ordered by the caller.  Nothing in it needs to start at
+ * zero; a call leaves its partials there.  The first call on a device looks
+ * up the array's device address (with that device current) and keeps it;
+ * LORA_ERR_LAUNCH if the lookup fails.
+ */
+lora_status_t lora_apply_layer_noalloc(const lora_module_io_t *io, uint32_t module_mask,
+                                       int32_t num_rows, const lora_adapter_entry_t *table,
+                                       int32_t num_slots, lora_segments_t seg, int32_t max_rank,
+                                       void *stream);
 
 /* A static, human-readable name for a status code. */
 const char *lora_status_string(lora_status_t status);

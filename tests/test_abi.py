@@ -13,7 +13,7 @@ import pytest
 import adapter_gemv_amd as lg
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "lora_gemv.h")
-OK, NULL, SHAPE, RANK, ALIGN, WS, MODULE, LAUNCH = range(8)
+OK, NULL, SHAPE, RANK, ALIGN, WS, MODULE, LAUNCH, SCRATCH = range(9)
 P = 0x10000          # an aligned fake device address (never dereferenced)
 BIG = 1 << 40
 
@@ -43,7 +43,7 @@ def seg(**kw):
 
 
 def test_status_strings():
-    for c in range(8):
+    for c in range(9):
         s = lg.status_string(c)
         assert s.startswith("LORA_")
     assert "unknown" in lg.status_string(99)
@@ -143,6 +143,24 @@ def test_layer_rejects(fn, args, code):
     f = getattr(lg.lib(), fn)
     assert f(a["io"], a["mask"], a["n"], a["table"], a["slots"], a["seg"], a["max_rank"], a["ws"], a["ws_bytes"],
              None) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(io=None), NULL), (dict(table=None), NULL), (dict(seg=seg(status=None)), NULL),
+    (dict(mask=0), MODULE), (dict(n=-1), SHAPE), (dict(max_rank=65), RANK),
+    (dict(io=ios(**{"4_y": P + 2})), ALIGN),
+    # the partials of 128 rows at rank 64 over all seven 70B projections fit the static scratch;
+    # 2048 rows do not (LORA_ERR_SCRATCH before any device work)
+    (dict(n=2048), SCRATCH),
+])
+def test_noalloc_rejects(args, code):
+    a = dict(io=ios(), mask=0x7F, n=128, table=P, slots=128, seg=seg(), max_rank=64)
+    a.update(args)
+    L = lg.lib()
+    assert L.lora_workspace_bytes(128, 128, 64, 7 * 8192) <= lg.STATIC_SCRATCH_BYTES
+    assert L.lora_workspace_bytes(2048, 128, 64, 7 * 8192) > lg.STATIC_SCRATCH_BYTES
+    assert L.lora_apply_layer_noalloc(a["io"], a["mask"], a["n"], a["table"], a["slots"], a["seg"], a["max_rank"],
+                                      None) == code
 
 
 def test_masked_out_modules_are_not_checked():
