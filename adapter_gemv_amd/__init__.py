@@ -18,8 +18,8 @@ import numpy as np
 
 __all__ = [
     "LoraError", "Segments", "segment_bound", "ModuleIO", "MODULES", "TABLE_ENTRY_DTYPE", "lib", "workspace_bytes",
-    "build_segments", "shrink", "expand", "apply_layer", "apply_layer_noalloc", "layer_shrink", "layer_expand",
-    "pack_table", "STATIC_SCRATCH_BYTES",
+    "build_segments", "shrink", "expand", "apply_layer", "apply_layer_noalloc", "decode_layer",
+    "decode_layer_launches", "layer_shrink", "layer_expand", "pack_table", "STATIC_SCRATCH_BYTES",
     "status_string", "MAX_RANK",
 ]
 
@@ -83,6 +83,10 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.restype = st
             f.argtypes = [ctypes.POINTER(_IO), u32, i32, vp, i32, _Seg, i32, vp, sz, vp]
+        L.lora_decode_layer.restype = st
+        L.lora_decode_layer.argtypes = [ctypes.POINTER(_IO), u32, i32, vp, vp, i32, _Seg, i32, vp, sz, vp]
+        L.lora_decode_layer_launches.restype = i32
+        L.lora_decode_layer_launches.argtypes = [ctypes.POINTER(_IO), u32, i32, i32, _Seg, i32]
         L.lora_apply_layer_noalloc.restype = st
         L.lora_apply_layer_noalloc.argtypes = [ctypes.POINTER(_IO), u32, i32, vp, i32, _Seg, i32, vp]
         L.lora_apply_layer_stacked.restype = st
@@ -318,6 +322,28 @@ def apply_layer(ios, num_rows, table, num_slots, seg, max_rank, ws, stream=None,
     """Delta of every projection given in ``ios`` ({name: ModuleIO}); see lora_apply_layer."""
     _layer(lib().lora_apply_layer, "lora_apply_layer", ios, num_rows, table, num_slots, seg, max_rank, ws, stream,
            module_mask)
+
+
+def decode_layer(ios, num_rows, row_adapter, table, num_slots, seg, max_rank, ws, stream=None, module_mask=None):
+    """Segments and the layer delta of a decode batch (one launch for a batch
+    of distinct adapters); see lora_decode_layer."""
+    import torch
+    _need(row_adapter, torch.int32, "row_adapter", 1)
+    if row_adapter.shape[0] < num_rows:
+        raise ValueError("row_adapter: fewer ids than num_rows")
+    arr, mask = _ios(ios, num_rows)
+    if module_mask is None:
+        module_mask = mask
+    _check(lib().lora_decode_layer(arr, module_mask, num_rows, _ptr(row_adapter), _ptr(table), num_slots, seg.c(),
+                                   max_rank, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "lora_decode_layer")
+
+
+def decode_layer_launches(ios, num_rows, num_slots, seg, max_rank, module_mask=None) -> int:
+    """Kernel launches lora_decode_layer makes for these arguments (1 or 3; 0 if it would reject them)."""
+    arr, mask = _ios(ios, num_rows)
+    return int(lib().lora_decode_layer_launches(arr, mask if module_mask is None else module_mask, num_rows,
+                                                num_slots, seg.c(), max_rank))
 
 
 def apply_layer_noalloc(ios, num_rows, table, num_slots, seg, max_rank, stream=None, module_mask=None):

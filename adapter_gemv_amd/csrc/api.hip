@@ -35,6 +35,18 @@ size_t ws_need(int num_rows, int num_slots, int max_rank, int64_t sum_d_in) {  /
   return a > b ? a : b;
 }
 
+// The workspace checks of a call whose own scratch is `need` bytes (0: the
+// call needs no workspace and *scratch is null).
+lora_status_t check_ws(void *ws, size_t ws_bytes, size_t need, void **scratch) {
+  *scratch = nullptr;
+  if (need == 0) return LORA_OK;
+  if (!ws) return LORA_ERR_NULL;
+  if (!aligned16(ws)) return LORA_ERR_ALIGN;
+  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
+  *scratch = ws;
+  return LORA_OK;
+}
+
 struct ModuleArgs {
   const void *x;
   int64_t ldx;
@@ -152,6 +164,9 @@ lora_status_t launch_phase(bool shrink, const ModuleArgs *ms, int n, int num_row
   fill_desc(d, ms, n, shrink, num_rows, num_slots, max_rank, table_cols, table, seg, ws);
   d.v = v_in;
   d.ldv = ldv;
+  // a call counts each bad segment and entry once: the shrink of a layer call,
+  // or lora_expand on the caller's v
+  d.count_errors = shrink || v_in != nullptr;
   const int64_t dec = (int64_t)d.max_seg * d.items_per_seg;
   int64_t sg = 0;
   if (num_rows >= kLongSegRows)
@@ -165,7 +180,8 @@ lora_status_t launch_phase(bool shrink, const ModuleArgs *ms, int n, int num_row
 // Common checks of the layer calls; fills the module list.
 lora_status_t check_layer(const lora_module_io_t *io, uint32_t module_mask, int32_t num_rows,
                           const lora_adapter_entry_t *table, int32_t num_slots, const lora_segments_t &seg,
-                          int32_t max_rank, void *ws, size_t ws_bytes, ModuleArgs *ms, int *n_out) {
+                          int32_t max_rank, void *ws, size_t ws_bytes, ModuleArgs *ms, int *n_out,
+                          void **scratch, int64_t *sum_d_in_out = nullptr) {
   if (!io || !table) return LORA_ERR_NULL;
   lora_status_t st = check_segments(seg);
   if (st != LORA_OK) return st;
@@ -186,11 +202,10 @@ lora_status_t check_layer(const lora_module_io_t *io, uint32_t module_mask, int3
     sum_d_in += m.d_in;
     ++n;
   }
-  const size_t need = partials_ws_bytes(num_rows, max_rank, sum_d_in);
-  if (need > 0 && !ws) return LORA_ERR_NULL;
-  if (need > 0 && !aligned16(ws)) return LORA_ERR_ALIGN;
-  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
+  st = check_ws(ws, ws_bytes, partials_ws_bytes(num_rows, max_rank, sum_d_in), scratch);
+  if (st != LORA_OK) return st;
   *n_out = n;
+  if (sum_d_in_out) *sum_d_in_out = sum_d_in;
   return LORA_OK;
 }
 
@@ -199,9 +214,12 @@ lora_status_t layer_phase(bool do_shrink, bool do_expand, const lora_module_io_t
                           lora_segments_t seg, int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
   ModuleArgs ms[LORA_NUM_MODULES];
   int n = 0;
-  lora_status_t st = check_layer(io, module_mask, num_rows, table, num_slots, seg, max_rank, ws, ws_bytes, ms, &n);
+  void *scratch = nullptr;
+  lora_status_t st =
+      check_layer(io, module_mask, num_rows, table, num_slots, seg, max_rank, ws, ws_bytes, ms, &n, &scratch);
   if (st != LORA_OK) return st;
   if (num_rows == 0) return LORA_OK;
+  ws = scratch;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (do_shrink) {
     st = launch_phase(true, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
@@ -257,12 +275,11 @@ lora_status_t lora_build_segments(const int32_t *row_adapter, int32_t num_rows, 
   if (st != LORA_OK) return st;
   if (num_rows < 0 || num_slots < 1) return LORA_ERR_SHAPE;
   if (num_rows > 0 && !row_adapter) return LORA_ERR_NULL;
-  const size_t need = segments_ws_bytes(num_rows, num_slots);
-  if (need > 0 && !ws) return LORA_ERR_NULL;
-  if (need > 0 && !aligned16(ws)) return LORA_ERR_ALIGN;
-  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
-  return launched(
-      launch_build_segments(row_adapter, 1, num_rows, num_slots, false, seg, ws, static_cast<hipStream_t>(stream)));
+  void *scratch = nullptr;
+  st = check_ws(ws, ws_bytes, segments_ws_bytes(num_rows, num_slots), &scratch);
+  if (st != LORA_OK) return st;
+  return launched(launch_build_segments(row_adapter, 1, num_rows, num_slots, false, seg, scratch,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 lora_status_t lora_shrink(const void *x, int64_t ldx, int32_t num_rows, int32_t d_in,
@@ -277,11 +294,11 @@ lora_status_t lora_shrink(const void *x, int64_t ldx, int32_t num_rows, int32_t 
   if (num_rows < 0 || num_slots < 1 || d_in <= 0 || ldx < d_in || ldv < max_rank) return LORA_ERR_SHAPE;
   if ((d_in & 7) || (ldx & 7) || (ldv & 3) || !aligned16(x) || !aligned16(v)) return LORA_ERR_ALIGN;
   if (!fits_u32(num_rows, ldx)) return LORA_ERR_SHAPE;
-  const size_t need = partials_ws_bytes(num_rows, max_rank, d_in);
-  if (need > 0 && !ws) return LORA_ERR_NULL;
-  if (need > 0 && !aligned16(ws)) return LORA_ERR_ALIGN;
-  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
+  void *scratch = nullptr;
+  st = check_ws(ws, ws_bytes, partials_ws_bytes(num_rows, max_rank, d_in), &scratch);
+  if (st != LORA_OK) return st;
   if (num_rows == 0) return LORA_OK;
+  ws = scratch;
   ModuleArgs m{x, ldx, nullptr, 0, d_in, 0, module};
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = launch_phase(true, &m, 1, num_rows, num_slots, max_rank, n_mod, table, seg, ws, nullptr, 0, s);
@@ -331,6 +348,124 @@ lora_status_t lora_apply_layer(const lora_module_io_t *io, uint32_t module_mask,
   return layer_phase(true, true, io, module_mask, num_rows, table, num_slots, seg, max_rank, ws, ws_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// The one-launch plan of lora_decode_layer.  Each block of the one-launch
+// kernel reads the whole A of its segment (its siblings, one per expand
+// tile, read the same lines through L2), so the plan bounds those repeated
+// reads: at most kOnePassRepeatBytes over all projections, counting one pass
+// over A per segment and one more per 4 further rows (segments are at most
+// the caller's bound, else one per row).  Measured on one MI355X with
+// distinct adapters per row: the launch is 2-3x faster than the three
+// launches of lora_build_segments + lora_apply_layer below about 150 MB of
+// repeated reads, even at 268 MB, and slower from 537 MB.  Batches of at most
+// kOnePassMaxRows rows, ranks up to 32.  False for any other batch.
+constexpr double kOnePassRepeatBytes = 320.0 * (1 << 20);
+
+bool onepass_plan(const ModuleArgs *ms, int n, int num_rows, const int32_t *ids, int num_slots, int max_rank,
+                  const lora_adapter_entry_t *table, const lora_segments_t &seg, OnePassDesc *od, int *grid) {
+  if (num_rows < 1 || num_rows > kOnePassMaxRows || max_rank > 32) return false;
+  const int lpr = max_rank <= 8 ? 1 : max_rank <= 16 ? 2 : 4;
+  const int nt = kOnePassPasses * (kDecodeThreads / lpr);
+  const int max_seg = segment_bound(num_rows, num_slots, seg);
+  // a bound below min(rows, slots) may drop segments: each block then ranks its slot in a bitmap of the slots
+  const bool bound_check = max_seg < (num_rows < num_slots ? num_rows : num_slots);
+  if (bound_check && num_slots > kOnePassMaxSlots) return false;
+  const double passes = max_seg + (num_rows - max_seg + 3) / 4;
+  double repeat = 0;
+  for (int i = 0; i < n; ++i)
+    repeat += (double)((ms[i].d_out + nt - 1) / nt) * ms[i].d_in * (8 * lpr) * 2 * passes;
+  if (repeat > kOnePassRepeatBytes) return false;
+  *od = OnePassDesc{};
+  LayerDesc &d = od->L;
+  d.nt = nt;
+  int item = 0;
+  for (int i = 0; i < n; ++i) {
+    ModuleDesc &m = d.mod[i];
+    m.x = static_cast<const uint16_t *>(ms[i].x);
+    m.ldx = ms[i].ldx;
+    m.y = static_cast<uint16_t *>(ms[i].y);
+    m.ldy = ms[i].ldy;
+    m.d_in = ms[i].d_in;
+    m.d_out = ms[i].d_out;
+    m.col = ms[i].col;
+    m.op_nt = nt;
+    m.op_n_tiles = (m.d_out + nt - 1) / nt;
+    m.n_items = m.op_n_tiles;
+    m.item_base = item;
+    item += m.op_n_tiles;
+  }
+  d.n_active = n;
+  d.items_per_seg = item;
+  d.table_cols = LORA_NUM_MODULES;
+  d.num_rows = num_rows;
+  d.num_slots = num_slots;
+  d.max_rank = max_rank;
+  d.long_min = 0x7fffffff;
+  d.max_seg = segment_bound(num_rows, num_slots, seg);
+  d.status = seg.status;
+  d.table = table;
+  od->seg = seg;
+  od->ids = ids;
+  od->row_slots = (num_rows + 7) / 8 * 8;
+  od->bound_check = bound_check;
+  const int64_t blocks = (int64_t)item * od->row_slots + 1;
+  if (blocks > 0x7fffffff) return false;
+  *grid = (int)blocks;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Segments and the layer delta of a decode batch: one launch when the batch
+// fits the one-launch kernel, else lora_build_segments + lora_apply_layer.
+lora_status_t lora_decode_layer(const lora_module_io_t *io, uint32_t module_mask, int32_t num_rows,
+                                const int32_t *row_adapter, const lora_adapter_entry_t *table, int32_t num_slots,
+                                lora_segments_t seg, int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
+  ModuleArgs ms[LORA_NUM_MODULES];
+  int n = 0;
+  void *scratch = nullptr;
+  lora_status_t st =
+      check_layer(io, module_mask, num_rows, table, num_slots, seg, max_rank, ws, ws_bytes, ms, &n, &scratch);
+  if (st != LORA_OK) return st;
+  if (num_rows > 0 && !row_adapter) return LORA_ERR_NULL;
+  void *seg_scratch = nullptr;
+  st = check_ws(ws, ws_bytes, segments_ws_bytes(num_rows, num_slots), &seg_scratch);
+  if (st != LORA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  OnePassDesc od;
+  int grid = 0;
+  if (onepass_plan(ms, n, num_rows, row_adapter, num_slots, max_rank, table, seg, &od, &grid))
+    return launched(launch_onepass(od, grid, s));
+  st = launched(launch_build_segments(row_adapter, 1, num_rows, num_slots, false, seg, seg_scratch, s));
+  if (st != LORA_OK || num_rows == 0) return st;
+  // the three-launch path
+  st = launch_phase(true, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, scratch, nullptr, 0, s);
+  if (st != LORA_OK) return st;
+  return launch_phase(false, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, scratch, nullptr, 0,
+                      s);
+}
+
+int32_t lora_decode_layer_launches(const lora_module_io_t *io, uint32_t module_mask, int32_t num_rows,
+                                   int32_t num_slots, lora_segments_t seg, int32_t max_rank) {
+  ModuleArgs ms[LORA_NUM_MODULES];
+  int n = 0;
+  void *scratch = nullptr;
+  // the argument checks without a workspace (an aligned stand-in of any size)
+  const lora_adapter_entry_t *table = reinterpret_cast<const lora_adapter_entry_t *>(uintptr_t{256});
+  if (check_layer(io, module_mask, num_rows, table, num_slots, seg, max_rank, reinterpret_cast<void *>(uintptr_t{256}),
+                  ~size_t{0} >> 1, ms, &n, &scratch) != LORA_OK)
+    return 0;
+  OnePassDesc od;
+  int grid = 0;
+  const int32_t *ids = reinterpret_cast<const int32_t *>(uintptr_t{256});
+  return onepass_plan(ms, n, num_rows, ids, num_slots, max_rank, table, seg, &od, &grid) ? 1 : 3;
+}
+
 // One pass per position of the rows' adapter lists: the segments of that
 // column, then the layer's shrink and expand, each pass adding its delta to y
 // in stream order (a row is in one segment per pass, so no two blocks of a
@@ -341,17 +476,19 @@ lora_status_t lora_apply_layer_stacked(const lora_module_io_t *io, uint32_t modu
                                        int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
   ModuleArgs ms[LORA_NUM_MODULES];
   int n = 0;
-  lora_status_t st = check_layer(io, module_mask, num_rows, table, num_slots, seg, max_rank, ws, ws_bytes, ms, &n);
+  void *scratch = nullptr;
+  lora_status_t st =
+      check_layer(io, module_mask, num_rows, table, num_slots, seg, max_rank, ws, ws_bytes, ms, &n, &scratch);
   if (st != LORA_OK) return st;
   if (depth < 1 || depth > LORA_MAX_STACK) return LORA_ERR_SHAPE;
   if (num_rows > 0 && !row_adapters) return LORA_ERR_NULL;
   if (pass_max_rank)
     for (int t = 0; t < depth; ++t)
       if (pass_max_rank[t] < 1 || pass_max_rank[t] > max_rank) return LORA_ERR_RANK;
-  const size_t need = segments_ws_bytes(num_rows, num_slots);
-  if (need > 0 && !ws) return LORA_ERR_NULL;
-  if (need > 0 && !aligned16(ws)) return LORA_ERR_ALIGN;
-  if (ws_bytes < need) return LORA_ERR_WORKSPACE;
+  void *seg_scratch = nullptr;
+  st = check_ws(ws, ws_bytes, segments_ws_bytes(num_rows, num_slots), &seg_scratch);
+  if (st != LORA_OK) return st;
+  ws = scratch ? scratch : seg_scratch;
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int t = 0; t < depth; ++t) {
     st = launched(launch_build_segments(row_adapters + t, depth, num_rows, num_slots, t > 0, seg, ws, s));
@@ -524,8 +661,9 @@ extern "C" lora_status_t lora_apply_layer_noalloc(const lora_module_io_t *io, ui
   int n = 0;
   // the argument checks of lora_apply_layer, with the static array as an
   // aligned workspace of its full size
+  void *unused = nullptr;
   lora_status_t st = check_layer(io, module_mask, num_rows, table, num_slots, seg, max_rank,
-                                 reinterpret_cast<void *>(uintptr_t{256}), LORA_STATIC_SCRATCH_BYTES, ms, &n);
+                                 reinterpret_cast<void *>(uintptr_t{256}), LORA_STATIC_SCRATCH_BYTES, ms, &n, &unused);
   if (st == LORA_ERR_WORKSPACE) return LORA_ERR_SCRATCH;
   if (st != LORA_OK) return st;
   if (num_rows == 0) return LORA_OK;

@@ -46,9 +46,10 @@ namespace lora {
 // the chunk's sum.  int8 rows are padded to 16 bytes, so the load stays in
 // its row; where d_in ends inside it, the second x piece lies past the row
 // of x and reads zero, and the padding bytes (always finite) add nothing.
-template <int JW, int RG, bool Q8>
+// row_of(r) gives the original row of sorted position pos0 + r.
+template <int JW, int RG, bool Q8, typename RowOf>
 __device__ __forceinline__ void decode_shrink_rows(const LayerDesc &d, const ModuleDesc &m, const void *A, int rank,
-                                                   int jw, int pos0, int nrows, int chunk) {
+                                                   int jw, int pos0, int nrows, int chunk, RowOf row_of) {
   constexpr int VPL = Q8 ? 16 : 8;  // k per lane and step
   const int lane = threadIdx.x & 63;
   const int j0 = wave_id() * jw;
@@ -59,7 +60,7 @@ __device__ __forceinline__ void decode_shrink_rows(const LayerDesc &d, const Mod
   rsrc_t rx[RG];
 #pragma unroll
   for (int r = 0; r < RG; ++r) {
-    const int b = r < nrows ? uniform(d.perm[pos0 + r]) : 0;
+    const int b = r < nrows ? uniform(row_of(r)) : 0;
     const bool ok = (unsigned)b < (unsigned)d.num_rows;  // a stray index reads zeros
     rx[r] = make_rsrc(m.x + (int64_t)(ok ? b : 0) * m.ldx, ok ? row_bytes : 0u);
   }
@@ -133,19 +134,22 @@ __device__ __forceinline__ void decode_shrink_block(const LayerDesc &d, int blk,
   const ModuleDesc m = module_of_item(d, it);
   const int chunk = it - m.item_base;
   int a, pos0, len;
-  if (!load_segment(d, s, it == 0, &a, &pos0, &len)) return;
+  if (!load_segment(d, s, it == 0 && d.count_errors, &a, &pos0, &len)) return;
   if (len >= d.long_min) return;  // an SGMV item takes this segment
   lora_adapter_entry_t e;
-  if (!load_entry(d, a, m.col, chunk == 0, &e)) return;
+  if (!load_entry(d, a, m.col, chunk == 0 && d.count_errors, &e)) return;
   const int rank = e.rank;
   const int jw = (rank + 3) >> 2;
   auto run = [&](auto q8) {
     constexpr bool Q8 = decltype(q8)::value;
     if (len == 1) {
-      decode_shrink_rows<JW, 1, Q8>(d, m, e.A, rank, jw, pos0, 1, chunk);
+      decode_shrink_rows<JW, 1, Q8>(d, m, e.A, rank, jw, pos0, 1, chunk, [&](int r) { return d.perm[pos0 + r]; });
     } else {
-      for (int r0 = 0; r0 < len; r0 += RGM)
-        decode_shrink_rows<JW, RGM, Q8>(d, m, e.A, rank, jw, pos0 + r0, min(RGM, len - r0), chunk);
+      for (int r0 = 0; r0 < len; r0 += RGM) {
+        const int p = pos0 + r0;
+        decode_shrink_rows<JW, RGM, Q8>(d, m, e.A, rank, jw, p, min(RGM, len - r0), chunk,
+                                        [&](int r) { return d.perm[p + r]; });
+      }
     }
   };
   if (e.format == LORA_FORMAT_INT8_ROWS) run(std::true_type{});
@@ -417,10 +421,10 @@ __device__ __forceinline__ void decode_expand_block(const LayerDesc &d, int blk,
   const ModuleDesc m = module_of_item(d, it);
   const int tile = it - m.item_base;
   int a, pos0, len;
-  if (!load_segment(d, s, it == 0, &a, &pos0, &len)) return;
+  if (!load_segment(d, s, it == 0 && d.count_errors, &a, &pos0, &len)) return;
   if (len >= d.long_min) return;  // an SGMV item takes this segment
   lora_adapter_entry_t e;
-  if (!load_entry(d, a, m.col, tile == 0, &e)) return;
+  if (!load_entry(d, a, m.col, tile == 0 && d.count_errors, &e)) return;
   constexpr int NTC = decode_expand_tile(LPR);
   auto run = [&](auto q8, auto lw) {
     constexpr bool Q8 = decltype(q8)::value;

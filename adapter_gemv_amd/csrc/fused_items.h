@@ -200,9 +200,7 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
     e.rank = __builtin_amdgcn_readlane(my_e.rank, i);
     e.scale = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_e.scale), i));
     e.format = __builtin_amdgcn_readlane(my_e.format, i);
-    ri.ok = valid && ri.b < f.num_rows && entry_ok(e, f.max_rank);
-    if (valid && ri.b < f.num_rows && e.rank != 0 && !ri.ok && tile == 0 && lane == 0)
-      atomicAdd(f.status, 1);  // a malformed entry, counted by the first column tile
+    ri.ok = valid && ri.b < f.num_rows && entry_ok(e, f.max_rank);  // a malformed entry: counted by the shrink
     ri.rank = e.rank;
     ri.fmt = e.format;
     ri.scale = e.scale;

@@ -6,6 +6,7 @@
 // the register tiling of both paths.
 #include "decode_items.h"
 #include "fused_items.h"
+#include "onepass_items.h"
 #include "sgmv_items.h"
 
 namespace lora {
@@ -101,6 +102,43 @@ __global__ __launch_bounds__(256) void shrink_reduce_kernel(LayerDesc d) {
   if ((unsigned)b < (unsigned)d.num_rows) v_out[(int64_t)b * d.ldv + j] = sum;
 }
 
+// One-launch decode (onepass_items.h): block 0 writes the segments; blocks
+// 1.. are (item, row), item-major over row_slots (a multiple of 8) rows, so
+// the blocks of one row share an XCD when blocks are dealt to the XCDs in
+// turn.  Waves per SIMD: 4 up to rank class 16, 3 for 32.
+template <int CLS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CLS <= 1 ? 4 : 3))) void lora_onepass_kernel(
+    OnePassDesc od) {
+  __shared__ __align__(16) uint8_t lds[kOnePassLdsBytes];
+  if (blockIdx.x == 0) {
+    op_build(od, lds);
+    return;
+  }
+  const LayerDesc &d = od.L;
+  const int R = od.row_slots;
+  const int b = (int)blockIdx.x - 1;
+  const int it = b / R, t = b - it * R;
+  if (t >= d.num_rows) return;
+  const ModuleDesc m = module_of_item(d, it);
+  const int c = it - m.item_base;
+  // every row's id, for the ballots and the slot rank (-1: past the batch, base only or a bad id)
+  const int raw_id = (int)threadIdx.x < d.num_rows ? od.ids[threadIdx.x] : -1;
+  const int idu = (unsigned)raw_id < (unsigned)d.num_slots ? raw_id : -1;
+  const int a = uniform(od.ids[t]);
+  if ((unsigned)a >= (unsigned)d.num_slots) return;  // base only, or a bad id (the last block counts it)
+  const lora_adapter_entry_t raw = d.table[(int64_t)a * d.table_cols + m.col];
+  lora_adapter_entry_t e;
+  e.A = uniform(raw.A);
+  e.B = uniform(raw.B);
+  e.rank = uniform(raw.rank);
+  e.scale = uniform(raw.scale);
+  e.format = uniform(raw.format);
+  e.reserved = 0;
+  if (!entry_ok(e, d.max_rank)) return;  // rank 0, or an entry the last block counts
+  if (e.format == LORA_FORMAT_INT8_ROWS) op_delta<CLS, true>(m, e, c, t, a, idu, od.bound_check, d.max_seg, lds);
+  else op_delta<CLS, false>(m, e, c, t, a, idu, od.bound_check, d.max_seg, lds);
+}
+
 // Base projection + delta (fused_items.h).
 __global__ __launch_bounds__(256) void lora_fused_kernel(FusedDesc f) {
   __shared__ __align__(16) uint8_t lds[kFusedLdsBytes];
@@ -144,6 +182,17 @@ hipError_t launch_shrink_reduce(const LayerDesc &d, hipStream_t stream) {
   const int64_t total = (int64_t)d.num_rows * d.max_rank;
   if (total <= 0) return hipSuccess;
   shrink_reduce_kernel<<<dim3((unsigned)((total + 255) / 256), (unsigned)d.n_active), 256, 0, stream>>>(d);
+  return hipGetLastError();
+}
+
+hipError_t launch_onepass(const OnePassDesc &d, int grid, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  switch (rank_class(d.L.max_rank)) {
+    case 0: lora_onepass_kernel<0><<<grid, 256, 0, stream>>>(d); break;
+    case 1: lora_onepass_kernel<1><<<grid, 256, 0, stream>>>(d); break;
+    case 2: lora_onepass_kernel<2><<<grid, 256, 0, stream>>>(d); break;
+    default: return hipErrorInvalidValue;  // the host plans the one-launch path up to rank 32 only
+  }
   return hipGetLastError();
 }
 

@@ -61,6 +61,8 @@ struct ModuleDesc {
   int32_t n_chunks;   // k-chunks of this module
   int32_t sg_item_base;  // first SGMV expand item (n-tile) of this module in a row tile
   int32_t sg_n_items;    // SGMV expand n-tiles of this module
+  int32_t op_nt;         // one-launch decode: outputs per expand tile
+  int32_t op_n_tiles;    // one-launch decode: expand tiles of this module
 };
 
 // Everything a decode kernel needs, passed by value.
@@ -79,6 +81,7 @@ struct LayerDesc {
   int32_t max_seg;        // segments the grid covers: min(rows, slots, the caller's bound)
   int32_t sg_items;       // SGMV expand items (n-tiles over all modules) per row tile
   int32_t sg_nt;          // SGMV expand n-tile
+  int32_t count_errors;   // whether this launch adds the segment and entry errors to the status word
   const int32_t *perm;
   const int32_t *seg_offsets;
   const int32_t *seg_adapter;
@@ -133,6 +136,29 @@ struct FusedDesc {
 };
 
 hipError_t launch_fused(const FusedDesc &f, int blocks, hipStream_t stream);
+
+// ---- One-launch decode (lora_decode_layer on batches of distinct
+// adapters): the grouping of the rows, the shrink and the expand of every
+// projection in one launch, with no hand-off between blocks.  Rows it takes
+// at most (one row per thread of a block).
+constexpr int kOnePassMaxRows = 256;
+// Slot ids a block can rank against the caller's segment bound (a bitmap in
+// LDS); a batch whose bound may drop segments takes the one-launch path only
+// with at most this many slots.
+constexpr int kOnePassMaxSlots = 8192;
+// Expand tile of a block: kOnePassPasses load passes of the block over B
+// (rank/8 lanes per output row, 256 lanes).
+constexpr int kOnePassPasses = 8;
+
+struct OnePassDesc {
+  LayerDesc L;               // first member: kernel_desc() reads it from the kernel arguments
+  lora_segments_t seg;       // written by the grid's last block
+  const int32_t *ids;        // [num_rows] adapter slot of each row
+  int32_t row_slots;         // rows per item of the grid: num_rows rounded up to a multiple of 8
+  int32_t bound_check;       // the caller's segment bound may drop segments: blocks rank their slot
+};
+
+hipError_t launch_onepass(const OnePassDesc &d, int grid, hipStream_t stream);
 
 inline int round_up(int a, int b) { return (a + b - 1) / b * b; }
 inline int partial_row_stride(int max_rank) { return round_up(max_rank, 8); }

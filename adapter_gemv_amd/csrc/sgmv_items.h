@@ -237,9 +237,9 @@ __device__ __forceinline__ void sgmv_shrink_block(const LayerDesc &d, int blk, u
   const ModuleDesc m = module_of_item(d, it);
   const int chunk = it - m.item_base;
   int a, seg0, len;
-  if (!load_segment(d, s, it == 0 && rt == 0, &a, &seg0, &len)) return;
+  if (!load_segment(d, s, it == 0 && rt == 0 && d.count_errors, &a, &seg0, &len)) return;
   lora_adapter_entry_t e;
-  if (!load_entry(d, a, m.col, chunk == 0 && rt == 0, &e)) return;
+  if (!load_entry(d, a, m.col, chunk == 0 && rt == 0 && d.count_errors, &e)) return;
   if (e.format == LORA_FORMAT_INT8_ROWS) sgmv_shrink_tile<NT, true>(d, m, e, chunk, seg0, len, rt, lds);
   else sgmv_shrink_tile<NT, false>(d, m, e, chunk, seg0, len, rt, lds);
 }
@@ -393,9 +393,9 @@ __device__ __forceinline__ void sgmv_expand_block(const LayerDesc &d, int blk, f
   const ModuleDesc m = module_of_item<true>(d, it);
   const int tile = it - m.sg_item_base;
   int a, seg0, len;
-  if (!load_segment(d, s, it == 0 && rt == 0, &a, &seg0, &len)) return;
+  if (!load_segment(d, s, it == 0 && rt == 0 && d.count_errors, &a, &seg0, &len)) return;
   lora_adapter_entry_t e;
-  if (!load_entry(d, a, m.col, tile == 0 && rt == 0, &e)) return;
+  if (!load_entry(d, a, m.col, tile == 0 && rt == 0 && d.count_errors, &e)) return;
   if (e.format == LORA_FORMAT_INT8_ROWS)
     sgmv_expand_tile<KT, true, VU>(d, m, e.B, e.rank, e.scale, seg0, len, rt, tile, v_lds);
   else

@@ -144,6 +144,26 @@ def fused_comparison(w, d, lg, stream, steps, traffic):
             "unfused": "torch.mm (bf16 GEMM library) into y, then lora_build_segments + lora_apply_layer"}
 
 
+def copy_ceiling(torch, stream, nbytes=1 << 30, reps=10):
+    """A plain device-to-device copy of nbytes on the launch stream: bytes read
+    plus bytes written per second (the practical HBM ceiling of this machine)."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            dst.copy_(src)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+    s = a.elapsed_time(b) * 1e-3 / reps
+    del src, dst
+    return 2 * nbytes / s / 1e9
+
+
 def rank_class(max_rank):
     """Template class of the grouped kernels for a launch's largest rank."""
     return 0 if max_rank <= 8 else 1 if max_rank <= 16 else 2 if max_rank <= 32 else 3
@@ -307,6 +327,9 @@ def main():
     ap.add_argument("--replicas", type=int, default=0,
                     help="independent copies of the adapters to rotate through (0 = enough to exceed 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=("decode", "phases"), default="decode",
+                    help="decode: a step is one lora_decode_layer call (one launch for batches that fit it); "
+                         "phases: lora_build_segments + lora_layer_shrink + lora_layer_expand")
     ap.add_argument("--no-segment-bound", action="store_true",
                     help="give the calls no bound on the segments (max_segments = 0): work items sized for one "
                          "adapter per row")
@@ -399,6 +422,9 @@ def main():
             lg.apply_layer_stacked(d.ios, w.num_rows, stack, d.table, w.num_slots, d.seg, w.max_rank, d.ws, stream,
                                    pass_max_rank=pass_rank)
             return
+        if args.path == "decode":
+            d.decode_layer(stream)  # segments + delta: one launch when the batch fits it, else three
+            return
         d.build_segments(stream)
         lg.layer_shrink(d.ios, w.num_rows, d.table, w.num_slots, d.seg, w.max_rank, d.ws, stream)
         lg.layer_expand(d.ios, w.num_rows, d.table, w.num_slots, d.seg, w.max_rank, d.ws, stream)
@@ -418,6 +444,17 @@ def main():
     ms = t0.elapsed_time(t1) / args.steps
     value = w.num_rows / (ms * 1e-3)
     gbps = traffic["total"] / (ms * 1e-3) / 1e9
+
+    # ---- spread: the same K steps again, each between its own pair of HIP
+    # events on the launch stream (outside the timed region above)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        launch(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
 
     # ---- each kernel's average duration: per phase, K launches back to back
     # (the same replicas in the same order) between two HIP events on the
@@ -440,6 +477,11 @@ def main():
     cols = [None] if stack is None else [stack[:, t].contiguous() for t in range(stack.shape[1])]
     per_pass = []
     kernels = {}  # name -> [launches, us, algorithmic bytes] per step
+    one_launch = args.path == "decode" and w.W is None and stack is None and dws[0].decode_launches() == 1
+    if one_launch:  # the step is one kernel: segments, shrink and expand of every projection
+        one_us = phase_us(lambda d: d.decode_layer(stream))
+        kernels[f"lora_onepass_kernel<{rank_class(w.max_rank)}>"] = [1, one_us, traffic["total"]]
+        cols = []
     for t, col in enumerate(cols):
         r = pass_rank[t]
         if col is None:
@@ -463,9 +505,13 @@ def main():
             k[0] += 1
             k[1] += us
             k[2] += passes[t][ph + "_bytes"]
-    phases = {"segments": (sum(p["segments"] for p in per_pass), 0),
-              "shrink": (sum(p["shrink"] for p in per_pass), traffic["shrink_bytes"]),
-              "expand": (sum(p["expand"] for p in per_pass), traffic["expand_bytes"])}
+    if one_launch:
+        phases = {"onepass": (one_us, traffic["total"])}
+    else:
+        phases = {"segments": (sum(p["segments"] for p in per_pass), 0),
+                  "shrink": (sum(p["shrink"] for p in per_pass), traffic["shrink_bytes"]),
+                  "expand": (sum(p["expand"] for p in per_pass), traffic["expand_bytes"])}
+    ceiling = copy_ceiling(torch, stream)
     kernel_name = max(kernels, key=lambda k: kernels[k][1])
     n_launch, tot_us, tot_bytes = kernels[kernel_name]
     achieved = tot_bytes / (tot_us * 1e-6) / 1e9
@@ -494,7 +540,16 @@ def main():
                 "algorithmic_bytes_per_launch": {"shrink": traffic["shrink_bytes"],
                                                  "expand": traffic["expand_bytes"]},
                 "achieved_gbps": round(gbps, 1),
-                "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2), "peak_gbps": PEAK_HBM_GBPS},
+                "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2), "peak_gbps": PEAK_HBM_GBPS,
+                "copy_ceiling_gbps": round(ceiling, 1), "pct_of_copy_ceiling": round(100 * gbps / ceiling, 2),
+                "copy_ceiling": "torch copy_ of 1 GiB on the launch stream, read + written bytes / time"},
+        "step_ms": {"median": round(float(np.median(per_step)), 5), "p10": round(float(np.percentile(per_step, 10)), 5),
+                    "p90": round(float(np.percentile(per_step, 90)), 5), "min": round(float(per_step.min()), 5),
+                    "max": round(float(per_step.max()), 5), "steps": int(per_step.size),
+                    "how": "each step between its own HIP events, in a pass after the timed region"},
+        "path": ("one launch (lora_decode_layer)" if one_launch else
+                 "lora_decode_layer (three launches)" if args.path == "decode" and w.W is None and stack is None
+                 else "separate launches"),
         "phases_us": {k: round(v[0], 2) for k, v in phases.items()},
         "kernels_algorithmic_bytes_per_launch": {k: int(round(v[2] / v[0])) for k, v in kernels.items()},
         "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,

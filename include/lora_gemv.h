@@ -51,8 +51,10 @@
  *    sets it to the number of rows whose id is >= num_slots; each delta call
  *    then adds one per segment that does not fit the batch and one per
  *    (segment, projection) whose table entry cannot be applied (rank above
- *    max_rank, a null or misaligned factor pointer).  It is a flag and a
- *    rough count, not a number of rows.
+ *    max_rank, a null or misaligned factor pointer).  A call made of two
+ *    parts counts in its first: lora_layer_shrink and lora_linear_shrink
+ *    add, lora_layer_expand and lora_linear_expand add nothing.  It is a
+ *    flag and a count of problems, not a number of rows.
  *  - Dimensions d_in, d_out and leading dimensions are counted in elements;
  *    d_in, d_out, ldx and ldy must be multiples of 8 and x, y pointers
  *    16-byte aligned (16-byte vector access).
@@ -199,11 +201,11 @@ typedef struct lora_module_io {
 
 /*
  * Workspace (device scratch) that covers every call with these sizes, in
- * bytes.  sum_d_in is the sum of d_in over the projections a call processes
- * (d_in for lora_shrink, the sum over the mask for the layer calls).  One
- * workspace of this size serves every call on the same stream.  A call that
- * needs none (lora_expand; lora_build_segments on up to 1024 rows and 8192
- * slots) accepts ws = NULL.  A workspace must be 16-byte aligned
+ * bytes.  sum_d_in is the sum of d_in over the projections a
+ * call processes (d_in for lora_shrink, the sum over the mask for the layer
+ * calls).  One workspace of this size serves every call on the same stream.
+ * A call that needs none (lora_expand; lora_build_segments on up to 1024 rows
+ * and 8192 slots) accepts ws = NULL.  A workspace must be 16-byte aligned
  * (LORA_ERR_ALIGN otherwise).  Returns 0 for invalid arguments.
  */
 size_t lora_workspace_bytes(int32_t num_rows, int32_t num_slots,
@@ -294,6 +296,57 @@ lora_status_t lora_apply_layer(const lora_module_io_t *io, uint32_t module_mask,
                                int32_t num_slots, lora_segments_t seg,
                                int32_t max_rank, void *ws, size_t ws_bytes,
                                void *stream);
+
+/*
+ * lora_decode_layer -- lora_build_segments(row_adapter, ...) followed by
+ * lora_apply_layer(...) with the same arguments: the rows grouped by adapter
+ * (seg is written exactly as lora_build_segments writes it) and the delta of
+ * every projection in module_mask.  Source: "m07 -- Multi-Adapter (LoRA)
+ * Serving", "6. Deep Dive A" (one batched kernel takes the batch and the
+ * index vector mapping each sequence to an adapter slot, and gathers inside
+ * the kernel; the cost is bandwidth) and "LoRA, quotas and noisy
+ * neighbours", "One weight read, many adapters" (rows tagged and grouped,
+ * the update applied in registers).
+ * A decode batch of at most 256 rows with max_rank <= 32 runs as ONE launch
+ * when its repeated reads of A stay small (see below): every block finds its
+ * row's segment from the ids itself, computes that segment's whole v and
+ * applies one tile of B, so no block waits on another and nothing passes
+ * through the workspace.  The blocks of one segment each read its A (served
+ * from L2 after the first), so the path is taken only while those repeated
+ * reads stay within about 320 MB (one pass over A per segment, one more per
+ * 4 further rows, segments counted by seg.max_segments when given).  Any
+ * other batch runs the three launches of lora_build_segments +
+ * lora_apply_layer.  lora_decode_layer_launches tells which.  Both give
+ * results within the oracle tolerance; the one-launch path sums A.x in a
+ * different order, so its bits may differ from lora_apply_layer's.  Results
+ * are bit-reproducible.
+ *
+ *   row_adapter  device int32 [num_rows], as for lora_build_segments
+ *   seg          written as by lora_build_segments; seg.max_segments
+ *                applies as there (rows of segments past the bound get no
+ *                delta); *seg.status gets the rows whose id is >= num_slots
+ *                or past the bound, plus one per (segment, projection) whose
+ *                entry cannot be applied
+ *   ws, ws_bytes at least lora_workspace_bytes(num_rows, num_slots,
+ *                max_rank, sum of the masked d_in) (the one-launch path uses
+ *                none of it)
+ *   other arguments as for lora_apply_layer.
+ * Errors: those of lora_apply_layer and lora_build_segments.
+ */
+lora_status_t lora_decode_layer(const lora_module_io_t *io, uint32_t module_mask,
+                                int32_t num_rows, const int32_t *row_adapter,
+                                const lora_adapter_entry_t *table, int32_t num_slots,
+                                lora_segments_t seg, int32_t max_rank, void *ws,
+                                size_t ws_bytes, void *stream);
+
+/*
+ * lora_decode_layer_launches -- the number of kernel launches
+ * lora_decode_layer makes for these arguments (host only, no device work):
+ * 1 for the one-launch path, 3 otherwise, 0 for arguments it would reject.
+ */
+int32_t lora_decode_layer_launches(const lora_module_io_t *io, uint32_t module_mask,
+                                   int32_t num_rows, int32_t num_slots,
+                                   lora_segments_t seg, int32_t max_rank);
 
 /*
  * The two launches of lora_apply_layer, for callers that interleave other

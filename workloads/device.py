@@ -46,7 +46,8 @@ class DeviceWorkload:
         self.seg = lg.Segments(w.num_rows + ws_extra_rows, device, max_segments=bound)
         sum_d_in = sum(m.d_in for m in w.modules)
         self.ws_bytes = lg.workspace_bytes(w.num_rows + ws_extra_rows, w.num_slots, w.max_rank, sum_d_in)
-        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
+        # zeroed: the head of a workspace must start at zero (lora_decode_layer's hand-off words)
+        self.ws = torch.zeros(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
         self.ios = {m.name: lg.ModuleIO(self.x[m.x_name], self.y[m.name]) for m in w.modules}
         self.W = self.lin_ios = None
         if w.W is not None:  # base weights: the fused calls, and a workspace for them
@@ -56,7 +57,7 @@ class DeviceWorkload:
                                            len(w.modules))
             if nb > self.ws_bytes:
                 self.ws_bytes = nb
-                self.ws = torch.empty(nb, dtype=torch.uint8, device=device)
+                self.ws = torch.zeros(nb, dtype=torch.uint8, device=device)
 
     def pack(self, base: int, ranks=None, scales=None) -> np.ndarray:
         w = self.w
@@ -82,6 +83,14 @@ class DeviceWorkload:
     def apply_layer(self, stream=None):
         lg.apply_layer(self.ios, self.w.num_rows, self.table, self.w.num_slots, self.seg, self.w.max_rank, self.ws,
                        stream)
+
+    def decode_layer(self, stream=None):
+        """Segments and every projection through lora_decode_layer."""
+        lg.decode_layer(self.ios, self.w.num_rows, self.ids, self.table, self.w.num_slots, self.seg, self.w.max_rank,
+                        self.ws, stream)
+
+    def decode_launches(self) -> int:
+        return lg.decode_layer_launches(self.ios, self.w.num_rows, self.w.num_slots, self.seg, self.w.max_rank)
 
     def step(self, stream=None):
         """One pass of the decode path: segments, then every projection."""
