@@ -353,16 +353,24 @@ lora_status_t lora_apply_layer(const lora_module_io_t *io, uint32_t module_mask,
 namespace {
 
 // The one-launch plan of lora_decode_layer.  Each block of the one-launch
-// kernel reads the whole A of its segment (its siblings, one per expand
-// tile, read the same lines through L2), so the plan bounds those repeated
-// reads: at most kOnePassRepeatBytes over all projections, counting one pass
-// over A per segment and one more per 4 further rows (segments are at most
-// the caller's bound, else one per row).  Measured on one MI355X with
-// distinct adapters per row: the launch is 2-3x faster than the three
-// launches of lora_build_segments + lora_apply_layer below about 150 MB of
-// repeated reads, even at 268 MB, and slower from 537 MB.  Batches of at most
-// kOnePassMaxRows rows, ranks up to 32.  False for any other batch.
+// kernel reads the whole A of its segment (its siblings, one per group of
+// expand tiles, read the same lines through L2), so the plan bounds those
+// repeated reads: at most kOnePassRepeatBytes over all projections, counting
+// one pass over A per block of a segment and one more per 4 further rows
+// (segments are at most the caller's bound, else one per row).  Measured on
+// one MI355X (steps replayed from a HIP graph, one projection d x d, a
+// distinct adapter per row, 16 to 256 rows, d 1024 to 8192, ranks 8 to 32):
+// the launch beats the three launches of lora_build_segments +
+// lora_apply_layer everywhere, by 2-3x up to 64 rows (4-9 us against 12-16
+// us), 18.9 against 27.4 us for 128 rows x 8192 at rank 16, 39 against 42 us
+// for 128 rows x 8192 at rank 32 (268 MB of repeated reads), and ties at the
+// same 268 MB with 256 rows.  Batches of at most kOnePassMaxRows rows, ranks
+// up to 32.  False for any other batch.
 constexpr double kOnePassRepeatBytes = 320.0 * (1 << 20);
+// The grid keeps this many blocks as tiles per block grow (measured: 128
+// rows x 8192 at rank 16 takes 17.1 us with one tile per block (513
+// blocks), 17.2 with two, 20.7 with four).
+constexpr int64_t kOnePassMinBlocks = 512;
 
 bool onepass_plan(const ModuleArgs *ms, int n, int num_rows, const int32_t *ids, int num_slots, int max_rank,
                   const lora_adapter_entry_t *table, const lora_segments_t &seg, OnePassDesc *od, int *grid) {
@@ -374,9 +382,18 @@ bool onepass_plan(const ModuleArgs *ms, int n, int num_rows, const int32_t *ids,
   const bool bound_check = max_seg < (num_rows < num_slots ? num_rows : num_slots);
   if (bound_check && num_slots > kOnePassMaxSlots) return false;
   const double passes = max_seg + (num_rows - max_seg + 3) / 4;
+  // tiles per block: doubled while the grid keeps kOnePassMinBlocks blocks
+  // (each block reads its segment's A once for all its tiles)
+  auto items = [&](int tpb) {
+    int64_t it = 0;
+    for (int i = 0; i < n; ++i) it += ((ms[i].d_out + nt - 1) / nt + tpb - 1) / tpb;
+    return it;
+  };
+  int tpb = 1;
+  while (tpb < 64 && items(2 * tpb) < items(tpb) && items(2 * tpb) * num_rows >= kOnePassMinBlocks) tpb *= 2;
   double repeat = 0;
   for (int i = 0; i < n; ++i)
-    repeat += (double)((ms[i].d_out + nt - 1) / nt) * ms[i].d_in * (8 * lpr) * 2 * passes;
+    repeat += (double)(((ms[i].d_out + nt - 1) / nt + tpb - 1) / tpb) * ms[i].d_in * (8 * lpr) * 2 * passes;
   if (repeat > kOnePassRepeatBytes) return false;
   *od = OnePassDesc{};
   LayerDesc &d = od->L;
@@ -393,9 +410,9 @@ bool onepass_plan(const ModuleArgs *ms, int n, int num_rows, const int32_t *ids,
     m.col = ms[i].col;
     m.op_nt = nt;
     m.op_n_tiles = (m.d_out + nt - 1) / nt;
-    m.n_items = m.op_n_tiles;
+    m.n_items = (m.op_n_tiles + tpb - 1) / tpb;
     m.item_base = item;
-    item += m.op_n_tiles;
+    item += m.n_items;
   }
   d.n_active = n;
   d.items_per_seg = item;
@@ -411,6 +428,7 @@ bool onepass_plan(const ModuleArgs *ms, int n, int num_rows, const int32_t *ids,
   od->ids = ids;
   od->row_slots = (num_rows + 7) / 8 * 8;
   od->bound_check = bound_check;
+  od->tiles_per_block = tpb;
   const int64_t blocks = (int64_t)item * od->row_slots + 1;
   if (blocks > 0x7fffffff) return false;
   *grid = (int)blocks;

@@ -105,9 +105,9 @@ __global__ __launch_bounds__(256) void shrink_reduce_kernel(LayerDesc d) {
 // One-launch decode (onepass_items.h): block 0 writes the segments; blocks
 // 1.. are (item, row), item-major over row_slots (a multiple of 8) rows, so
 // the blocks of one row share an XCD when blocks are dealt to the XCDs in
-// turn.  Waves per SIMD: 4 up to rank class 16, 3 for 32.
+// turn.  Compiled for 3 waves per SIMD (the 16-pass B tile).
 template <int CLS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CLS <= 1 ? 4 : 3))) void lora_onepass_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void lora_onepass_kernel(
     OnePassDesc od) {
   __shared__ __align__(16) uint8_t lds[kOnePassLdsBytes];
   if (blockIdx.x == 0) {
@@ -135,8 +135,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CLS <= 1 ? 
   e.format = uniform(raw.format);
   e.reserved = 0;
   if (!entry_ok(e, d.max_rank)) return;  // rank 0, or an entry the last block counts
-  if (e.format == LORA_FORMAT_INT8_ROWS) op_delta<CLS, true>(m, e, c, t, a, idu, od.bound_check, d.max_seg, lds);
-  else op_delta<CLS, false>(m, e, c, t, a, idu, od.bound_check, d.max_seg, lds);
+  const int tpb = od.tiles_per_block;
+  if (e.format == LORA_FORMAT_INT8_ROWS) op_delta<CLS, true>(m, e, c, tpb, t, a, idu, od.bound_check, d.max_seg, lds);
+  else op_delta<CLS, false>(m, e, c, tpb, t, a, idu, od.bound_check, d.max_seg, lds);
 }
 
 // Base projection + delta (fused_items.h).

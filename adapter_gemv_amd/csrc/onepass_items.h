@@ -15,11 +15,11 @@
 // the segment whose first row is t (blocks of other rows leave at once).  It
 // reads the ids of the batch and its row's table entry itself, so no block
 // waits for a grouping pass, and then
-//   1. requests its tile of B (kOnePassPasses load passes of the block, kept
-//      in registers) and, for a one-row segment, its tile of y;
+//   1. requests, for a one-row segment, its tile of y;
 //   2. computes the whole v = A.x of its segment's rows (every k of A),
 //      times the entry's scale, into LDS;
-//   3. adds B.v to its tile of y.
+//   3. loads its tile of B (kOnePassPasses load passes of the block, kept in
+//      registers) and adds B.v to its tile of y.
 // No block hands anything to another: the blocks of one (segment,
 // projection) each compute the same v.  They sit on one XCD (the grid is
 // item-major over a multiple of 8 rows and blocks are dealt to the XCDs in
@@ -41,6 +41,7 @@ constexpr int kOpVOff = 1280;                                 // v [kOpGroup][64
 constexpr int kOpMaxTile = kOnePassPasses * kDecodeThreads;   // largest tile (one lane per B row)
 constexpr int kOpDeltaOff = kOpVOff + kOpGroup * 64 * 4;      // one tile of sums
 constexpr int kOnePassLdsBytes = kOpDeltaOff + kOpMaxTile * 4;
+static_assert(kOpMaxTile % (kDecodeThreads * 8) == 0, "the y update takes whole steps of 8 columns per thread");
 
 // Block-wide sum of one int per thread (256 threads); s_w holds 4 ints.
 __device__ __forceinline__ int op_block_sum(int x, int *s_w) {
@@ -229,10 +230,14 @@ template <bool Q8>
 __device__ __forceinline__ void op_update_y(const ModuleDesc &m, const void *B, int row, int n0, int tile_len,
                                             const float *delta, u32x4 pre, bool use_pre) {
   const int t = threadIdx.x;
-  const int col = t * 8;
   const rsrc_t ry = make_rsrc(m.y + (int64_t)row * m.ldy + n0, (uint32_t)tile_len * 2);
-  if (col < tile_len) {
-    const u32x4 yv = use_pre ? pre : buf_ld16(ry, (uint32_t)col * 2, 0);
+  // 8 columns per thread and step: a tile of up to kOpMaxTile columns takes
+  // kOpMaxTile / 2048 steps; `pre` holds the first step's y
+#pragma unroll
+  for (int step = 0; step < kOpMaxTile / (kDecodeThreads * 8); ++step) {
+    const int col = (step * kDecodeThreads + t) * 8;
+    if (col >= tile_len) break;
+    const u32x4 yv = use_pre && step == 0 ? pre : buf_ld16(ry, (uint32_t)col * 2, 0);
     float dl[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) dl[k] = delta[col + k];
@@ -292,27 +297,28 @@ __device__ __forceinline__ void op_expand_rows(const ModuleDesc &m, const lora_a
   }
 }
 
-// Tile c of projection m for the segment of row `row` (slot a, entry e; idu:
+// Tiles [c*tpb, c*tpb + tpb) of projection m for the segment of row `row` (slot a, entry e; idu:
 // row u's id in thread u), unless the segment lies past the caller's bound
 // (checked when bound_check: the first max_seg slots in ascending order keep
 // their delta).  CLS: the launch's rank class (rows of A per wave, lanes per
 // B row).
 template <int CLS, bool Q8>
-__device__ __forceinline__ void op_delta(const ModuleDesc &m, const lora_adapter_entry_t &e, int c, int row, int a,
-                                         int idu, bool bound_check, int max_seg, uint8_t *lds) {
+__device__ __forceinline__ void op_delta(const ModuleDesc &m, const lora_adapter_entry_t &e, int c, int tpb, int row,
+                                         int a, int idu, bool bound_check, int max_seg, uint8_t *lds) {
   constexpr int JW = 2 << CLS;
   constexpr int LPR = 1 << CLS;
   const int t = threadIdx.x;
   const int *s_rows = reinterpret_cast<const int *>(lds + kOpRowsOff);
   float *v_lds = reinterpret_cast<float *>(lds + kOpVOff);
   float *delta = reinterpret_cast<float *>(lds + kOpDeltaOff);
-  const int n0 = c * m.op_nt;
+  const int tile0 = c * tpb;
+  const int tiles = min(tpb, m.op_n_tiles - tile0);  // this block's tiles: [tile0, tile0 + tiles)
+  const int n0 = tile0 * m.op_nt;
   const int tile_len = min(m.op_nt, m.d_out - n0);
-  // 1. the tile of B and the row's tile of y, requested before anything
-  // waits: a row whose adapter no other row shares (the case this path is
-  // planned for) needs nothing else
+  // 1. the row's first tile of y, requested before anything waits (a row whose
+  // adapter no other row shares, the case this path is planned for, needs
+  // nothing else); B follows the shrink
   OpBTile<LPR, Q8> bt;
-  bt.load(e.B, e.rank, m.d_out, n0, tile_len);
   const rsrc_t ry = make_rsrc(m.y + (int64_t)row * m.ldy + n0, (uint32_t)tile_len * 2);
   const u32x4 y_pre = buf_ld16(ry, t * 8 < tile_len ? (uint32_t)t * 16 : kOutOfRange, 0);
   // the segment of the row, while those loads are in flight: the ballots
@@ -327,9 +333,14 @@ __device__ __forceinline__ void op_delta(const ModuleDesc &m, const lora_adapter
           max_seg)
     return;
   if (len == 1) {
-    // 2. v of the row, 3. its tile of y
+    // 2. v of the row, 3. its tiles of y
     op_shrink_rows<JW, 1, Q8>(m, e, s_rows, 1, v_lds);
-    op_expand_rows<LPR, Q8>(m, e, bt, n0, tile_len, s_rows, 1, v_lds, delta, y_pre, true);
+    for (int i = 0; i < tiles; ++i) {
+      const int ni = n0 + i * m.op_nt;
+      const int len_i = min(m.op_nt, m.d_out - ni);
+      bt.load(e.B, e.rank, m.d_out, ni, len_i);  // after the shrink: the registers of both do not fit
+      op_expand_rows<LPR, Q8>(m, e, bt, ni, len_i, s_rows, 1, v_lds, delta, y_pre, i == 0);
+    }
     return;
   }
   constexpr int RG = 4;  // rows of x per pass over A
@@ -337,8 +348,12 @@ __device__ __forceinline__ void op_delta(const ModuleDesc &m, const lora_adapter
     const int nr = min(kOpGroup, len - r0);
     for (int r1 = 0; r1 < nr; r1 += RG)
       op_shrink_rows<JW, RG, Q8>(m, e, s_rows + r0 + r1, min(RG, nr - r1), v_lds + r1 * 64);
-    bt.load(e.B, e.rank, m.d_out, n0, tile_len);
-    op_expand_rows<LPR, Q8>(m, e, bt, n0, tile_len, s_rows + r0, nr, v_lds, delta, zero4(), false);
+    for (int i = 0; i < tiles; ++i) {
+      const int ni = n0 + i * m.op_nt;
+      const int len_i = min(m.op_nt, m.d_out - ni);
+      bt.load(e.B, e.rank, m.d_out, ni, len_i);
+      op_expand_rows<LPR, Q8>(m, e, bt, ni, len_i, s_rows + r0, nr, v_lds, delta, zero4(), false);
+    }
   }
 }
 

@@ -86,6 +86,11 @@ SHAPES = [
     (256, 256, 4096, 2048, 16, "distinct"),
     (256, 7, 1024, 1040, (16, 0, 12), "random"),              # an untargeted slot
     (97, 8192, 2048, 1024, 8, "random_wide"),                 # ids over the largest slot table
+    # rank 8 and below: one lane per B row, tiles of 4096 columns (two steps
+    # of the y update), full and ragged, one- and multi-row segments
+    (24, 24, 1024, 4096 + 72, 8, "distinct"),
+    (3, 3, 512, 8192, (8, 4, 1), "distinct"),
+    (48, 6, 1024, 3000 + 8, 8, "random"),
 ]
 
 
@@ -102,16 +107,17 @@ def test_shapes_one_launch(shape):
     check(w, launches=1)
 
 
-@pytest.mark.parametrize("fmt", ["int8", "mixed"])
-def test_int8_factors(fmt):
+@pytest.mark.parametrize("fmt,max_rank,d_out", [("int8", 32, 2 * 1024 + 8), ("mixed", 32, 2 * 1024 + 8),
+                                                 ("int8", 8, 4096 + 8)])
+def test_int8_factors(fmt, max_rank, d_out):
     slots, rows = 24, 96
     ids = np.random.default_rng(4).integers(0, slots, size=rows)
     ranks = np.zeros((slots, 7), np.int32)
-    ranks[:, 0] = np.resize(np.array([8, 16, 3, 24, 32, 13]), slots)
+    ranks[:, 0] = np.resize(np.array([8, 16, 3, 24, 32, 13]), slots).clip(max=max_rank)
     code = gen.FMT_INT8_ROWS if fmt == "int8" else \
         (np.where(np.arange(slots)[:, None] % 2 == 0, gen.FMT_INT8_ROWS, gen.FMT_BF16) * np.ones((1, 7), int)
          ).astype(np.int32)
-    w = bw(41, rows, slots, 2056, 2 * 1024 + 8, None, ids, ranks=ranks, x_std=1.0, max_rank=32, fmt=code)
+    w = bw(41, rows, slots, 2056, d_out, None, ids, ranks=ranks, x_std=1.0, max_rank=max_rank, fmt=code)
     check(w, launches=1)
 
 
@@ -241,8 +247,9 @@ def test_graph_replay_follows_device_data():
 
 def test_three_launch_paths():
     # more rows than one block holds; rank 64; and too many repeated reads
-    # of A (256 rows with their own rank-32 adapters, 4096 -> 4096)
+    # of A (256 rows with their own rank-32 adapters, 16384 -> 4096: two
+    # blocks of 2 tiles per row, each reading its 1 MiB of A: 537 MB)
     ids = np.random.default_rng(2).integers(0, 300, size=300)
     check(bw(70, 300, 300, 1024, 1024, 16, ids, x_std=1.0), launches=3)
     check(bw(71, 16, 16, 2048, 8192, 64, np.arange(16), x_std=1.0), launches=3)
-    check(bw(72, 256, 256, 4096, 4096, 32, np.arange(256), x_std=1.0), launches=3)
+    check(bw(72, 256, 256, 16384, 4096, 32, np.arange(256), x_std=1.0), launches=3)
