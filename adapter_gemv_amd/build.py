@@ -15,6 +15,9 @@ INCLUDE = os.path.join(ROOT, "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.hip", "segments.hip", "kernels.hip", "batch_former.cpp"]
+# the benchmark's read-ceiling kernel: a library of its own, outside the C ABI
+READ_CEILING_SRC = "read_ceiling.hip"
+READ_CEILING_LIB = os.path.join(HERE, "libread_ceiling.so")
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -35,11 +38,24 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _build_read_ceiling() -> None:
+    tmp = READ_CEILING_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", os.path.join(CSRC, READ_CEILING_SRC), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed on {READ_CEILING_SRC}")
+    os.replace(tmp, READ_CEILING_LIB)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link liblora_gemv.so (always rebuilds)."""
+    """Compile every source for gfx950 and link liblora_gemv.so, and the
+    benchmark's libread_ceiling.so (always rebuilds)."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
+    with ThreadPoolExecutor(len(SOURCES) + 1) as ex:
+        side = ex.submit(_build_read_ceiling)
         objs = list(ex.map(_compile, SOURCES))
+        side.result()
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -3,7 +3,10 @@
 
 One step = one pass of the whole decode hot path over one batch: the segment
 build and the delta of every projection of the workload (grouped shrink and
-grouped expand launches), with inputs resident in HBM.  Prints one JSON line.
+grouped expand launches, or the one launch of lora_decode_layer where the
+batch fits it), with inputs resident in HBM.  The K timed steps replay from
+one captured HIP graph, as a serving loop replays its decode step (--no-graph:
+every launch from the host).  Prints one JSON line.
 
 Default workload: the 70B full layer (q, k, v, o, gate, up, down at rank 64)
 with 128 decode rows, each with its own adapter (128 resident adapters), bf16.
@@ -162,6 +165,43 @@ def copy_ceiling(torch, stream, nbytes=1 << 30, reps=10):
     s = a.elapsed_time(b) * 1e-3 / reps
     del src, dst
     return 2 * nbytes / s / 1e9
+
+
+def read_ceiling(torch, stream, nbytes, reps=20, pool_bytes=1 << 30):
+    """A kernel that only reads (libread_ceiling.so), over nbytes per launch,
+    each launch in the next of enough buffers to span pool_bytes (as the
+    adapter replicas do, so the reads come from HBM): bytes read per second,
+    reps launches replayed from one HIP graph on the launch stream."""
+    import ctypes
+    here = os.path.dirname(os.path.abspath(__file__))
+    lib = ctypes.CDLL(os.path.join(here, "adapter_gemv_amd", "libread_ceiling.so"))
+    lib.read_ceiling_launch.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.read_ceiling_blocks.argtypes = [ctypes.c_uint64]
+    nbuf = max(2, -(-pool_bytes // nbytes) + 1)
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+    sink = torch.zeros(lib.read_ceiling_blocks(nbytes), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+
+    def launch(i):
+        rc = lib.read_ceiling_launch(bufs[i % nbuf].data_ptr(), nbytes, sink.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"read_ceiling_launch: hip error {rc}")
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(reps):
+            launch(i)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        g.replay()
+        torch.cuda.synchronize()
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    del bufs, sink, g
+    return nbytes / (us * 1e-6) / 1e9, us
 
 
 def rank_class(max_rank):
@@ -330,6 +370,8 @@ def main():
     ap.add_argument("--path", choices=("decode", "phases"), default="decode",
                     help="decode: a step is one lora_decode_layer call (one launch for batches that fit it); "
                          "phases: lora_build_segments + lora_layer_shrink + lora_layer_expand")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every step from the host (default: the K steps replay from one captured HIP graph)")
     ap.add_argument("--no-segment-bound", action="store_true",
                     help="give the calls no bound on the segments (max_segments = 0): work items sized for one "
                          "adapter per row")
@@ -433,15 +475,40 @@ def main():
         launch(i)
     torch.cuda.synchronize()
 
+    use_graph = not args.no_graph
+
+    def captured(fn, n):
+        """fn(0), ..., fn(n-1), captured on the launch stream into one HIP graph
+        and replayed once untimed (the replay uploads the graph).  The library
+        calls launch kernels only: no allocation, copy or memset is recorded."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                fn(i)
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    def run_timed(fn, n):
+        """ms for fn(0..n-1) between two HIP events on the launch stream: one
+        replay of their graph, or n launches from the host"""
+        g = captured(fn, n) if use_graph else None
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        if g is not None:
+            with torch.cuda.stream(stream):
+                g.replay()
+        else:
+            for i in range(n):
+                fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
     # ---- timed region: K steps between two HIP events on the launch stream.
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(args.steps):
-        launch(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    ms = run_timed(launch, args.steps) / args.steps
     value = w.num_rows / (ms * 1e-3)
     gbps = traffic["total"] / (ms * 1e-3) / 1e9
 
@@ -462,14 +529,7 @@ def main():
     # from the steps above, so each phase can repeat on its own (the expand
     # then adds its delta more than once, which timing does not care about).
     def phase_us(fn):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for i in range(args.steps):
-            fn(dws[i % reps])
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / args.steps * 1e3
+        return run_timed(lambda i: fn(dws[i % reps]), args.steps) / args.steps * 1e3
 
     # A stacked step runs the kernels once per pass (one column of the adapter
     # lists each, in that column's rank class); a kernel's figures sum over
@@ -512,6 +572,7 @@ def main():
                   "shrink": (sum(p["shrink"] for p in per_pass), traffic["shrink_bytes"]),
                   "expand": (sum(p["expand"] for p in per_pass), traffic["expand_bytes"])}
     ceiling = copy_ceiling(torch, stream)
+    read_gbps, read_us = read_ceiling(torch, stream, int(traffic["total"]))
     kernel_name = max(kernels, key=lambda k: kernels[k][1])
     n_launch, tot_us, tot_bytes = kernels[kernel_name]
     achieved = tot_bytes / (tot_us * 1e-6) / 1e9
@@ -542,11 +603,18 @@ def main():
                 "achieved_gbps": round(gbps, 1),
                 "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2), "peak_gbps": PEAK_HBM_GBPS,
                 "copy_ceiling_gbps": round(ceiling, 1), "pct_of_copy_ceiling": round(100 * gbps / ceiling, 2),
-                "copy_ceiling": "torch copy_ of 1 GiB on the launch stream, read + written bytes / time"},
+                "copy_ceiling": "torch copy_ of 1 GiB on the launch stream, read + written bytes / time",
+                "read_ceiling_gbps": round(read_gbps, 1), "read_ceiling_us": round(read_us, 2),
+                "pct_of_read_ceiling": round(100 * gbps / read_gbps, 2),
+                "read_ceiling": "a read-only kernel over the step's algorithmic bytes, from buffers spanning 1 GiB, "
+                                "replayed from a HIP graph"},
         "step_ms": {"median": round(float(np.median(per_step)), 5), "p10": round(float(np.percentile(per_step, 10)), 5),
                     "p90": round(float(np.percentile(per_step, 90)), 5), "min": round(float(per_step.min()), 5),
                     "max": round(float(per_step.max()), 5), "steps": int(per_step.size),
-                    "how": "each step between its own HIP events, in a pass after the timed region"},
+                    "how": "each step launched from the host between its own HIP events, in a pass after the "
+                           "timed region"},
+        "launch": ("the K steps (and each kernel's K launches) replayed from one captured HIP graph, "
+                   "after one untimed replay" if use_graph else "every launch from the host"),
         "path": ("one launch (lora_decode_layer)" if one_launch else
                  "lora_decode_layer (three launches)" if args.path == "decode" and w.W is None and stack is None
                  else "separate launches"),

@@ -36,6 +36,22 @@ def test_exports_every_declared_symbol():
         getattr(L, n)
 
 
+def test_read_ceiling_library_is_separate():
+    # the benchmark's read-ceiling kernel lives in a library of its own: the C ABI exports no such symbol
+    here = os.path.dirname(lg.LIB_PATH)
+    path = os.path.join(here, "libread_ceiling.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    assert {"read_ceiling_launch", "read_ceiling_blocks"} <= set(re.findall(r"\bT (\w+)", out))
+    main = subprocess.run(["nm", "-D", "--defined-only", lg.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    assert "read_ceiling" not in main
+    L = ctypes.CDLL(path)
+    L.read_ceiling_blocks.argtypes = [ctypes.c_uint64]
+    assert [L.read_ceiling_blocks(n) for n in (1, 65536, 65537, 1 << 30)] == [1, 1, 2, 16384]
+    L.read_ceiling_launch.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    assert L.read_ceiling_launch(None, 64, P, None) != 0  # rejected before any HIP call
+    assert L.read_ceiling_launch(P, 0, P, None) != 0
+
+
 def seg(**kw):
     d = dict(perm=P, seg_offsets=P, seg_adapter=P, num_segments=P, tile_counts=P, status=P)
     d.update(kw)
