@@ -1,6 +1,6 @@
 // One-launch decode: the grouping of the rows by adapter, the shrink and the
-// expand of every projection in a single launch, for a decode batch in which
-// every row has its own adapter (lora_decode_layer).
+// expand of every projection in a single launch, for a small decode batch
+// (lora_decode_layer).
 //
 // "m07 -- Multi-Adapter (LoRA) Serving", "6. Deep Dive A": one batched
 // kernel receives the batch and the index vector mapping each sequence to an
@@ -12,19 +12,20 @@
 // rows are tagged and grouped, and the update is applied in registers.
 //
 // Blocks.  Block (item it, row t) takes expand tile c of one projection for
-// the segment whose first row is t (blocks of other rows leave at once).  It
-// reads the ids of the batch and its row's table entry itself, so no block
-// waits for a grouping pass, and then
-//   1. requests, for a one-row segment, its tile of y;
-//   2. computes the whole v = A.x of its segment's rows (every k of A),
-//      times the entry's scale, into LDS;
+// row t and, when t is the first, fifth, ... row of its adapter's segment,
+// the next rows of that segment up to 4 (blocks of the other rows leave at
+// once).  It reads the ids of the batch and its row's table entry itself, so
+// no block waits for a grouping pass, and then
+//   1. requests its row's tile of y;
+//   2. computes v = A.x of its rows (every k of A, one pass over A for all of
+//      them), times the entry's scale, into LDS;
 //   3. loads its tile of B (kOnePassPasses load passes of the block, kept in
-//      registers) and adds B.v to its tile of y.
-// No block hands anything to another: the blocks of one (segment,
-// projection) each compute the same v.  They sit on one XCD (the grid is
-// item-major over a multiple of 8 rows and blocks are dealt to the XCDs in
-// turn) and stream A in the same order at the same time, so the repeated
-// reads of A are served by that XCD's L2 and A crosses HBM about once.
+//      registers) and adds B.v to its rows' tiles of y.
+// No block hands anything to another: the blocks of one (rows, projection)
+// each compute the same v.  They sit on one XCD (the grid is item-major over
+// a multiple of 8 rows and blocks are dealt to the XCDs in turn) and stream
+// A in the same order at the same time, so the repeated reads of A are
+// served by that XCD's L2 and A crosses HBM about once per group of rows.
 // Block 0 writes the segments and the status word as lora_build_segments
 // followed by lora_apply_layer would; it runs beside the others.
 #pragma once
@@ -36,10 +37,10 @@ namespace lora {
 // LDS of a one-launch block (bytes).
 constexpr int kOpRowsOff = 0;                                 // 256 ints: the segment's rows, ascending
 constexpr int kOpMiscOff = 1024;                              // 64 ints: ballots and broadcasts
-constexpr int kOpGroup = 16;                                  // rows whose v is staged together
-constexpr int kOpVOff = 1280;                                 // v [kOpGroup][64] (times scale)
+constexpr int kOpRowsPerBlock = 4;                            // rows of a segment per block: one pass over A
+constexpr int kOpVOff = 1280;                                 // v [kOpRowsPerBlock][64] (times scale)
 constexpr int kOpMaxTile = kOnePassPasses * kDecodeThreads;   // largest tile (one lane per B row)
-constexpr int kOpDeltaOff = kOpVOff + kOpGroup * 64 * 4;      // one tile of sums
+constexpr int kOpDeltaOff = kOpVOff + kOpRowsPerBlock * 64 * 4;  // one tile of sums
 constexpr int kOnePassLdsBytes = kOpDeltaOff + kOpMaxTile * 4;
 static_assert(kOpMaxTile % (kDecodeThreads * 8) == 0, "the y update takes whole steps of 8 columns per thread");
 
@@ -54,11 +55,11 @@ __device__ __forceinline__ int op_block_sum(int x, int *s_w) {
   return total;
 }
 
-// The segment of row t: false when an earlier row has the same id (it
-// applies the delta).  Otherwise *len_out rows, ascending, are in LDS at
-// kOpRowsOff.  `id` is row t's slot, in [0, num_slots) (uniform); idu is
-// row u's id in thread u (-1 past the batch).
-__device__ __forceinline__ bool op_row_segment(int t, int id, int idu, uint8_t *lds, int *len_out) {
+// The segment of row t: its rows, ascending, in LDS at kOpRowsOff, their
+// count in *len_out and row t's place among them in *pos_out.  `id` is row
+// t's slot, in [0, num_slots) (uniform); idu is row u's id in thread u (-1
+// past the batch).
+__device__ __forceinline__ void op_row_segment(int t, int id, int idu, uint8_t *lds, int *len_out, int *pos_out) {
   const int u = threadIdx.x, lane = u & 63, w = u >> 6;
   int *s_rows = reinterpret_cast<int *>(lds + kOpRowsOff);
   int *s_misc = reinterpret_cast<int *>(lds + kOpMiscOff);
@@ -82,7 +83,7 @@ __device__ __forceinline__ bool op_row_segment(int t, int id, int idu, uint8_t *
   }
   __syncthreads();
   *len_out = uniform(len);
-  return uniform(earlier) == 0;
+  *pos_out = uniform(earlier);
 }
 
 // The number of distinct valid slot ids of the batch below slot a: its
@@ -222,22 +223,30 @@ struct OpBTile {
   }
 };
 
+// This thread's first 16 bytes of y in row `row` of the tile at n0: the
+// y update's first step, requested ahead of it.
+__device__ __forceinline__ u32x4 op_load_y0(const ModuleDesc &m, int row, int n0, int tile_len) {
+  const rsrc_t ry = make_rsrc(m.y + (int64_t)row * m.ldy + n0, (uint32_t)tile_len * 2);
+  const int t = threadIdx.x;
+  return buf_ld16(ry, t * 8 < tile_len ? (uint32_t)t * 16 : kOutOfRange, 0);
+}
+
 // y += delta for one row over one tile: the tile's sums wait in LDS; each
-// thread takes 8 consecutive outputs (16 bytes of y).  With use_pre, `pre`
-// holds this thread's y, requested early.  Q8: the B row scales multiply
-// the sums here.  Ends with a block barrier.
+// thread takes 8 consecutive outputs (16 bytes of y) per step.  y0 holds the
+// first step's y (op_load_y0), requested early.  Q8: the B row scales
+// multiply the sums here.  Ends with a block barrier.
 template <bool Q8>
 __device__ __forceinline__ void op_update_y(const ModuleDesc &m, const void *B, int row, int n0, int tile_len,
-                                            const float *delta, u32x4 pre, bool use_pre) {
+                                            const float *delta, u32x4 y0) {
   const int t = threadIdx.x;
   const rsrc_t ry = make_rsrc(m.y + (int64_t)row * m.ldy + n0, (uint32_t)tile_len * 2);
   // 8 columns per thread and step: a tile of up to kOpMaxTile columns takes
-  // kOpMaxTile / 2048 steps; `pre` holds the first step's y
+  // kOpMaxTile / 2048 steps
 #pragma unroll
   for (int step = 0; step < kOpMaxTile / (kDecodeThreads * 8); ++step) {
     const int col = (step * kDecodeThreads + t) * 8;
     if (col >= tile_len) break;
-    const u32x4 yv = use_pre && step == 0 ? pre : buf_ld16(ry, (uint32_t)col * 2, 0);
+    const u32x4 yv = step == 0 ? y0 : buf_ld16(ry, (uint32_t)col * 2, 0);
     float dl[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) dl[k] = delta[col + k];
@@ -262,7 +271,9 @@ __device__ __forceinline__ void op_update_y(const ModuleDesc &m, const void *B, 
 }
 
 // B.v for the staged rows rows[0, nr) over the block's tile (B in bt, v in
-// v_lds), added to their y.
+// v_lds), added to their y.  With use_pre, `pre` holds the first row's
+// op_load_y0; the other rows request theirs in the update (requesting each
+// one a row ahead measured no faster).
 template <int LPR, bool Q8>
 __device__ __forceinline__ void op_expand_rows(const ModuleDesc &m, const lora_adapter_entry_t &e,
                                                const OpBTile<LPR, Q8> &bt, int n0, int tile_len, const int *rows,
@@ -293,7 +304,8 @@ __device__ __forceinline__ void op_expand_rows(const ModuleDesc &m, const lora_a
       if (n < tile_len) delta[n] = acc[ii];
     }
     __syncthreads();
-    op_update_y<Q8>(m, e.B, uniform(rows[i]), n0, tile_len, delta, pre, use_pre && i == 0);
+    op_update_y<Q8>(m, e.B, uniform(rows[i]), n0, tile_len, delta,
+                    use_pre && i == 0 ? pre : op_load_y0(m, uniform(rows[i]), n0, tile_len));
   }
 }
 
@@ -307,7 +319,6 @@ __device__ __forceinline__ void op_delta(const ModuleDesc &m, const lora_adapter
                                          int a, int idu, bool bound_check, int max_seg, uint8_t *lds) {
   constexpr int JW = 2 << CLS;
   constexpr int LPR = 1 << CLS;
-  const int t = threadIdx.x;
   const int *s_rows = reinterpret_cast<const int *>(lds + kOpRowsOff);
   float *v_lds = reinterpret_cast<float *>(lds + kOpVOff);
   float *delta = reinterpret_cast<float *>(lds + kOpDeltaOff);
@@ -315,45 +326,43 @@ __device__ __forceinline__ void op_delta(const ModuleDesc &m, const lora_adapter
   const int tiles = min(tpb, m.op_n_tiles - tile0);  // this block's tiles: [tile0, tile0 + tiles)
   const int n0 = tile0 * m.op_nt;
   const int tile_len = min(m.op_nt, m.d_out - n0);
-  // 1. the row's first tile of y, requested before anything waits (a row whose
-  // adapter no other row shares, the case this path is planned for, needs
-  // nothing else); B follows the shrink
+  // 1. the row's first tile of y, requested before anything waits
   OpBTile<LPR, Q8> bt;
-  const rsrc_t ry = make_rsrc(m.y + (int64_t)row * m.ldy + n0, (uint32_t)tile_len * 2);
-  const u32x4 y_pre = buf_ld16(ry, t * 8 < tile_len ? (uint32_t)t * 16 : kOutOfRange, 0);
+  const u32x4 y_pre = op_load_y0(m, row, n0, tile_len);
   // the segment of the row, while those loads are in flight: the ballots
   // compare against a copy of the slot made here, so the wait for the ids
   // cannot be hoisted above the loads
   int a_here = a;
   asm volatile("" : "+s"(a_here));
-  int len;
-  if (!op_row_segment(row, a_here, idu, lds, &len)) return;  // an earlier row of this slot applies it
+  int len, pos;
+  op_row_segment(row, a_here, idu, lds, &len, &pos);
+  // the block of every kOpRowsPerBlock-th row of the segment takes that row
+  // and the next ones (one pass over A for all of them); the rest leave
+  if (pos % kOpRowsPerBlock != 0) return;
   if (bound_check &&  // the caller's bound on the segments: slots past it get no delta (counted by block 0)
       op_slot_rank(a_here, idu, reinterpret_cast<uint32_t *>(delta), reinterpret_cast<int *>(lds + kOpMiscOff)) >=
           max_seg)
     return;
-  if (len == 1) {
-    // 2. v of the row, 3. its tiles of y
-    op_shrink_rows<JW, 1, Q8>(m, e, s_rows, 1, v_lds);
-    for (int i = 0; i < tiles; ++i) {
-      const int ni = n0 + i * m.op_nt;
-      const int len_i = min(m.op_nt, m.d_out - ni);
-      bt.load(e.B, e.rank, m.d_out, ni, len_i);  // after the shrink: the registers of both do not fit
-      op_expand_rows<LPR, Q8>(m, e, bt, ni, len_i, s_rows, 1, v_lds, delta, y_pre, i == 0);
-    }
-    return;
-  }
-  constexpr int RG = 4;  // rows of x per pass over A
-  for (int r0 = 0; r0 < len; r0 += kOpGroup) {
-    const int nr = min(kOpGroup, len - r0);
-    for (int r1 = 0; r1 < nr; r1 += RG)
-      op_shrink_rows<JW, RG, Q8>(m, e, s_rows + r0 + r1, min(RG, nr - r1), v_lds + r1 * 64);
+  const int nr = min(kOpRowsPerBlock, len - pos);
+  const int *my_rows = s_rows + pos;  // my_rows[0] == row
+  // 2. v of the rows (every k of A), 3. their tiles of y; B follows the
+  // shrink: the registers of both do not fit
+  if (nr == 1) {  // a row whose adapter no other row shares: the case to be fast
+    op_shrink_rows<JW, 1, Q8>(m, e, my_rows, 1, v_lds);
     for (int i = 0; i < tiles; ++i) {
       const int ni = n0 + i * m.op_nt;
       const int len_i = min(m.op_nt, m.d_out - ni);
       bt.load(e.B, e.rank, m.d_out, ni, len_i);
-      op_expand_rows<LPR, Q8>(m, e, bt, ni, len_i, s_rows + r0, nr, v_lds, delta, zero4(), false);
+      op_expand_rows<LPR, Q8>(m, e, bt, ni, len_i, my_rows, 1, v_lds, delta, y_pre, i == 0);
     }
+    return;
+  }
+  op_shrink_rows<JW, kOpRowsPerBlock, Q8>(m, e, my_rows, nr, v_lds);
+  for (int i = 0; i < tiles; ++i) {
+    const int ni = n0 + i * m.op_nt;
+    const int len_i = min(m.op_nt, m.d_out - ni);
+    bt.load(e.B, e.rank, m.d_out, ni, len_i);
+    op_expand_rows<LPR, Q8>(m, e, bt, ni, len_i, my_rows, nr, v_lds, delta, y_pre, i == 0);
   }
 }
 

@@ -73,9 +73,10 @@ def algorithmic(w, ids=None):
                         [(m.name, m.index, m.d_in, m.d_out, m.x_name) for m in w.modules], w.ranks, w.fmt)
 
 
-def cpu_baseline(w, min_seconds=10.0, max_passes=64):
+def cpu_baseline(w, min_seconds=10.0, max_passes=100000):
     """The oracle (single-threaded C, fp64) on the same seeded inputs: whole
-    batches, repeated until about min_seconds of CPU work."""
+    batches, repeated until about min_seconds of CPU work (max_passes only
+    bounds a batch so small that a pass takes microseconds)."""
     import numpy as np
     import oracle
     try:

@@ -315,8 +315,7 @@ lora_status_t lora_apply_layer(const lora_module_io_t *io, uint32_t module_mask,
  * from L2 after the first), so the path is taken only while those repeated
  * reads stay within about 320 MB (one pass over A per block of a segment,
  * one more per 4 further rows, segments counted by seg.max_segments when
- * given).  Any
- * other batch runs the three launches of lora_build_segments +
+ * given).  Any other batch runs the three launches of lora_build_segments +
  * lora_apply_layer.  lora_decode_layer_launches tells which.  Both give
  * results within the oracle tolerance; the one-launch path sums A.x in a
  * different order, so its bits may differ from lora_apply_layer's.  Results

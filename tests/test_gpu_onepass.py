@@ -80,7 +80,8 @@ SHAPES = [
     (5, 300, 1032, 1000, 16, "distinct"),
     (64, 4, 2056, 520, 32, "random"),
     (65, 65, 3064, 4104, 16, "distinct"),
-    (40, 1, 1024, 2048, 8, "equal"),                          # one 40-row segment (groups of 16 rows)
+    (40, 1, 1024, 2048, 8, "equal"),                          # one 40-row segment (blocks of 4 rows)
+    (18, 1, 512, 520, 16, "equal"),                           # 18 rows: four blocks of 4 rows and one of 2
     (33, 9, 2048 + 24, 1024 + 8, (1, 3, 5, 12, 24, 28, 31, 7, 2), "random"),
     (200, 20, 512, 3000, (8, 16, 32), "random"),
     (256, 256, 4096, 2048, 16, "distinct"),
