@@ -20,7 +20,7 @@ __all__ = [
     "LoraError", "Segments", "segment_bound", "ModuleIO", "MODULES", "TABLE_ENTRY_DTYPE", "lib", "workspace_bytes",
     "build_segments", "shrink", "expand", "apply_layer", "apply_layer_noalloc", "decode_layer",
     "decode_layer_launches", "layer_shrink", "layer_expand", "pack_table", "STATIC_SCRATCH_BYTES",
-    "status_string", "MAX_RANK",
+    "status_string", "MAX_RANK", "host_lib",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -104,8 +104,35 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
+_host = None
+
+
+def host_lib() -> ctypes.CDLL:
+    """The library of the host-only calls (lora_form_batch, lora_status_string):
+    liblora_gemv.so, or with LORA_SANITIZE=1 in the environment their
+    AddressSanitizer + UndefinedBehaviorSanitizer build liblora_host_san.so
+    (``python -m adapter_gemv_amd.build --sanitize``; the process must have
+    the sanitizer runtime preloaded)."""
+    global _host
+    if _host is None:
+        if os.environ.get("LORA_SANITIZE") != "1":
+            return lib()
+        path = os.path.join(HERE, "liblora_host_san.so")
+        if not os.path.exists(path):
+            raise LoraError(f"{path} is missing: build it with `python -m adapter_gemv_amd.build --sanitize`")
+        L = ctypes.CDLL(path)
+        L.lora_status_string.restype = ctypes.c_char_p
+        L.lora_status_string.argtypes = [ctypes.c_int]
+        L.lora_form_batch.restype = ctypes.c_int
+        L.lora_form_batch.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+        _host = L
+    return _host
+
+
 def status_string(code: int) -> str:
-    return lib().lora_status_string(code).decode()
+    return host_lib().lora_status_string(code).decode()
 
 
 def _check(code: int, what: str):
@@ -402,7 +429,7 @@ def form_batch(adapters, max_batch: int, max_distinct: int, min_batch: int = 0, 
         raise LoraError("form_batch: waited_ms must match adapters")
     out = np.empty(max(1, min(int(max_batch), a.size)), np.int32)
     count = ctypes.c_int32(0)
-    code = lib().lora_form_batch(a.ctypes.data_as(ctypes.c_void_p), a.size,
+    code = host_lib().lora_form_batch(a.ctypes.data_as(ctypes.c_void_p), a.size,
                                  None if w is None else w.ctypes.data_as(ctypes.c_void_p), float(max_wait_ms),
                                  int(max_batch), int(max_distinct), int(min_batch), int(reserved_tail),
                                  out.ctypes.data_as(ctypes.c_void_p), ctypes.byref(count))

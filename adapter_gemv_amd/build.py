@@ -14,7 +14,12 @@ LIB = os.path.join(HERE, "liblora_gemv.so")
 INCLUDE = os.path.join(ROOT, "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "segments.hip", "kernels.hip", "batch_former.cpp"]
+SOURCES = ["api.hip", "segments.hip", "kernels.hip", "batch_former.cpp", "status.cpp"]
+# the host-only calls (lora_form_batch, lora_status_string), built apart with
+# the host compiler under AddressSanitizer and UndefinedBehaviorSanitizer
+HOST_SOURCES = ["batch_former.cpp", "status.cpp"]
+HOST_SAN_LIB = os.path.join(HERE, "liblora_host_san.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g", "-O1"]
 # the benchmark's read-ceiling kernel: a library of its own, outside the C ABI
 READ_CEILING_SRC = "read_ceiling.hip"
 READ_CEILING_LIB = os.path.join(HERE, "libread_ceiling.so")
@@ -36,6 +41,22 @@ def _compile(src: str) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError(f"hipcc failed on {src}")
     return obj
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """The host-only calls as liblora_host_san.so: g++ with ASan + UBSan (no
+    GPU code; loaded instead of liblora_gemv.so for them when LORA_SANITIZE=1)."""
+    tmp = HOST_SAN_LIB + ".tmp"
+    cmd = [os.environ.get("CXX", "g++"), "-std=c++17", "-fPIC", "-shared", "-Wall", *SANITIZE_FLAGS,
+           "-I", INCLUDE, *[os.path.join(CSRC, f) for f in HOST_SOURCES], "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("g++ failed on the sanitizer build of the host code")
+    os.replace(tmp, HOST_SAN_LIB)
+    if verbose:
+        print(f"built {HOST_SAN_LIB}")
+    return HOST_SAN_LIB
 
 
 def _build_read_ceiling() -> None:
@@ -69,4 +90,7 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--sanitize" in sys.argv[1:]:
+        build_host_sanitized(verbose=True)
+    else:
+        build(verbose=True)

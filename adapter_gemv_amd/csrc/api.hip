@@ -253,22 +253,6 @@ size_t lora_linear_workspace_bytes(int32_t num_rows, int32_t num_slots, int32_t 
   return part + vplanes > seg ? part + vplanes : seg;
 }
 
-const char *lora_status_string(lora_status_t status) {
-  switch (status) {
-    case LORA_OK: return "LORA_OK";
-    case LORA_ERR_NULL: return "LORA_ERR_NULL: a required pointer is NULL";
-    case LORA_ERR_SHAPE: return "LORA_ERR_SHAPE: a size or leading dimension is out of range";
-    case LORA_ERR_RANK: return "LORA_ERR_RANK: max_rank outside [1, LORA_MAX_RANK]";
-    case LORA_ERR_ALIGN: return "LORA_ERR_ALIGN: pointer or dimension not 16-byte / 8-element aligned";
-    case LORA_ERR_WORKSPACE: return "LORA_ERR_WORKSPACE: workspace too small";
-    case LORA_ERR_MODULE: return "LORA_ERR_MODULE: bad module index, n_mod or module mask";
-    case LORA_ERR_LAUNCH: return "LORA_ERR_LAUNCH: kernel launch failed";
-    case LORA_ERR_SCRATCH:
-      return "LORA_ERR_SCRATCH: the call needs more scratch than LORA_STATIC_SCRATCH_BYTES";
-  }
-  return "unknown lora_status_t";
-}
-
 lora_status_t lora_build_segments(const int32_t *row_adapter, int32_t num_rows, int32_t num_slots,
                                   lora_segments_t seg, void *ws, size_t ws_bytes, void *stream) {
   lora_status_t st = check_segments(seg);

@@ -45,6 +45,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lora_oracle.c")
 _LIB = os.path.join(_HERE, "liblora_oracle.so")
+# AddressSanitizer + UndefinedBehaviorSanitizer build, loaded instead when
+# LORA_SANITIZE=1 (the process must have the sanitizer runtime preloaded)
+_SAN_LIB = os.path.join(_HERE, "liblora_oracle_san.so")
+_SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _u16p = ctypes.POINTER(ctypes.c_uint16)
@@ -55,24 +59,33 @@ _vpp = ctypes.POINTER(ctypes.c_void_p)
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with the host C compiler (no fast-math, -O2)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile the oracle with the host C compiler (no fast-math, -O2); with
+    sanitize, its ASan + UBSan build liblora_oracle_san.so instead."""
+    out = _SAN_LIB if sanitize else _LIB
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
         subprocess.run(
             ["gcc", "-std=c99", "-O2", "-fno-fast-math", "-ffp-contract=off",
-             "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC],
+             "-fPIC", "-shared", "-Wall", "-Wextra", *(_SANITIZE_FLAGS if sanitize else []), "-o", tmp, _SRC],
             check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, out)
+    return out
+
+
+def library_path() -> str:
+    """The oracle library this process loads: the sanitizer build when
+    LORA_SANITIZE=1, else the plain one."""
+    return _SAN_LIB if os.environ.get("LORA_SANITIZE") == "1" else _LIB
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
-        _lib = _configure(ctypes.CDLL(_LIB))
+        path = library_path()
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+            build(force=True, sanitize=path == _SAN_LIB)
+        _lib = _configure(ctypes.CDLL(path))
     return _lib
 
 

@@ -159,7 +159,7 @@ lg = pytest.importorskip("adapter_gemv_amd")
 
 def _native_or_skip():
     try:
-        lg.lib()
+        lg.host_lib()
     except lg.LoraError as e:  # pragma: no cover - library not built
         pytest.skip(str(e))
 
