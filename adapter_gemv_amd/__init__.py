@@ -20,7 +20,7 @@ __all__ = [
     "LoraError", "Segments", "segment_bound", "ModuleIO", "MODULES", "TABLE_ENTRY_DTYPE", "lib", "workspace_bytes",
     "build_segments", "shrink", "expand", "apply_layer", "apply_layer_noalloc", "decode_layer",
     "decode_layer_launches", "layer_shrink", "layer_expand", "pack_table", "STATIC_SCRATCH_BYTES",
-    "status_string", "MAX_RANK", "host_lib",
+    "status_string", "MAX_RANK", "host_lib", "LinearIO", "LinearQ4IO", "Q4_GROUP",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -54,6 +54,12 @@ class _IO(ctypes.Structure):
 class _LinIO(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("ldx", ctypes.c_int64), ("W", ctypes.c_void_p), ("ldw", ctypes.c_int64),
                 ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64), ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32)]
+
+
+class _LinQ4IO(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("ldx", ctypes.c_int64), ("Wq", ctypes.c_void_p), ("ldwq", ctypes.c_int64),
+                ("Ws", ctypes.c_void_p), ("lds", ctypes.c_int64), ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64),
+                ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32)]
 
 
 _lib = None
@@ -98,6 +104,10 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.restype = st
             f.argtypes = [ctypes.POINTER(_LinIO), u32, i32, vp, vp, i32, _Seg, i32, vp, sz, vp]
+        for name in ("lora_linear_layer_q4", "lora_linear_shrink_q4", "lora_linear_expand_q4"):
+            f = getattr(L, name)
+            f.restype = st
+            f.argtypes = [ctypes.POINTER(_LinQ4IO), u32, i32, vp, vp, i32, _Seg, i32, vp, sz, vp]
         L.lora_form_batch.restype = st
         L.lora_form_batch.argtypes = [vp, i32, vp, ctypes.c_float, i32, i32, i32, i32, vp, vp]
         _lib = L
@@ -237,6 +247,21 @@ class LinearIO:
         self.d_out = int(W.shape[0] if d_out is None else d_out)
 
 
+Q4_GROUP = 128  # LORA_Q4_GROUP
+
+
+class LinearQ4IO:
+    """One projection for linear_layer_q4: x [rows, >= d_in] bf16, Wq uint8
+    [d_out, >= d_in / 2] (packed signed 4-bit weights, the even input in the
+    low nibble), Ws float32 [d_out, >= d_in / Q4_GROUP] (group scales), y
+    [rows, >= d_out] bf16 (written)."""
+
+    def __init__(self, x, Wq, Ws, y, d_in=None, d_out=None):
+        self.x, self.Wq, self.Ws, self.y = x, Wq, Ws, y
+        self.d_in = int(x.shape[1] if d_in is None else d_in)
+        self.d_out = int(Wq.shape[0] if d_out is None else d_out)
+
+
 def linear_workspace_bytes(num_rows: int, num_slots: int, max_rank: int, sum_d_in: int, n_modules: int) -> int:
     return int(lib().lora_linear_workspace_bytes(num_rows, num_slots, max_rank, sum_d_in, n_modules))
 
@@ -244,22 +269,34 @@ def linear_workspace_bytes(num_rows: int, num_slots: int, max_rank: int, sum_d_i
 def linear_layer(ios, num_rows, row_adapter, table, num_slots, seg, max_rank, ws, stream=None, module_mask=None,
                  _fn="lora_linear_layer"):
     """Base projection + delta of every projection in ``ios`` ({name:
-    LinearIO}); see lora_linear_layer."""
+    LinearIO}, or {name: LinearQ4IO} for 4-bit base weights); see
+    lora_linear_layer and lora_linear_layer_q4."""
     import torch
     _need(row_adapter, torch.int32, "row_adapter", 1)
-    arr = (_LinIO * 7)()
+    q4 = any(isinstance(io, LinearQ4IO) for io in ios.values())
+    arr = ((_LinQ4IO if q4 else _LinIO) * 7)()
     mask = 0
     for i, name in enumerate(MODULES):
         io = ios.get(name)
         if io is None:
             continue
-        for t, what in ((io.x, "x"), (io.W, "W"), (io.y, "y")):
+        if isinstance(io, LinearQ4IO) != q4:
+            raise TypeError("linear_layer: every projection LinearIO, or every projection LinearQ4IO")
+        for t, what in ((io.x, "x"), (io.y, "y")) + (() if q4 else ((io.W, "W"),)):
             _need(t, torch.bfloat16, f"{name}.{what}", 2)
         if io.x.shape[0] < num_rows or io.y.shape[0] < num_rows:
             raise ValueError(f"{name}: fewer rows than num_rows")
-        arr[i] = _LinIO(io.x.data_ptr(), io.x.stride(0), io.W.data_ptr(), io.W.stride(0), io.y.data_ptr(),
-                        io.y.stride(0), io.d_in, io.d_out)
+        if q4:
+            _need(io.Wq, torch.uint8, f"{name}.Wq", 2)
+            _need(io.Ws, torch.float32, f"{name}.Ws", 2)
+            arr[i] = _LinQ4IO(io.x.data_ptr(), io.x.stride(0), io.Wq.data_ptr(), io.Wq.stride(0), io.Ws.data_ptr(),
+                              io.Ws.stride(0), io.y.data_ptr(), io.y.stride(0), io.d_in, io.d_out)
+        else:
+            arr[i] = _LinIO(io.x.data_ptr(), io.x.stride(0), io.W.data_ptr(), io.W.stride(0), io.y.data_ptr(),
+                            io.y.stride(0), io.d_in, io.d_out)
         mask |= 1 << i
+    if q4:
+        _fn += "_q4"
     _check(getattr(lib(), _fn)(arr, mask if module_mask is None else module_mask, num_rows, _ptr(row_adapter),
                                _ptr(table), num_slots, seg.c(), max_rank, _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(stream)), _fn)

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "lora_internal.h"
 
@@ -508,13 +509,51 @@ lora_status_t lora_apply_layer_stacked(const lora_module_io_t *io, uint32_t modu
 
 namespace {
 
+// One projection of a fused call, from either io struct.
+struct LinearArgs {
+  const void *x;
+  int64_t ldx;
+  const void *W;   // bf16 [d_out][ldw] elements, or 4-bit [d_out][ldw] bytes
+  int64_t ldw;
+  const float *Ws; // 4-bit: group scales [d_out][ldws]
+  int64_t ldws;
+  void *y;
+  int64_t ldy;
+  int32_t d_in, d_out;
+};
+
+lora_status_t check_linear(const lora_linear_io_t &m, LinearArgs *a) {
+  if (!m.x || !m.y || !m.W) return LORA_ERR_NULL;
+  if (m.d_in <= 0 || m.d_out <= 0 || m.ldx < m.d_in || m.ldy < m.d_out || m.ldw < m.d_in) return LORA_ERR_SHAPE;
+  if ((m.d_in & 7) || (m.d_out & 7) || (m.ldx & 7) || (m.ldy & 7) || (m.ldw & 7) || !aligned16(m.x) ||
+      !aligned16(m.y) || !aligned16(m.W))
+    return LORA_ERR_ALIGN;
+  if (!fits_u32(m.d_out, m.ldw)) return LORA_ERR_SHAPE;
+  *a = LinearArgs{m.x, m.ldx, m.W, m.ldw, nullptr, 0, m.y, m.ldy, m.d_in, m.d_out};
+  return LORA_OK;
+}
+
+lora_status_t check_linear(const lora_linear_q4_io_t &m, LinearArgs *a) {
+  if (!m.x || !m.y || !m.Wq || !m.Ws) return LORA_ERR_NULL;
+  if (m.d_in <= 0 || m.d_out <= 0 || m.ldx < m.d_in || m.ldy < m.d_out) return LORA_ERR_SHAPE;
+  if ((m.d_in % LORA_Q4_GROUP) || (m.d_out & 7) || (m.ldx & 7) || (m.ldy & 7) || (m.ldwq & 15) ||
+      !aligned16(m.x) || !aligned16(m.y) || !aligned16(m.Wq) || (reinterpret_cast<uintptr_t>(m.Ws) & 3))
+    return LORA_ERR_ALIGN;
+  if (m.ldwq < m.d_in / 2 || m.lds < m.d_in / LORA_Q4_GROUP) return LORA_ERR_SHAPE;
+  if ((int64_t)m.d_out * m.ldwq > (int64_t)0xFFFFFF00 || (int64_t)m.d_out * m.lds * 4 > (int64_t)0xFFFFFF00)
+    return LORA_ERR_SHAPE;
+  *a = LinearArgs{m.x, m.ldx, m.Wq, m.ldwq, static_cast<const float *>(m.Ws), m.lds, m.y, m.ldy, m.d_in, m.d_out};
+  return LORA_OK;
+}
+
 // Base projection + delta: the grouped shrink and the partials summed into one
 // v plane per projection (original row order) (do_shrink), then the fused
-// kernel (do_fused).
-lora_status_t linear_phase(bool do_shrink, bool do_fused, const lora_linear_io_t *io, uint32_t module_mask,
-                           int32_t num_rows, const int32_t *row_adapter, const lora_adapter_entry_t *table,
-                           int32_t num_slots, lora_segments_t seg, int32_t max_rank, void *ws, size_t ws_bytes,
-                           void *stream) {
+// kernel (do_fused).  IO: lora_linear_io_t (bf16 base) or lora_linear_q4_io_t.
+template <typename IO>
+lora_status_t linear_phase(bool do_shrink, bool do_fused, const IO *io, uint32_t module_mask, int32_t num_rows,
+                           const int32_t *row_adapter, const lora_adapter_entry_t *table, int32_t num_slots,
+                           lora_segments_t seg, int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
+  constexpr bool kQ4 = std::is_same<IO, lora_linear_q4_io_t>::value;
   if (!io || !table) return LORA_ERR_NULL;
   lora_status_t st = check_segments(seg);
   if (st != LORA_OK) return st;
@@ -523,17 +562,15 @@ lora_status_t linear_phase(bool do_shrink, bool do_fused, const lora_linear_io_t
   if (max_rank < 1 || max_rank > LORA_MAX_RANK) return LORA_ERR_RANK;
   if (num_rows > 0 && !row_adapter) return LORA_ERR_NULL;
   ModuleArgs ms[LORA_NUM_MODULES];
+  LinearArgs la[LORA_NUM_MODULES];
   int n = 0;
   int64_t sum_d_in = 0;
   for (int c = 0; c < LORA_NUM_MODULES; ++c) {
     if (!(module_mask & (1u << c))) continue;
-    const lora_linear_io_t &m = io[c];
-    if (!m.x || !m.y || !m.W) return LORA_ERR_NULL;
-    if (m.d_in <= 0 || m.d_out <= 0 || m.ldx < m.d_in || m.ldy < m.d_out || m.ldw < m.d_in) return LORA_ERR_SHAPE;
-    if ((m.d_in & 7) || (m.d_out & 7) || (m.ldx & 7) || (m.ldy & 7) || (m.ldw & 7) || !aligned16(m.x) ||
-        !aligned16(m.y) || !aligned16(m.W))
-      return LORA_ERR_ALIGN;
-    if (!fits_u32(num_rows, m.ldx) || !fits_u32(num_rows, m.ldy) || !fits_u32(m.d_out, m.ldw)) return LORA_ERR_SHAPE;
+    st = check_linear(io[c], &la[n]);
+    if (st != LORA_OK) return st;
+    const LinearArgs &m = la[n];
+    if (!fits_u32(num_rows, m.ldx) || !fits_u32(num_rows, m.ldy)) return LORA_ERR_SHAPE;
     ms[n] = ModuleArgs{m.x, m.ldx, m.y, m.ldy, m.d_in, m.d_out, c};
     sum_d_in += m.d_in;
     ++n;
@@ -566,12 +603,14 @@ lora_status_t linear_phase(bool do_shrink, bool do_fused, const lora_linear_io_t
   const int row_tiles = (num_rows + kFusedRows - 1) / kFusedRows;
   int64_t blocks = 0;
   for (int i = 0; i < n; ++i) {
-    const lora_linear_io_t &m = io[ms[i].col];
+    const LinearArgs &m = la[i];
     FusedModule &fm = f.mod[i];
     fm.x = static_cast<const uint16_t *>(m.x);
     fm.ldx = m.ldx;
-    fm.W = static_cast<const uint16_t *>(m.W);
+    fm.W = m.W;
     fm.ldw = m.ldw;
+    fm.Ws = m.Ws;
+    fm.ldws = m.ldws;
     fm.y = static_cast<uint16_t *>(m.y);
     fm.ldy = m.ldy;
     fm.v = vplanes + (int64_t)i * num_rows * rs;
@@ -595,7 +634,7 @@ lora_status_t linear_phase(bool do_shrink, bool do_fused, const lora_linear_io_t
   f.num_segments = seg.num_segments;
   f.seg_adapter = seg.seg_adapter;
   f.max_seg = segment_bound(num_rows, num_slots, seg);
-  return launched(launch_fused(f, (int)blocks, s));
+  return launched(launch_fused(f, kQ4, (int)blocks, s));
 }
 
 }  // namespace
@@ -619,6 +658,29 @@ lora_status_t lora_linear_shrink(const lora_linear_io_t *io, uint32_t module_mas
 lora_status_t lora_linear_expand(const lora_linear_io_t *io, uint32_t module_mask, int32_t num_rows,
                                  const int32_t *row_adapter, const lora_adapter_entry_t *table, int32_t num_slots,
                                  lora_segments_t seg, int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
+  return linear_phase(false, true, io, module_mask, num_rows, row_adapter, table, num_slots, seg, max_rank, ws,
+                      ws_bytes, stream);
+}
+
+lora_status_t lora_linear_layer_q4(const lora_linear_q4_io_t *io, uint32_t module_mask, int32_t num_rows,
+                                   const int32_t *row_adapter, const lora_adapter_entry_t *table, int32_t num_slots,
+                                   lora_segments_t seg, int32_t max_rank, void *ws, size_t ws_bytes, void *stream) {
+  return linear_phase(true, true, io, module_mask, num_rows, row_adapter, table, num_slots, seg, max_rank, ws,
+                      ws_bytes, stream);
+}
+
+lora_status_t lora_linear_shrink_q4(const lora_linear_q4_io_t *io, uint32_t module_mask, int32_t num_rows,
+                                    const int32_t *row_adapter, const lora_adapter_entry_t *table,
+                                    int32_t num_slots, lora_segments_t seg, int32_t max_rank, void *ws,
+                                    size_t ws_bytes, void *stream) {
+  return linear_phase(true, false, io, module_mask, num_rows, row_adapter, table, num_slots, seg, max_rank, ws,
+                      ws_bytes, stream);
+}
+
+lora_status_t lora_linear_expand_q4(const lora_linear_q4_io_t *io, uint32_t module_mask, int32_t num_rows,
+                                    const int32_t *row_adapter, const lora_adapter_entry_t *table,
+                                    int32_t num_slots, lora_segments_t seg, int32_t max_rank, void *ws,
+                                    size_t ws_bytes, void *stream) {
   return linear_phase(false, true, io, module_mask, num_rows, row_adapter, table, num_slots, seg, max_rank, ws,
                       ws_bytes, stream);
 }

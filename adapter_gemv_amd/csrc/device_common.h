@@ -141,6 +141,19 @@ __device__ __forceinline__ u32x4 i8x8_to_bf16x8(u32x2 q) {
   }
   return u32x4{o[0], o[1], o[2], o[3]};
 }
+// Eight signed 4-bit values (one dword, value j in bits 4j .. 4j+3, two's
+// complement) as eight bf16 values: each is sign-extended and converted to
+// fp32, whose upper half is then the exact bf16 (|q| <= 8 needs 4 bits).
+__device__ __forceinline__ u32x4 q4x8_to_bf16x8(uint32_t q) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = (float)((int32_t)(q << (28 - 8 * i)) >> 28);
+    const float hi = (float)((int32_t)(q << (24 - 8 * i)) >> 28);
+    o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+  }
+  return u32x4{o[0], o[1], o[2], o[3]};
+}
 // Eight int8 values (one 8-byte load) times eight floats, in fp32: each byte
 // is sign-extended and converted exactly, then multiplied and added.
 __device__ __forceinline__ float dot8_i8_f32(u32x2 q, const float *v, float c) {

@@ -59,9 +59,11 @@ struct FusedRowLoads {
   f32x4_t v[2];
 };
 
+// Q4: the base weight is 4-bit with group scales (lora_linear_layer_q4).
+template <bool Q4>
 __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t *lds) {
   constexpr int XL = kFusedRows * 8 / 256;   // x pieces per thread per round (4)
-  constexpr int WL = kFusedCols * 8 / 256;   // W pieces per thread per round (2)
+  constexpr int WL = kFusedCols * 8 / 256;   // bf16 W pieces per thread per round (2)
   constexpr int RPW = kFusedRows / 4;        // epilogue rows per wave (32)
   const int t = threadIdx.x, lane = t & 63, w = wave_id();
   const FusedModule m = fused_module_of(f, blk);
@@ -91,15 +93,22 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
     const int r = row0 + i * 32 + (t >> 3);
     xoff[i] = r < f.num_rows ? (uint32_t)((int64_t)r * m.ldx * 2) : kOutOfRange;
   }
-  const rsrc_t rw = make_rsrc(m.W, (uint32_t)((int64_t)m.d_out * m.ldw * 2));
-  uint32_t woff[WL];
+  // W of a round: bf16, WL pieces of 8 values per thread (rows 32i + t/8);
+  // 4-bit, one 8-byte piece of 16 values per thread (row t/4, values
+  // 16 (t%4) .. +16 of the round), widened to bf16 on the way into LDS
+  const int64_t w_row_bytes = Q4 ? m.ldw : m.ldw * 2;
+  const rsrc_t rw = make_rsrc(m.W, (uint32_t)((int64_t)m.d_out * w_row_bytes));
+  constexpr int WP = Q4 ? 1 : WL;
+  uint32_t woff[WP];
 #pragma unroll
-  for (int i = 0; i < WL; ++i) {
-    const int n = n0 + i * 32 + (t >> 3);
-    woff[i] = n < m.d_out ? (uint32_t)((int64_t)n * m.ldw * 2) : kOutOfRange;
+  for (int i = 0; i < WP; ++i) {
+    const int n = n0 + (Q4 ? (t >> 2) : i * 32 + (t >> 3));
+    woff[i] = n < m.d_out ? (uint32_t)((int64_t)n * w_row_bytes) : kOutOfRange;
   }
+  using WRaw = typename std::conditional<Q4, u32x2, u32x4>::type;
   struct Stage {
-    u32x4 x[XL], wv[WL];
+    u32x4 x[XL];
+    WRaw wv[WP];
   };
   auto load = [&](Stage &st, int k0) {  // one round; past d_in: zero, no traffic
     const int k = k0 + piece * 8;
@@ -107,15 +116,28 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
     const uint32_t kb = (uint32_t)k * 2;
 #pragma unroll
     for (int i = 0; i < XL; ++i) st.x[i] = buf_ld16(rx, kon && xoff[i] != kOutOfRange ? xoff[i] + kb : kOutOfRange, 0);
+    if constexpr (Q4) {
+      const int kq = k0 + 16 * (t & 3);
+      st.wv[0] = __builtin_amdgcn_raw_buffer_load_b64(
+          rw, kq < m.d_in && woff[0] != kOutOfRange ? woff[0] + (uint32_t)kq / 2 : kOutOfRange, 0, kNonTemporal);
+    } else {
 #pragma unroll
-    for (int i = 0; i < WL; ++i)
-      st.wv[i] = buf_ld16_stream(rw, kon && woff[i] != kOutOfRange ? woff[i] + kb : kOutOfRange, 0);
+      for (int i = 0; i < WL; ++i)
+        st.wv[i] = buf_ld16_stream(rw, kon && woff[i] != kOutOfRange ? woff[i] + kb : kOutOfRange, 0);
+    }
   };
   auto store = [&](const Stage &st, uint8_t *buf) {
 #pragma unroll
     for (int i = 0; i < XL; ++i) *(u32x4 *)(buf + shrink_lds_off(i * 32 + (t >> 3), piece)) = st.x[i];
+    if constexpr (Q4) {
+      const int row = t >> 2, p0 = 2 * (t & 3);
+      *(u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(row, p0)) = q4x8_to_bf16x8(st.wv[0].x);
+      *(u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(row, p0 + 1)) = q4x8_to_bf16x8(st.wv[0].y);
+    } else {
 #pragma unroll
-    for (int i = 0; i < WL; ++i) *(u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(i * 32 + (t >> 3), piece)) = st.wv[i];
+      for (int i = 0; i < WL; ++i)
+        *(u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(i * 32 + (t >> 3), piece)) = st.wv[i];
+    }
   };
   f32x4_t acc[2][4];
 #pragma unroll
@@ -123,7 +145,7 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int r_in = lane & 15, g = lane >> 4;
-  auto compute = [&](const uint8_t *buf) {
+  auto compute = [&](const uint8_t *buf, f32x4_t (&acc)[2][4]) {
 #pragma unroll
     for (int ks = 0; ks < kShrinkRound / 32; ++ks) {
       u32x4 xo[2], wo[4];
@@ -141,6 +163,26 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
                                                                 0, 0);
     }
   };
+  // 4-bit: the two rounds of a main-loop step are one group of kQ4Group
+  // inputs; its sums collect apart and meet the group's scale of each
+  // output column (this lane's columns n0 + 16 nt + r_in), requested one
+  // step ahead
+  static_assert(2 * kShrinkRound == kQ4Group, "one group per main-loop step");
+  f32x4_t gacc[Q4 ? 2 : 1][Q4 ? 4 : 1];
+  float sc_cur[4] = {0.f, 0.f, 0.f, 0.f}, sc_nxt[4] = {0.f, 0.f, 0.f, 0.f};
+  const rsrc_t rs_w = make_rsrc(Q4 ? m.Ws : nullptr, Q4 ? (uint32_t)((int64_t)m.d_out * m.ldws * 4) : 0u);
+  const int n_groups = Q4 ? m.d_in / kQ4Group : 0;
+  auto load_scales = [&](float (&sc)[4], int grp) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int n = n0 + nt * 16 + r_in;
+      sc[nt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             rs_w, n < m.d_out && grp < n_groups ?
+                                                       (uint32_t)(((int64_t)n * m.ldws + grp) * 4) : kOutOfRange,
+                                             0, 0));
+    }
+  };
+  if constexpr (Q4) load_scales(sc_cur, 0);
   // Two rounds in flight; round i goes to buffer i & 1 (see the SGMV shrink).
   Stage s0, s1;
   load(s0, 0);
@@ -148,14 +190,34 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
   const int rounds = (m.d_in + kShrinkRound - 1) / kShrinkRound;
   for (int r = 0; r < rounds; r += 2) {
     uint8_t *b0 = lds, *b1 = lds + kShrinkBufBytes;
+    if constexpr (Q4) {
+      load_scales(sc_nxt, r / 2 + 1);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) gacc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
     store(s0, b0);
     load(s0, (r + 2) * kShrinkRound);
     __syncthreads();
-    compute(b0);
+    if constexpr (Q4) compute(b0, gacc);
+    else compute(b0, acc);
     store(s1, b1);
     load(s1, (r + 3) * kShrinkRound);
     __syncthreads();
-    compute(b1);
+    if constexpr (Q4) {
+      compute(b1, gacc);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(sc_cur[nt], gacc[mt][nt][i], acc[mt][nt][i]);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) sc_cur[nt] = sc_nxt[nt];
+    } else {
+      compute(b1, acc);
+    }
   }
   __syncthreads();  // every wave is done with the round buffers
 

@@ -141,9 +141,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void l
 }
 
 // Base projection + delta (fused_items.h).
+template <bool Q4>
 __global__ __launch_bounds__(256) void lora_fused_kernel(FusedDesc f) {
   __shared__ __align__(16) uint8_t lds[kFusedLdsBytes];
-  fused_block(f, blockIdx.x, lds);
+  fused_block<Q4>(f, blockIdx.x, lds);
 }
 
 int rank_class(int max_rank) { return max_rank <= 8 ? 0 : max_rank <= 16 ? 1 : max_rank <= 32 ? 2 : 3; }
@@ -197,9 +198,10 @@ hipError_t launch_onepass(const OnePassDesc &d, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_fused(const FusedDesc &f, int blocks, hipStream_t stream) {
+hipError_t launch_fused(const FusedDesc &f, bool q4, int blocks, hipStream_t stream) {
   if (blocks <= 0) return hipSuccess;
-  lora_fused_kernel<<<blocks, 256, 0, stream>>>(f);
+  if (q4) lora_fused_kernel<true><<<blocks, 256, 0, stream>>>(f);
+  else lora_fused_kernel<false><<<blocks, 256, 0, stream>>>(f);
   return hipGetLastError();
 }
 

@@ -102,11 +102,18 @@ struct LayerDesc {
 constexpr int kFusedRows = 128;
 constexpr int kFusedCols = 64;
 
+// 4-bit base weights: inputs per scale (a group of consecutive inputs of one
+// output row); the fused kernel's two 64-k rounds per main-loop step make one.
+constexpr int kQ4Group = LORA_Q4_GROUP;
+static_assert(kQ4Group == 128, "the fused kernel scales one group per two 64-k rounds");
+
 struct FusedModule {
   const uint16_t *x;  // [num_rows][ldx]
   int64_t ldx;
-  const uint16_t *W;  // [d_out][ldw], bf16 base weight
+  const void *W;      // bf16 base weight [d_out][ldw] elements, or 4-bit [d_out][ldw] bytes
   int64_t ldw;
+  const float *Ws;    // 4-bit base weight: fp32 group scales [d_out][ldws]
+  int64_t ldws;
   uint16_t *y;        // [num_rows][ldy], written
   int64_t ldy;
   const float *v;     // [num_rows][rs]: the row's unscaled rank-r vector
@@ -135,7 +142,8 @@ struct FusedDesc {
   int32_t max_seg;
 };
 
-hipError_t launch_fused(const FusedDesc &f, int blocks, hipStream_t stream);
+// q4: the base weights of every projection are 4-bit with group scales.
+hipError_t launch_fused(const FusedDesc &f, bool q4, int blocks, hipStream_t stream);
 
 // ---- One-launch decode (lora_decode_layer on batches of distinct
 // adapters): the grouping of the rows, the shrink and the expand of every

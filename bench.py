@@ -41,6 +41,9 @@ DESCRIPTIONS = {
                      "style adapter of its own (rank 16), all 7 projections, 128 rows; one pass per adapter",
     "fused_layer_r64": "70B full layer decode, base projection + delta fused: bf16 W of all 7 projections (1.63 GB) "
                        "and 128 distinct rank-64 adapters, 128 rows; y written once",
+    "fused_layer_q4_r64": "70B full layer decode, base projection + delta fused with a 4-bit base: signed 4-bit W "
+                          "of all 7 projections with one fp32 scale per 128 inputs (0.43 GB), 120 rows with distinct "
+                          "rank-64 adapters and 8 base-only rows; y written once",
 }
 
 
@@ -255,7 +258,7 @@ def counter_traffic(workload, kernel):
 
 def _short_kernel_name(name):
     import re
-    m = re.search(r"(\w+_kernel)(<\d+>)?", name)
+    m = re.search(r"(\w+_kernel)(<\w+>)?", name)
     return (m.group(1) + (m.group(2) or "")) if m else name.strip('"')[:60]
 
 
@@ -421,9 +424,12 @@ def main():
         w, former = formed_workload(gen)
     else:
         w = gen.make_workload(args.workload)
+    q4 = w.W is not None and hasattr(next(iter(w.W.values())), "scales")
     if w.W is not None:  # fused: + the base weights, y written once (not read)
         traffic = algorithmic(w)
-        w_bytes = sum(2 * m.d_in * m.d_out for m in w.modules)
+        # bf16: 2 bytes per weight; 4-bit: half a byte per weight and 4 bytes per group scale
+        w_bytes = sum(m.d_in * m.d_out // 2 + m.d_out * (m.d_in // gen.Q4_GROUP) * 4 if q4 else
+                      2 * m.d_in * m.d_out for m in w.modules)
         y_write = traffic["y"] // 2
         b_bytes = traffic["expand_bytes"] - traffic["y"]
         traffic["total"] = w_bytes + traffic["adapters"] + traffic["x"] + y_write
@@ -561,7 +567,8 @@ def main():
                                                         stream))
         per_pass.append({"segments": seg_us, "shrink": shr_us, "expand": exp_us})
         for ph, us in (("shrink", shr_us), ("expand", exp_us)):
-            name = "lora_fused_kernel" if (w.W is not None and ph == "expand") else f"lora_{ph}_kernel<{rank_class(r)}>"
+            name = f"lora_fused_kernel<{'true' if q4 else 'false'}>" if (w.W is not None and ph == "expand") \
+                else f"lora_{ph}_kernel<{rank_class(r)}>"
             k = kernels.setdefault(name, [0, 0.0, 0])
             k[0] += 1
             k[1] += us
@@ -591,7 +598,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8xbf16" if (w.fmt != 0).any() else "bf16",  # int8 factors: exact in bf16/fp32 products
+        # int8 factors, 4-bit base: integers exact in the bf16/fp32 products
+        "dtype": "int4xbf16" if q4 else "int8xbf16" if (w.fmt != 0).any() else "bf16",
         "data": "synthetic (seeded, shapes of the pages' 70B workloads)",
         "config": {"workload": DESCRIPTIONS[args.workload], "name": args.workload, "rows": w.num_rows,
                    "distinct_adapters": int(len(np.unique(w.ids[w.ids >= 0]))),
@@ -629,8 +637,10 @@ def main():
     }
     if former is not None:
         out["batch_former"] = former
-    if w.W is not None:
+    if w.W is not None and not q4:  # torch has no 4-bit GEMM to compare with
         out["fused"] = fused_comparison(w, dws[0], lg, stream, args.steps, traffic)
+    elif q4:
+        out["fused"] = {"base_weight_bytes": traffic["base_weights"], "base_format": "4-bit, fp32 scale per 128"}
     if stack is not None:
         out["stacked"] = {"depth": len(per_pass), "pass_max_rank": pass_rank,
                           "passes_us": [{k: round(v, 2) for k, v in p.items()} for p in per_pass],

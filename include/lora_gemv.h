@@ -440,6 +440,67 @@ lora_status_t lora_linear_expand(const lora_linear_io_t *io, uint32_t module_mas
                                  lora_segments_t seg, int32_t max_rank, void *ws,
                                  size_t ws_bytes, void *stream);
 
+/* Inputs of a row of a 4-bit base weight that share one scale. */
+#define LORA_Q4_GROUP 128
+
+/* One projection of a layer with a 4-bit base weight, for
+ * lora_linear_layer_q4.  W[n][k] = Ws[n][k / LORA_Q4_GROUP] * q[n][k], with
+ * q[n][k] the signed 4-bit value (two's complement, -8 .. 7) in byte k / 2 of
+ * row n of Wq: the low nibble for even k, the high nibble for odd k. */
+typedef struct lora_linear_q4_io {
+  const void *x;  /* device, bf16 [num_rows][ldx]                            */
+  int64_t ldx;
+  const void *Wq; /* device, uint8 [d_out][ldwq]: packed 4-bit weights      */
+  int64_t ldwq;   /* bytes per row: >= d_in / 2, a multiple of 16           */
+  const void *Ws; /* device, fp32 [d_out][lds]: the group scales            */
+  int64_t lds;    /* floats per row: >= d_in / LORA_Q4_GROUP                */
+  void *y;        /* device, bf16 [num_rows][ldy]: written, W.x + delta     */
+  int64_t ldy;
+  int32_t d_in;   /* a multiple of LORA_Q4_GROUP                            */
+  int32_t d_out;
+} lora_linear_q4_io_t;
+
+/*
+ * lora_linear_layer_q4 -- lora_linear_layer with 4-bit base weights: the
+ * base dequantised in the kernel, the BF16 (or int8) adapter term added in
+ * its epilogue and the sum accumulated in fp32 before the one bf16 rounding.
+ * Rows with an adapter and base-only rows (id negative or >= num_slots) mix
+ * in one batch.  Source: "12. Adapter Serving and Multi-Tenant
+ * Customization", "Interactions with other engine mechanisms", Quantization
+ * (an INT4 base with BF16 adapters: dequantise the base, add the adapter
+ * contribution, accumulate wide; one batch mixes rows with and without an
+ * adapter).  The matrix cores take each 4-bit value exactly (as bf16) and
+ * each group's sum is scaled once, in fp32.
+ *
+ *   io           array of LORA_NUM_MODULES entries, read where module_mask
+ *                has a bit: x, Wq, y 16-byte aligned, Ws 4-byte aligned;
+ *                d_out, ldx, ldy multiples of 8; Wq and Ws below 4 GiB
+ *   other arguments as for lora_linear_layer (the same workspace size).
+ *
+ * Errors: those of lora_linear_layer; LORA_ERR_NULL for a null Wq or Ws,
+ * LORA_ERR_ALIGN for a d_in that is not a multiple of LORA_Q4_GROUP or an
+ * ldwq that is not a multiple of 16, LORA_ERR_SHAPE for ldwq < d_in / 2 or
+ * lds < d_in / LORA_Q4_GROUP.
+ */
+lora_status_t lora_linear_layer_q4(const lora_linear_q4_io_t *io, uint32_t module_mask,
+                                   int32_t num_rows, const int32_t *row_adapter,
+                                   const lora_adapter_entry_t *table, int32_t num_slots,
+                                   lora_segments_t seg, int32_t max_rank, void *ws,
+                                   size_t ws_bytes, void *stream);
+
+/* The two parts of lora_linear_layer_q4, as for lora_linear_shrink and
+ * lora_linear_expand. */
+lora_status_t lora_linear_shrink_q4(const lora_linear_q4_io_t *io, uint32_t module_mask,
+                                    int32_t num_rows, const int32_t *row_adapter,
+                                    const lora_adapter_entry_t *table, int32_t num_slots,
+                                    lora_segments_t seg, int32_t max_rank, void *ws,
+                                    size_t ws_bytes, void *stream);
+lora_status_t lora_linear_expand_q4(const lora_linear_q4_io_t *io, uint32_t module_mask,
+                                    int32_t num_rows, const int32_t *row_adapter,
+                                    const lora_adapter_entry_t *table, int32_t num_slots,
+                                    lora_segments_t seg, int32_t max_rank, void *ws,
+                                    size_t ws_bytes, void *stream);
+
 /* Most adapters one row may carry in lora_apply_layer_stacked. */
 #define LORA_MAX_STACK 8
 

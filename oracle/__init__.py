@@ -100,6 +100,13 @@ def _configure(lib):
         _u16p, ctypes.c_int64, ctypes.c_int32,
         _i32p, ctypes.c_int32, _vpp, _vpp, _i32p, _f32p, _i32p, ctypes.c_int32,
         _i32p, ctypes.c_int32, _f64p, _f64p, _f64p, _f64p]
+    lib.oracle_base_bf16.restype = None
+    lib.oracle_base_bf16.argtypes = [_u16p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _u16p, ctypes.c_int64,
+                                     _i32p, ctypes.c_int32, _f64p]
+    lib.oracle_base_q4.restype = None
+    lib.oracle_base_q4.argtypes = [ctypes.POINTER(ctypes.c_uint8), ctypes.c_int64, _f32p, ctypes.c_int64,
+                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _u16p, ctypes.c_int64,
+                                   _i32p, ctypes.c_int32, _f64p]
     return lib
 
 
@@ -241,20 +248,31 @@ def lora_layer_stacked(workload, row_adapters, rows=None, modules=None, pass_max
     return out
 
 
-def _bf16_f64(bits: np.ndarray) -> np.ndarray:
-    return (np.ascontiguousarray(bits).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-
-
-def base_projection(W: np.ndarray, x: np.ndarray, rows=None, block: int = 2048) -> np.ndarray:
-    """W.x for the selected rows in fp64: W uint16 (bf16) [d_out, d_in], x
-    uint16 [num_rows, >= d_in].  Each product of two bf16 values is exact in
-    fp64; W is decoded a block of rows at a time."""
+def base_projection(W, x: np.ndarray, rows=None) -> np.ndarray:
+    """W.x for the selected rows in fp64 (oracle_base_bf16 / oracle_base_q4:
+    plain loops, ascending k): W uint16 (bf16) [d_out, d_in], or a 4-bit
+    weight (an object with q uint8 [d_out, ldwq], two signed 4-bit values per
+    byte with the lower input index in the low nibble; scales fp32
+    [d_out, lds], one per `group` consecutive inputs of a row; d_in, d_out);
+    x uint16 [num_rows, >= d_in]."""
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    sel = np.arange(x.shape[0], dtype=np.int32) if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    if hasattr(W, "scales"):
+        d_out, d_in = W.d_out, W.d_in
+        out = np.empty((sel.size, d_out), np.float64)
+        q, s = np.ascontiguousarray(W.q), np.ascontiguousarray(W.scales)
+        lib.oracle_base_q4(q.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), q.shape[1], _ptr(s, _f32p), s.shape[1],
+                           W.group, d_out, d_in, _ptr(x, _u16p), x.shape[1], _ptr(sel, _i32p), sel.size,
+                           _ptr(out, _f64p))
+        return out
+    W = np.ascontiguousarray(W)
     d_out, d_in = W.shape
-    xs = _bf16_f64(x[:, :d_in] if rows is None else x[np.asarray(rows), :d_in])
-    out = np.empty((xs.shape[0], d_out), np.float64)
-    for n0 in range(0, d_out, block):
-        out[:, n0:n0 + block] = xs @ _bf16_f64(W[n0:n0 + block]).T
+    out = np.empty((sel.size, d_out), np.float64)
+    lib.oracle_base_bf16(_ptr(W, _u16p), W.shape[1], d_out, d_in, _ptr(x, _u16p), x.shape[1], _ptr(sel, _i32p),
+                         sel.size, _ptr(out, _f64p))
     return out
+
 
 
 def linear_layer(workload, rows=None, modules=None) -> dict:

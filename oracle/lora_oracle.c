@@ -34,7 +34,10 @@
  *  - a table rank outside [0, max_rank] is an error: skipped and counted;
  *  - scale (alpha/r) multiplies the delta, 1.0 when unspecified;
  *  - the oracle keeps y in double with no output rounding;
- *  - int8 factors: one fp32 scale per row (see the int8 functions below).
+ *  - int8 factors: one fp32 scale per row (see the int8 functions below);
+ *  - a 4-bit base weight: signed values in [-8, 7], two per byte (the lower
+ *    input index in the low nibble), one fp32 scale per output row and group
+ *    of consecutive inputs (see oracle_base_q4 below).
  */
 #include <stdint.h>
 #include <string.h>
@@ -229,4 +232,60 @@ int32_t oracle_lora_module(const uint16_t *x, int64_t ldx, int32_t num_rows,
                     bf16_value(y0[(int64_t)b * ldy + n]) + dr[n];
     }
     return bad;
+}
+
+/*
+ * Base projection of a linear layer, the shared term of the forward
+ * y = Wx + (B.A)x.(alpha/r) ("m07 -- Multi-Adapter (LoRA) Serving", "6. Deep
+ * Dive A"): for each selected row b = rows[i] and output n,
+ *     out[i][n] = sum over k ascending of W[n][k] * x[b][k]
+ * in double.  W is bf16 [d_out][ldw] (row n: the weights of output n).
+ */
+void oracle_base_bf16(const uint16_t *W, int64_t ldw, int32_t d_out, int32_t d_in,
+                      const uint16_t *x, int64_t ldx, const int32_t *rows, int32_t n_sel,
+                      double *out)
+{
+    for (int32_t i = 0; i < n_sel; ++i) {
+        const uint16_t *xr = x + (int64_t)rows[i] * ldx;
+        for (int32_t n = 0; n < d_out; ++n) {
+            const uint16_t *w = W + (int64_t)n * ldw;
+            double s = 0.0;
+            for (int32_t k = 0; k < d_in; ++k)
+                s += bf16_value(w[k]) * bf16_value(xr[k]);
+            out[(int64_t)i * d_out + n] = s;
+        }
+    }
+}
+
+/* The signed 4-bit value k of a packed row: byte k/2, low nibble for even k. */
+static int32_t q4_value(const uint8_t *row, int32_t k)
+{
+    uint32_t nib = (k % 2 == 0) ? (row[k / 2] & 0xFu) : (row[k / 2] >> 4);
+    return nib >= 8 ? (int32_t)nib - 16 : (int32_t)nib;
+}
+
+/*
+ * The same with a 4-bit base weight ("12. Adapter Serving and Multi-Tenant
+ * Customization", "Interactions with other engine mechanisms", Quantization:
+ * the base in INT4, the adapter in BF16, the base dequantised and the sum
+ * accumulated wide).  W[n][k] = Ws[n][k / group] * q[n][k], with q the signed
+ * 4-bit value k of row n of Wq ([d_out][ldwq] bytes) and Ws fp32
+ * [d_out][lds]; the product of an fp32 scale and a 4-bit integer is exact in
+ * double.
+ */
+void oracle_base_q4(const uint8_t *Wq, int64_t ldwq, const float *Ws, int64_t lds,
+                    int32_t group, int32_t d_out, int32_t d_in, const uint16_t *x,
+                    int64_t ldx, const int32_t *rows, int32_t n_sel, double *out)
+{
+    for (int32_t i = 0; i < n_sel; ++i) {
+        const uint16_t *xr = x + (int64_t)rows[i] * ldx;
+        for (int32_t n = 0; n < d_out; ++n) {
+            const uint8_t *q = Wq + (int64_t)n * ldwq;
+            const float *sc = Ws + (int64_t)n * lds;
+            double s = 0.0;
+            for (int32_t k = 0; k < d_in; ++k)
+                s += ((double)sc[k / group] * (double)q4_value(q, k)) * bf16_value(xr[k]);
+            out[(int64_t)i * d_out + n] = s;
+        }
+    }
 }

@@ -205,3 +205,55 @@ def test_segment_bound_counts_distinct_valid_slots():
     s.max_segments = -1
     with pytest.raises(ValueError):
         s.c()
+
+
+def lin_ios(q4=False, **over):
+    if q4:
+        arr = (lg._LinQ4IO * 7)()
+        for i in range(7):
+            arr[i] = lg._LinQ4IO(P, 8192, P, 4096, P, 64, P, 8192, 8192, 8192)
+    else:
+        arr = (lg._LinIO * 7)()
+        for i in range(7):
+            arr[i] = lg._LinIO(P, 8192, P, 8192, P, 8192, 8192, 8192)
+    for k, v in over.items():
+        i, field = k.split("_", 1)
+        setattr(arr[int(i)], field, v)
+    return arr
+
+
+LIN_BAD = [
+    (dict(io=None), NULL), (dict(table=None), NULL), (dict(ws=None), NULL), (dict(row_adapter=None), NULL),
+    (dict(mask=0), MODULE), (dict(n=-1), SHAPE), (dict(max_rank=0), RANK), (dict(ws_bytes=1024), WS),
+]
+
+
+@pytest.mark.parametrize("fn", ["lora_linear_layer", "lora_linear_shrink", "lora_linear_expand"])
+@pytest.mark.parametrize("args,code", LIN_BAD + [
+    (dict(io=lin_ios(**{"2_W": None})), NULL), (dict(io=lin_ios(**{"0_ldw": 4096})), SHAPE),
+    (dict(io=lin_ios(**{"3_W": P + 2})), ALIGN), (dict(io=lin_ios(**{"1_d_in": 1004, "1_ldx": 1008})), ALIGN),
+])
+def test_linear_rejects(fn, args, code):
+    a = dict(io=lin_ios(), mask=0x7F, n=128, row_adapter=P, table=P, slots=128, seg=seg(), max_rank=64, ws=P,
+             ws_bytes=1 << 40)
+    a.update(args)
+    assert getattr(lg.lib(), fn)(a["io"], a["mask"], a["n"], a["row_adapter"], a["table"], a["slots"], a["seg"],
+                                 a["max_rank"], a["ws"], a["ws_bytes"], None) == code
+
+
+@pytest.mark.parametrize("fn", ["lora_linear_layer_q4", "lora_linear_shrink_q4", "lora_linear_expand_q4"])
+@pytest.mark.parametrize("args,code", LIN_BAD + [
+    (dict(io=lin_ios(True, **{"2_Wq": None})), NULL), (dict(io=lin_ios(True, **{"5_Ws": None})), NULL),
+    (dict(io=lin_ios(True, **{"0_d_in": 8000, "0_ldx": 8000})), ALIGN),   # not a multiple of 128
+    (dict(io=lin_ios(True, **{"1_ldwq": 4088})), ALIGN),                  # not a multiple of 16
+    (dict(io=lin_ios(True, **{"1_ldwq": 4080})), SHAPE),                  # < d_in / 2
+    (dict(io=lin_ios(True, **{"4_lds": 63})), SHAPE),                     # < d_in / 128
+    (dict(io=lin_ios(True, **{"6_Ws": P + 2})), ALIGN), (dict(io=lin_ios(True, **{"3_Wq": P + 8})), ALIGN),
+    (dict(io=lin_ios(True, **{"2_ldwq": 1 << 20})), SHAPE),               # W of 8 GiB
+])
+def test_linear_q4_rejects(fn, args, code):
+    a = dict(io=lin_ios(True), mask=0x7F, n=128, row_adapter=P, table=P, slots=128, seg=seg(), max_rank=64, ws=P,
+             ws_bytes=1 << 40)
+    a.update(args)
+    assert getattr(lg.lib(), fn)(a["io"], a["mask"], a["n"], a["row_adapter"], a["table"], a["slots"], a["seg"],
+                                 a["max_rank"], a["ws"], a["ws_bytes"], None) == code

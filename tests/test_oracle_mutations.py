@@ -8,6 +8,7 @@ import subprocess
 import pytest
 
 import oracle
+import tests.test_fused_oracle as fused
 import tests.test_oracle_pins as pins
 
 SRC = open(oracle._SRC).read()
@@ -38,6 +39,21 @@ MUTATIONS = {
                           "const int8_t *a = qa + (int64_t)j * d_in; (void)lda8;"),
     "q8_A_values_after_rank_scales": ("(const int8_t *)(sa + round_up(rank, 4))", "(const int8_t *)(sa + rank)"),
     "q8_B_values_after_d_out_scales": ("(const int8_t *)(sb + round_up(d_out, 4))", "(const int8_t *)(sb + d_out)"),
+    "base_W_transposed": ("s += bf16_value(w[k]) * bf16_value(xr[k]);",
+                          "s += bf16_value(W[(int64_t)k * d_out + n]) * bf16_value(xr[k]); (void)w;"),
+    "base_drop_last_k": ("for (int32_t k = 0; k < d_in; ++k)\n                s += bf16_value(w[k])",
+                         "for (int32_t k = 0; k < d_in - 1; ++k)\n                s += bf16_value(w[k])"),
+    "q4_nibbles_swapped": ("uint32_t nib = (k % 2 == 0) ? (row[k / 2] & 0xFu) : (row[k / 2] >> 4);",
+                           "uint32_t nib = (k % 2 == 1) ? (row[k / 2] & 0xFu) : (row[k / 2] >> 4);"),
+    "q4_unsigned": ("return nib >= 8 ? (int32_t)nib - 16 : (int32_t)nib;", "return (int32_t)nib;"),
+    "q4_offset_binary": ("return nib >= 8 ? (int32_t)nib - 16 : (int32_t)nib;", "return (int32_t)nib - 8;"),
+    "q4_group_by_modulo": ("s += ((double)sc[k / group]", "s += ((double)sc[k % group]"),
+    "q4_no_scale": ("s += ((double)sc[k / group] * (double)q4_value(q, k)) * bf16_value(xr[k]);",
+                    "s += ((double)q4_value(q, k)) * bf16_value(xr[k]); (void)sc;"),
+    "q4_rows_by_d_in": ("const uint8_t *q = Wq + (int64_t)n * ldwq;",
+                        "const uint8_t *q = Wq + (int64_t)n * (d_in / 2); (void)ldwq;"),
+    "q4_scale_rows_by_groups": ("const float *sc = Ws + (int64_t)n * lds;",
+                                "const float *sc = Ws + (int64_t)n * (d_in / group); (void)lds;"),
 }
 
 CHECKS = [
@@ -51,6 +67,12 @@ CHECKS = [
     (pins.test_segments_vs_stable_sort, dict(n=257, slots=9, seed=3)),
     (pins.test_int8_matches_bf16_twin_exactly, dict(d_in=24, d_out=10, rank=5, rows=6, slots=3)),
     (pins.test_int8_exact_rational, {}),
+    (fused.test_one_hot_base_weights_gather_x_exactly, {}),
+    (fused.test_base_projection_exact_rational, {}),
+    (fused.test_q4_matches_its_bf16_twin_exactly, {}),
+    (fused.test_q4_exact_rational, {}),
+    (fused.test_q4_one_hot_gathers_scaled_x, {}),
+    (fused.test_q4_codes_decode_in_order, {}),
 ]
 
 

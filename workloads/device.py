@@ -51,8 +51,17 @@ class DeviceWorkload:
         self.ios = {m.name: lg.ModuleIO(self.x[m.x_name], self.y[m.name]) for m in w.modules}
         self.W = self.lin_ios = None
         if w.W is not None:  # base weights: the fused calls, and a workspace for them
-            self.W = {m.name: bf16_tensor(w.W[m.name], device) for m in w.modules}
-            self.lin_ios = {m.name: lg.LinearIO(self.x[m.x_name], self.W[m.name], self.y[m.name]) for m in w.modules}
+            self.W, self.lin_ios = {}, {}
+            for m in w.modules:
+                W = w.W[m.name]
+                if hasattr(W, "scales"):  # 4-bit weights and their group scales
+                    q = torch.from_numpy(np.ascontiguousarray(W.q)).to(device)
+                    sc = torch.from_numpy(np.ascontiguousarray(W.scales, dtype=np.float32)).to(device)
+                    self.W[m.name] = (q, sc)
+                    self.lin_ios[m.name] = lg.LinearQ4IO(self.x[m.x_name], q, sc, self.y[m.name], d_in=m.d_in)
+                else:
+                    self.W[m.name] = bf16_tensor(W, device)
+                    self.lin_ios[m.name] = lg.LinearIO(self.x[m.x_name], self.W[m.name], self.y[m.name])
             nb = lg.linear_workspace_bytes(w.num_rows + ws_extra_rows, w.num_slots, w.max_rank, sum_d_in,
                                            len(w.modules))
             if nb > self.ws_bytes:

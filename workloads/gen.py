@@ -119,7 +119,8 @@ class Workload:
     notes: dict = field(default_factory=dict)
     fmt: np.ndarray | None = None    # int32 [num_slots, N_MOD]: FMT_BF16 or FMT_INT8_ROWS
     stack: np.ndarray | None = None  # int32 [num_rows, depth]: several adapters per row (ids = column 0)
-    W: dict | None = None            # module name -> uint16 [d_out, d_in]: base weights (fused workloads)
+    W: dict | None = None            # module name -> base weight (fused workloads): uint16 [d_out, d_in]
+                                     # bf16, or a Q4Weight
 
     def __post_init__(self):
         if self.fmt is None:
@@ -435,6 +436,53 @@ def add_base_weights(w: Workload) -> Workload:
     return w
 
 
+Q4_GROUP = 128  # inputs per scale of a 4-bit base weight (LORA_Q4_GROUP)
+
+
+@dataclass
+class Q4Weight:
+    """A 4-bit base weight: q uint8 [d_out, d_in / 2] (two signed 4-bit
+    values per byte, the lower input index in the low nibble), scales fp32
+    [d_out, d_in / group]: W[n][k] = scales[n][k // group] * value k of row n."""
+    q: np.ndarray
+    scales: np.ndarray
+    group: int
+    d_in: int
+    d_out: int
+
+
+def quantize_q4(Wbits: np.ndarray, group: int = Q4_GROUP) -> Q4Weight:
+    """Symmetric 4-bit quantisation of a bf16 weight [d_out, d_in], one scale
+    per `group` inputs of a row: scale = max|w| / 7 over the group (1 for an
+    all-zero group), q = round-half-even(w / scale) clamped to [-8, 7]."""
+    d_out, d_in = Wbits.shape
+    assert d_in % group == 0 and d_in % 2 == 0
+    wf = bf16_to_f32(Wbits).astype(np.float64).reshape(d_out, d_in // group, group)
+    scales = (np.abs(wf).max(axis=2) / 7.0).astype(np.float32)
+    scales[scales == 0] = 1.0
+    q = np.clip(np.rint(wf / scales[:, :, None].astype(np.float64)), -8, 7).astype(np.int8).reshape(d_out, d_in)
+    nib = (q & 0xF).astype(np.uint8)
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    return Q4Weight(packed, scales, group, d_in, d_out)
+
+
+def add_base_weights_q4(w: Workload, group: int = Q4_GROUP) -> Workload:
+    """4-bit base weights for every projection: the bf16 draws of
+    add_base_weights quantised by quantize_q4."""
+    add_base_weights(w)
+    w.W = {name: quantize_q4(W, group) for name, W in w.W.items()}
+    return w
+
+
+def fused_layer_q4(seed=8, rank=64, rows=128):
+    """fused_layer with 4-bit base weights (0.43 GB of weights and scales):
+    the pages' INT4 base with BF16 adapters, 8 of the 128 rows base-only."""
+    w = full_layer(seed, rank, rows)
+    w.ids[::16] = -1  # base-only rows in the same batch
+    w.name = f"fused_layer_q4_r{rank}_b{rows}"
+    return add_base_weights_q4(w)
+
+
 def fused_layer(seed=8, rank=64, rows=128):
     """The full 70B layer of full_layer_r64 with its base weights: base
     projection and adapter delta together (1.63 GB of W and 2.65 GB of
@@ -529,6 +577,7 @@ WORKLOADS = {
     "full_layer_r64_int8": lambda seed=3: full_layer(seed, fmt=FMT_INT8_ROWS),
     "stacked_layer": stacked_layer,
     "fused_layer_r64": fused_layer,
+    "fused_layer_q4_r64": fused_layer_q4,
 }
 
 
