@@ -12,6 +12,11 @@ import numpy as np
 
 REL, ABS = 1e-2, 1e-3
 
+# every comparison's strict relative figure, max |gpu - oracle| / max |oracle
+# row| over its rows: reported at the end of the session (tests/conftest.py),
+# not part of the bar
+STRICT: list = []
+
 
 def note(msg: str):
     """Name the GPU case about to run (flushed, so a crash still shows it)."""
@@ -34,7 +39,9 @@ def check_rows(gpu, ref, what: str, rel=REL, abs_=ABS):
                              f"gpu={gpu[r, c]!r} oracle={ref[r, c]!r} tol={tol[r, 0]!r}")
     # strict relative figure (reported, not part of the bar)
     scale = np.maximum(np.abs(ref).max(axis=1, keepdims=True), 1e-300)
-    return float((err / scale).max())
+    strict = float((err / scale).max())
+    STRICT.append((what, strict, int(ref.shape[0])))
+    return strict
 
 
 def bf16_host(t):
