@@ -12,10 +12,11 @@
 // ids are base-only rows and join no segment; ids >= num_slots are counted
 // into the status word and skipped.
 //
-// A row's place inside its group of equal ids is the number of earlier rows
-// with the same id.  Each thread finds it by scanning the ids of its block
-// from LDS, and the last row of each id in the block writes the block's count
-// for that id, so no atomics are needed and the result is deterministic.
+// A block sorts its rows by slot id with a stable radix sort (one bit per
+// pass; a ballot splits each wave's rows, the waves' counts place them), so
+// rows of one slot keep their order, no atomics are needed and the result is
+// deterministic.  A row's place inside its group of equal ids is then its
+// sorted place minus the start of its id's run.
 //   * up to kSegSmallMax rows: one block (sized to the batch) does everything;
 //   * more rows: per chunk of kSegChunk rows, counts per slot and in-chunk
 //     ranks; then one block scans the count table in slot-major order, which
@@ -105,82 +106,93 @@ __device__ void count_long_tiles(const lora_segments_t &seg, int n, int segs, in
   }
 }
 
-// Rows of this block with the same id before / after row t.  s_ids holds the
-// block's ids in LDS (16-byte aligned, -1 past the end, so a valid id never
-// matches padding); four ids per LDS read.
-__device__ void same_id_counts(const int *s_ids, int len, int t, int id, int *before, int *after) {
-  const int4 *s4 = reinterpret_cast<const int4 *>(s_ids);
-  const int n4 = (len + 3) >> 2;
-  int bf = 0, tot = 0;
-  for (int b4 = 0; b4 < n4; ++b4) {
-    const int4 v = s4[b4];
-    const int b = b4 * 4;
-    const int e0 = v.x == id, e1 = v.y == id, e2 = v.z == id, e3 = v.w == id;
-    tot += e0 + e1 + e2 + e3;
-    bf += (e0 & (b < t)) + (e1 & (b + 1 < t)) + (e2 & (b + 2 < t)) + (e3 & (b + 3 < t));
+// Stable sort of the block's rows by key, keys in [0, 2^bits): one pass per
+// bit, least significant first.  In a pass a ballot splits each wave's rows
+// into zeros and ones; a row goes to (zeros of earlier waves + zeros below it
+// in its wave), or past every zero to (ones of earlier waves + ones below
+// it), so equal keys keep their order.  In: this thread's key and value.
+// Out: the key and value at sorted place threadIdx.x; the sorted keys stay in
+// s_key[return value].  s_w holds THREADS/64 ints.
+template <int THREADS>
+__device__ int block_radix_sort(int *key, int *val, int bits, int (*s_key)[THREADS], int (*s_val)[THREADS],
+                                int *s_w) {
+  constexpr int kWaves = THREADS / 64;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int buf = 0;
+  for (int b = 0; b < bits; ++b) {
+    const bool one = (*key >> b) & 1;
+    const uint64_t zeros = __ballot(!one);
+    const int zb = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(zeros >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)zeros, 0u));
+    if (lane == 0) s_w[w] = __popcll(zeros);
+    __syncthreads();
+    int zw = 0, ztot = 0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+      const int c = s_w[k];
+      zw += k < w ? c : 0;
+      ztot += c;
+    }
+    const int dest = one ? ztot + (64 * w - zw) + (lane - zb) : zw + zb;
+    s_key[buf][dest] = *key;
+    s_val[buf][dest] = *val;
+    __syncthreads();  // also: every wave has read s_w before the next pass writes it
+    *key = s_key[buf][t];
+    *val = s_val[buf][t];
+    buf ^= 1;  // the next pass writes the other buffer while this one may still be read
   }
-  *before = bf;
-  *after = tot - bf - 1;  // tot counts row t itself
+  return buf ^ 1;
 }
 
-// Slot tables up to this size keep their counts in LDS.
-constexpr int kSegLdsSlots = 8192;
+// Bits of the keys 0 .. num_slots (num_slots: a row with no segment).
+__device__ __forceinline__ int key_bits(int num_slots) { return 32 - __clz(num_slots); }
 
-// n <= THREADS rows in one block.  Per slot, the low 16 bits of the scanned
-// value count rows and the high 16 bits count non-empty slots (n <= 1024,
-// so neither overflows), so one scan gives row offsets and segment indices.
+// n <= THREADS rows in one block: the rows sorted by slot, then segment
+// starts where the slot changes, one scan for their indices, and the
+// outputs; the status word gets the ids >= num_slots (and, past the caller's
+// bound, the rows of the dropped segments).
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void seg_small_kernel(const int32_t *__restrict__ ids, int stride, int n,
-                                                            int num_slots, bool add_status, lora_segments_t seg,
-                                                            int32_t *__restrict__ ws_counts) {
-  __shared__ __align__(16) int s_ids[THREADS];
-  __shared__ int s_counts[kSegLdsSlots];
+                                                            int num_slots, bool add_status, lora_segments_t seg) {
+  __shared__ int s_key[2][THREADS];
+  __shared__ int s_row[2][THREADS];
+  __shared__ int s_start[THREADS];
   __shared__ int s_w[THREADS / 64 + 1];
-  int32_t *counts = num_slots <= kSegLdsSlots ? s_counts : ws_counts;
   const int t = threadIdx.x;
-  int id = -1, bad = 0;
+  int key = num_slots, bad = 0;  // num_slots: no segment (base only, a bad id, or past the batch)
   if (t < n) {
     const int r = ids[(int64_t)t * stride];
     if (r >= num_slots) bad = 1;
-    else if (r >= 0) id = r;
+    else if (r >= 0) key = r;
   }
-  s_ids[t] = id;
-  for (int a = t; a < num_slots; a += THREADS) counts[a] = 0;
-  int nbad;
-  block_excl_scan<THREADS>(bad, &nbad, s_w);  // also orders the LDS and count stores
-  int before = 0, after = 0;
-  if (id >= 0) same_id_counts(s_ids, n, t, id, &before, &after);
-  if (id >= 0 && after == 0) counts[id] = before + 1;
+  int row = t;
+  const int fb = block_radix_sort<THREADS>(&key, &row, key_bits(num_slots), s_key, s_row, s_w);
+  // thread t now holds sorted place t; rows with no segment sort last
+  const bool valid = key < num_slots;
+  const bool starts = valid && (t == 0 || s_key[fb][t - 1] != key);
+  int nseg, nvalid, nbad;
+  const int sidx = block_excl_scan<THREADS>(starts ? 1 : 0, &nseg, s_w);
+  block_excl_scan<THREADS>(valid ? 1 : 0, &nvalid, s_w);
+  block_excl_scan<THREADS>(bad, &nbad, s_w);
+  if (valid) seg.perm[t] = row;
+  if (starts) {
+    seg.seg_offsets[sidx] = t;
+    seg.seg_adapter[sidx] = key;
+    s_start[sidx] = t;
+  }
   __syncthreads();
-  int carry = 0;  // rows | segments << 16 of the slots before this pass
-  int tiles = 0;  // this thread's SGMV tiles of kept segments: expand | shrink << 16 (at most 144 each)
-  for (int base = 0; base < num_slots; base += THREADS) {
-    const int a = base + t;
-    const int c = a < num_slots ? counts[a] : 0;
-    const int v = c | (c > 0 ? 1 << 16 : 0);
-    int tot;
-    const int ex = block_excl_scan<THREADS>(v, &tot, s_w) + carry;
-    if (a < num_slots) {
-      counts[a] = ex & 0xffff;
-      if (c > 0) {
-        seg.seg_offsets[ex >> 16] = ex & 0xffff;
-        seg.seg_adapter[ex >> 16] = a;
-        const bool kept = seg.max_segments <= 0 || (ex >> 16) < seg.max_segments;
-        if (kept && n >= kLongSegRows && c >= kLongSegRows)
-          tiles += ceil_div(c, kSgmvExpandRows) | ceil_div(c, kSgmvShrinkRows) << 16;
-      }
-    }
-    carry += tot;
+  int tiles = 0;  // SGMV tiles of a kept segment: expand | shrink << 16 (at most 144 each)
+  if (starts && (seg.max_segments <= 0 || sidx < seg.max_segments) && n >= kLongSegRows) {
+    const int len = (sidx + 1 < nseg ? s_start[sidx + 1] : nvalid) - t;
+    if (len >= kLongSegRows) tiles = ceil_div(len, kSgmvExpandRows) | ceil_div(len, kSgmvShrinkRows) << 16;
   }
   int all_tiles;
   block_excl_scan<THREADS>(tiles, &all_tiles, s_w);  // its barriers also publish every segment start
   if (t == 0) {
-    finish_segments(seg, carry >> 16, carry & 0xffff, add_status, nbad);
+    finish_segments(seg, nseg, nvalid, add_status, nbad);
     seg.tile_counts[0] = all_tiles >> 16;
     seg.tile_counts[1] = all_tiles & 0xffff;
   }
-  __syncthreads();
-  if (id >= 0) seg.perm[counts[id] + before] = t;
 }
 
 // Chunk c of kSegChunk rows: hist[a * nchunks + c] = rows of slot a in the
@@ -190,26 +202,34 @@ __global__ __launch_bounds__(kSegChunk) void seg_chunk_kernel(const int32_t *__r
                                                               int num_slots, int nchunks, int32_t *__restrict__ hist,
                                                               int32_t *__restrict__ lrank,
                                                               int32_t *__restrict__ badc) {
-  __shared__ __align__(16) int s_ids[kSegChunk];
+  __shared__ int s_key[2][kSegChunk];
+  __shared__ int s_row[2][kSegChunk];
   __shared__ int s_w[kSegChunk / 64 + 1];
   const int t = threadIdx.x;
   const int c = blockIdx.x;
-  const int row = c * kSegChunk + t;
   const int len = min(kSegChunk, n - c * kSegChunk);
-  int id = -1, bad = 0;
+  int key = num_slots, bad = 0;  // num_slots: no segment
   if (t < len) {
-    const int r = ids[(int64_t)row * stride];
+    const int r = ids[(int64_t)(c * kSegChunk + t) * stride];
     if (r >= num_slots) bad = 1;
-    else if (r >= 0) id = r;
+    else if (r >= 0) key = r;
   }
-  s_ids[t] = id;
   for (int a = t; a < num_slots; a += kSegChunk) hist[(size_t)a * nchunks + c] = 0;
   int nbad;
   block_excl_scan<kSegChunk>(bad, &nbad, s_w);  // also orders the zeroing before the counts
-  int before = 0, after = 0;
-  if (id >= 0) same_id_counts(s_ids, len, t, id, &before, &after);
-  if (id >= 0 && after == 0) hist[(size_t)id * nchunks + c] = before + 1;
-  if (id >= 0) lrank[row] = before;
+  int row = t;
+  const int fb = block_radix_sort<kSegChunk>(&key, &row, key_bits(num_slots), s_key, s_row, s_w);
+  if (key < num_slots) {
+    // the run of this key in the sorted chunk: [first, last]
+    int lo = 0, hi = t;  // first place with a key >= this one
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_key[fb][mid] < key) lo = mid + 1;
+      else hi = mid;
+    }
+    lrank[c * kSegChunk + row] = t - lo;
+    if (t + 1 == kSegChunk || s_key[fb][t + 1] != key) hist[(size_t)key * nchunks + c] = t - lo + 1;
+  }
   if (t == 0) badc[c] = nbad;
 }
 
@@ -291,7 +311,7 @@ inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 }  // namespace
 
 size_t segments_ws_bytes(int num_rows, int num_slots) {
-  if (num_rows <= kSegSmallMax) return num_slots <= kSegLdsSlots ? 0 : align256((size_t)num_slots * 4);
+  if (num_rows <= kSegSmallMax) return 0;
   const size_t nchunks = ((size_t)num_rows + kSegChunk - 1) / kSegChunk;
   return align256((size_t)num_rows * 4) + align256(nchunks * 4) + align256(nchunks * (size_t)num_slots * 4);
 }
@@ -300,13 +320,11 @@ hipError_t launch_build_segments(const int32_t *ids, int stride, int n, int num_
                                  const lora_segments_t &seg, void *ws, hipStream_t stream) {
   char *w = static_cast<char *>(ws);
   if (n <= 256) {
-    seg_small_kernel<256><<<1, 256, 0, stream>>>(ids, stride, n, num_slots, add_status, seg,
-                                                 reinterpret_cast<int32_t *>(w));
+    seg_small_kernel<256><<<1, 256, 0, stream>>>(ids, stride, n, num_slots, add_status, seg);
     return hipGetLastError();
   }
   if (n <= kSegSmallMax) {
-    seg_small_kernel<kSegSmallMax><<<1, kSegSmallMax, 0, stream>>>(ids, stride, n, num_slots, add_status, seg,
-                                                                  reinterpret_cast<int32_t *>(w));
+    seg_small_kernel<kSegSmallMax><<<1, kSegSmallMax, 0, stream>>>(ids, stride, n, num_slots, add_status, seg);
     return hipGetLastError();
   }
   const int nchunks = (n + kSegChunk - 1) / kSegChunk;

@@ -204,8 +204,8 @@ typedef struct lora_module_io {
  * bytes.  sum_d_in is the sum of d_in over the projections a
  * call processes (d_in for lora_shrink, the sum over the mask for the layer
  * calls).  One workspace of this size serves every call on the same stream.
- * A call that needs none (lora_expand; lora_build_segments on up to 1024 rows
- * and 8192 slots) accepts ws = NULL.  A workspace must be 16-byte aligned
+ * A call that needs none (lora_expand; lora_build_segments on up to 1024
+ * rows) accepts ws = NULL.  A workspace must be 16-byte aligned
  * (LORA_ERR_ALIGN otherwise).  Returns 0 for invalid arguments.
  */
 size_t lora_workspace_bytes(int32_t num_rows, int32_t num_slots,

@@ -86,7 +86,6 @@ def test_workspace_query():
     (dict(ids=None), NULL),
     (dict(n=5000, ws=None), NULL),           # long batches need workspace
     (dict(n=5000, ws_bytes=0), WS),          # long batches need workspace
-    (dict(n=128, slots=20000, ws_bytes=0), WS),  # so do very large slot tables
     (dict(seg=seg(max_segments=-1)), SHAPE),
 ])
 def test_build_segments_rejects(args, code):
