@@ -30,6 +30,7 @@
 // followed by lora_apply_layer would; it runs beside the others.
 #pragma once
 
+#include "block_sort.h"
 #include "decode_items.h"
 
 namespace lora {
@@ -391,56 +392,38 @@ __device__ __forceinline__ int op_block_scan(int x, int *total, int *s_w) {
 }
 
 // Block 0 of the grid: the segments and the status word as
-// lora_build_segments followed by lora_apply_layer leave them.  One pass over
-// the ids in LDS gives every row its stable place in slot order (valid rows
-// of smaller slots, and earlier rows of its own); a scan over the sorted ids
-// then marks where each segment starts.  The status word gets the rows whose
+// lora_build_segments followed by lora_apply_layer leave them.  A stable
+// radix sort on the slot (block_sort.h) gives every row its place in slot
+// order; a scan over the sorted ids then marks where each segment starts.
+// The table entries of a kept segment's projections are requested together.
+// The status word gets the rows whose
 // id is >= num_slots, the rows of segments past the bound, and one per (kept
 // segment, projection) whose entry cannot be applied.
 __device__ __forceinline__ void op_build(const OnePassDesc &od, uint8_t *lds) {
   const LayerDesc &d = od.L;
   const int t = threadIdx.x, n = d.num_rows;
-  int *s_ids = reinterpret_cast<int *>(lds);           // [256] id of each row (-1: none)
-  int *s_sid = reinterpret_cast<int *>(lds + 1024);    // [256] ids in sorted order
-  int *s_start = reinterpret_cast<int *>(lds + 2048);  // [256] sorted start of each segment
-  int *s_w = reinterpret_cast<int *>(lds + 3072);
-  int id = -1, bad = 0;
+  auto s_key = reinterpret_cast<int (*)[kDecodeThreads]>(lds);         // [2][256] keys, sorted
+  auto s_row = reinterpret_cast<int (*)[kDecodeThreads]>(lds + 2048);  // [2][256] their rows
+  int *s_start = reinterpret_cast<int *>(lds + 4096);                  // [256] sorted start of each segment
+  int *s_w = reinterpret_cast<int *>(lds + 5120);
+  int key = d.num_slots, bad = 0;  // num_slots: no segment (base only, a bad id, or past the batch)
   if (t < n) {
     const int r = od.ids[t];
     if (r >= d.num_slots) bad = 1;
-    else if (r >= 0) id = r;
+    else if (r >= 0) key = r;
   }
-  s_ids[t] = id;
-  s_sid[t] = -1;
-  __syncthreads();
-  // four ids per LDS read over the rows of the batch
-  const int4 *ids4 = reinterpret_cast<const int4 *>(s_ids);
-  int before = 0, same = 0, less = 0;
-  if (id >= 0) {
-    const int n4 = (n + 3) >> 2;
-#pragma unroll 4
-    for (int u4 = 0; u4 < n4; ++u4) {
-      const int4 v = ids4[u4];
-      const int u = u4 * 4;
-      const int e0 = v.x == id, e1 = v.y == id, e2 = v.z == id, e3 = v.w == id;
-      same += e0 + e1 + e2 + e3;
-      before += (e0 & (u < t)) + (e1 & (u + 1 < t)) + (e2 & (u + 2 < t)) + (e3 & (u + 3 < t));
-      less += (v.x >= 0 && v.x < id) + (v.y >= 0 && v.y < id) + (v.z >= 0 && v.z < id) + (v.w >= 0 && v.w < id);
-    }
-  }
-  const int pos = less + before;  // place in slot order, rows of one slot ascending
-  if (id >= 0) {
-    s_sid[pos] = id;
-    od.seg.perm[pos] = t;
-  }
-  __syncthreads();
-  // thread p now looks at sorted place p
-  const int sid = s_sid[t];
-  const bool starts = sid >= 0 && (t == 0 || s_sid[t - 1] != sid);
+  int row = t;
+  // rows in slot order, rows of one slot ascending (a stable sort on the slot)
+  const int fb = block_radix_sort<kDecodeThreads>(&key, &row, key_bits(d.num_slots), s_key, s_row, s_w);
+  // thread t now looks at sorted place t
+  const int sid = key;
+  const bool valid = sid < d.num_slots;
+  const bool starts = valid && (t == 0 || s_key[fb][t - 1] != sid);
   int nseg;
   const int seg = op_block_scan(starts ? 1 : 0, &nseg, s_w);
-  const int nvalid = op_block_sum(id >= 0 ? 1 : 0, s_w);
+  const int nvalid = op_block_sum(valid ? 1 : 0, s_w);
   const int nbad = op_block_sum(bad, s_w);
+  if (valid) od.seg.perm[t] = row;
   if (starts) {
     od.seg.seg_offsets[seg] = t;
     od.seg.seg_adapter[seg] = sid;
@@ -456,11 +439,15 @@ __device__ __forceinline__ void op_build(const OnePassDesc &od, uint8_t *lds) {
     tiles = (len + kSgmvExpandRows - 1) / kSgmvExpandRows | ((len + kSgmvShrinkRows - 1) / kSgmvShrinkRows) << 16;
   const int all_tiles = op_block_sum(tiles, s_w);
   int errs = 0;
-  if (kept_start)
-    for (int i = 0; i < d.n_active; ++i) {
-      const lora_adapter_entry_t e = d.table[(int64_t)sid * d.table_cols + kernel_desc().mod[i].col];
-      if (e.rank != 0 && !entry_ok(e, d.max_rank)) ++errs;
-    }
+  if (kept_start) {
+    lora_adapter_entry_t es[kMaxModules];
+#pragma unroll
+    for (int i = 0; i < kMaxModules; ++i)
+      if (i < d.n_active) es[i] = d.table[(int64_t)sid * d.table_cols + kernel_desc().mod[i].col];
+#pragma unroll
+    for (int i = 0; i < kMaxModules; ++i)
+      if (i < d.n_active && es[i].rank != 0 && !entry_ok(es[i], d.max_rank)) ++errs;
+  }
   const int nerr = op_block_sum(errs, s_w);
   if (t == 0) {
     if (kept == nseg) od.seg.seg_offsets[nseg] = nvalid;
