@@ -20,7 +20,7 @@ __all__ = [
     "LoraError", "Segments", "segment_bound", "ModuleIO", "MODULES", "TABLE_ENTRY_DTYPE", "lib", "workspace_bytes",
     "build_segments", "shrink", "expand", "apply_layer", "apply_layer_noalloc", "decode_layer",
     "decode_layer_launches", "layer_shrink", "layer_expand", "pack_table", "STATIC_SCRATCH_BYTES",
-    "status_string", "MAX_RANK", "host_lib", "LinearIO", "LinearQ4IO", "Q4_GROUP",
+    "status_string", "MAX_RANK", "host_lib", "LinearIO", "LinearQ4IO", "Q4_GROUP", "MASK_INT8_ITEMS", "module_mask",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -372,6 +372,20 @@ def _ios(ios, num_rows):
         arr[i] = _IO(io.x.data_ptr(), io.x.stride(0), io.y.data_ptr(), io.y.stride(0), io.d_in, io.d_out)
         mask |= 1 << i
     return arr, mask
+
+
+MASK_INT8_ITEMS = 1 << 16  # LORA_MASK_INT8_ITEMS
+
+
+def module_mask(ios, int8_items: bool = False) -> int:
+    """The module_mask of the projections in ``ios`` ({name: io}); with
+    int8_items, LORA_MASK_INT8_ITEMS too (the table's entries are int8: the
+    shrink's items are sized for one-byte factors)."""
+    mask = 0
+    for i, name in enumerate(MODULES):
+        if name in ios:
+            mask |= 1 << i
+    return mask | (MASK_INT8_ITEMS if int8_items else 0)
 
 
 def _layer(fn, what, ios, num_rows, table, num_slots, seg, max_rank, ws, stream, module_mask):

@@ -56,6 +56,7 @@ struct ModuleArgs {
   int32_t d_in;
   int32_t d_out;
   int32_t col;
+  bool int8_items = false;  // the call's LORA_MASK_INT8_ITEMS: items sized for one-byte factors
 };
 
 // Work decomposition: the n-tile of the decode expand.  An item takes the
@@ -85,13 +86,16 @@ lora_status_t launched(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_E
 
 // Shrink k-chunk.  Prefill-sized batches: 2 * kKChunkMin (fewer partials to
 // write and sum).  Decode batches: about 128 KiB of A per item at the
-// launch's rank class (1024 k at rank 64, longer below), halved while the
-// batch would give fewer than 512 items, never below kKChunkMin (the
-// workspace is sized for that chunk).
+// launch's rank class (1024 k at rank 64, longer below; twice the k when the
+// caller states int8 factors, LORA_MASK_INT8_ITEMS), halved while the batch
+// would give fewer than 512 items, never below kKChunkMin (the workspace is
+// sized for that chunk).  Measured on the 70B layer at rank 64 with int8
+// factors: shrink 137 -> 109 us with 2048 k instead of 1024 (and bf16
+// factors 186 -> 196 us: the hint is the caller's).
 int pick_kc(int num_rows, int max_rank, int64_t max_seg, const ModuleArgs *ms, int n) {
   if (num_rows >= kPrefillRows) return 2 * kKChunkMin;
   const int cls = max_rank <= 8 ? 8 : max_rank <= 16 ? 16 : max_rank <= 32 ? 32 : 64;
-  int kc = kKChunkMin * (64 / cls);
+  int kc = kKChunkMin * (64 / cls) * (n > 0 && ms[0].int8_items ? 2 : 1);
   if (kc > 4 * kKChunkMin) kc = 4 * kKChunkMin;
   while (kc > kKChunkMin) {
     int64_t items = 0;
@@ -186,6 +190,8 @@ lora_status_t check_layer(const lora_module_io_t *io, uint32_t module_mask, int3
   if (!io || !table) return LORA_ERR_NULL;
   lora_status_t st = check_segments(seg);
   if (st != LORA_OK) return st;
+  const bool int8_items = (module_mask & LORA_MASK_INT8_ITEMS) != 0;
+  module_mask &= ~LORA_MASK_INT8_ITEMS;
   if (module_mask == 0 || module_mask >= (1u << LORA_NUM_MODULES)) return LORA_ERR_MODULE;
   if (num_rows < 0 || num_slots < 1) return LORA_ERR_SHAPE;
   if (max_rank < 1 || max_rank > LORA_MAX_RANK) return LORA_ERR_RANK;
@@ -199,7 +205,7 @@ lora_status_t check_layer(const lora_module_io_t *io, uint32_t module_mask, int3
     if ((m.d_in & 7) || (m.d_out & 7) || (m.ldx & 7) || (m.ldy & 7) || !aligned16(m.x) || !aligned16(m.y))
       return LORA_ERR_ALIGN;
     if (!fits_u32(num_rows, m.ldx) || !fits_u32(num_rows, m.ldy)) return LORA_ERR_SHAPE;
-    ms[n] = ModuleArgs{m.x, m.ldx, m.y, m.ldy, m.d_in, m.d_out, c};
+    ms[n] = ModuleArgs{m.x, m.ldx, m.y, m.ldy, m.d_in, m.d_out, c, int8_items};
     sum_d_in += m.d_in;
     ++n;
   }
@@ -557,6 +563,8 @@ lora_status_t linear_phase(bool do_shrink, bool do_fused, const IO *io, uint32_t
   if (!io || !table) return LORA_ERR_NULL;
   lora_status_t st = check_segments(seg);
   if (st != LORA_OK) return st;
+  const bool int8_items = (module_mask & LORA_MASK_INT8_ITEMS) != 0;
+  module_mask &= ~LORA_MASK_INT8_ITEMS;
   if (module_mask == 0 || module_mask >= (1u << LORA_NUM_MODULES)) return LORA_ERR_MODULE;
   if (num_rows < 0 || num_slots < 1) return LORA_ERR_SHAPE;
   if (max_rank < 1 || max_rank > LORA_MAX_RANK) return LORA_ERR_RANK;
@@ -571,7 +579,7 @@ lora_status_t linear_phase(bool do_shrink, bool do_fused, const IO *io, uint32_t
     if (st != LORA_OK) return st;
     const LinearArgs &m = la[n];
     if (!fits_u32(num_rows, m.ldx) || !fits_u32(num_rows, m.ldy)) return LORA_ERR_SHAPE;
-    ms[n] = ModuleArgs{m.x, m.ldx, m.y, m.ldy, m.d_in, m.d_out, c};
+    ms[n] = ModuleArgs{m.x, m.ldx, m.y, m.ldy, m.d_in, m.d_out, c, int8_items};
     sum_d_in += m.d_in;
     ++n;
   }

@@ -465,18 +465,19 @@ def main():
         d = dws[i % reps]
         if d.W is not None:
             d.build_segments(stream)
-            lg.linear_layer(d.lin_ios, w.num_rows, d.ids, d.table, w.num_slots, d.seg, w.max_rank, d.ws, stream)
+            lg.linear_layer(d.lin_ios, w.num_rows, d.ids, d.table, w.num_slots, d.seg, w.max_rank, d.ws, stream,
+                            module_mask=d.mask)
             return
         if stack is not None:
             lg.apply_layer_stacked(d.ios, w.num_rows, stack, d.table, w.num_slots, d.seg, w.max_rank, d.ws, stream,
-                                   pass_max_rank=pass_rank)
+                                   pass_max_rank=pass_rank, module_mask=d.mask)
             return
         if args.path == "decode":
             d.decode_layer(stream)  # segments + delta: one launch when the batch fits it, else three
             return
         d.build_segments(stream)
-        lg.layer_shrink(d.ios, w.num_rows, d.table, w.num_slots, d.seg, w.max_rank, d.ws, stream)
-        lg.layer_expand(d.ios, w.num_rows, d.table, w.num_slots, d.seg, w.max_rank, d.ws, stream)
+        lg.layer_shrink(d.ios, w.num_rows, d.table, w.num_slots, d.seg, w.max_rank, d.ws, stream, module_mask=d.mask)
+        lg.layer_expand(d.ios, w.num_rows, d.table, w.num_slots, d.seg, w.max_rank, d.ws, stream, module_mask=d.mask)
 
     for i in range(args.warmup):
         launch(i)
@@ -557,14 +558,14 @@ def main():
             seg_us = phase_us(lambda d: lg.build_segments(col, w.num_slots, d.seg, d.ws, stream))
         if w.W is not None:  # the fused call's two parts: grouped shrink (+ v sums), fused kernel
             shr_us = phase_us(lambda d: lg.linear_shrink(d.lin_ios, w.num_rows, d.ids, d.table, w.num_slots, d.seg,
-                                                         r, d.ws, stream))
+                                                         r, d.ws, stream, module_mask=d.mask))
             exp_us = phase_us(lambda d: lg.linear_expand(d.lin_ios, w.num_rows, d.ids, d.table, w.num_slots, d.seg,
-                                                         r, d.ws, stream))
+                                                         r, d.ws, stream, module_mask=d.mask))
         else:
             shr_us = phase_us(lambda d: lg.layer_shrink(d.ios, w.num_rows, d.table, w.num_slots, d.seg, r, d.ws,
-                                                        stream))
+                                                        stream, module_mask=d.mask))
             exp_us = phase_us(lambda d: lg.layer_expand(d.ios, w.num_rows, d.table, w.num_slots, d.seg, r, d.ws,
-                                                        stream))
+                                                        stream, module_mask=d.mask))
         per_pass.append({"segments": seg_us, "shrink": shr_us, "expand": exp_us})
         for ph, us in (("shrink", shr_us), ("expand", exp_us)):
             name = f"lora_fused_kernel<{'true' if q4 else 'false'}>" if (w.W is not None and ph == "expand") \
@@ -624,6 +625,7 @@ def main():
                            "timed region"},
         "launch": ("the K steps (and each kernel's K launches) replayed from one captured HIP graph, "
                    "after one untimed replay" if use_graph else "every launch from the host"),
+        "int8_items": bool(dws[0].int8_items),  # LORA_MASK_INT8_ITEMS passed (every targeted entry int8)
         "path": ("one launch (lora_decode_layer)" if one_launch else
                  "lora_decode_layer (three launches)" if args.path == "decode" and w.W is None and stack is None
                  else "separate launches"),

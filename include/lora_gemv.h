@@ -78,6 +78,17 @@ extern "C" {
 
 /* Table columns of a transformer layer, in this order. */
 #define LORA_NUM_MODULES 7
+
+/* A flag the layer calls (lora_apply_layer and its parts, lora_decode_layer,
+ * lora_apply_layer_noalloc, lora_apply_layer_stacked, lora_linear_layer and
+ * its parts and their _q4 forms) accept in module_mask beside the module
+ * bits: the caller's table entries are int8 (LORA_FORMAT_INT8_ROWS), so the
+ * shrink's work items take twice the k of a bf16 item (as many bytes per
+ * item).  Results are the same within the tolerance with or without it and
+ * for entries of either format; pass the same flag to both parts of a split
+ * call.  Source: "m07 -- Multi-Adapter (LoRA) Serving", "9. Bottlenecks and
+ * Evolution", item 3 (int8 adapters halve the bytes). */
+#define LORA_MASK_INT8_ITEMS (1u << 16)
 enum {
   LORA_Q = 0, LORA_K = 1, LORA_V = 2, LORA_O = 3,
   LORA_GATE = 4, LORA_UP = 5, LORA_DOWN = 6

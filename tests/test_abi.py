@@ -145,6 +145,8 @@ def ios(**over):
     (dict(io=None), NULL), (dict(table=None), NULL), (dict(ws=None), NULL), (dict(seg=seg(num_segments=None)), NULL),
     (dict(seg=seg(max_segments=-1)), SHAPE),
     (dict(mask=0), MODULE), (dict(mask=0x80), MODULE),
+    (dict(mask=1 << 16), MODULE), (dict(mask=0x7F | 1 << 17), MODULE),   # the int8-items flag alone; an unknown bit
+    (dict(mask=0x7F | 1 << 16, n=-1), SHAPE),                             # the flag with the modules is accepted
     (dict(n=-1), SHAPE), (dict(slots=0), SHAPE),
     (dict(max_rank=0), RANK), (dict(max_rank=100), RANK),
     (dict(io=ios(**{"3_x": None})), NULL), (dict(io=ios(**{"0_y": None})), NULL),

@@ -153,3 +153,33 @@ def test_int8_paged_table():
                             paged_capacity_rank=int(w.ranks.max()),
                             placement=rng.permutation(w.num_slots), fmt=fmt)
     check_workload(w2, oracle.lora_layer(w2), "layer")
+
+
+@pytest.mark.parametrize("fmt", ["int8", "bf16"])
+def test_int8_items_flag_with_either_format(fmt):
+    # LORA_MASK_INT8_ITEMS only sizes the shrink's items (twice the k): with
+    # or without it, and on bf16 entries too, the delta is within tolerance;
+    # the split call with the flag on both parts equals the whole call
+    from tests.parity import check_rows
+    rows, slots, d_in, d_out = 96, 96, 8192, 1032
+    ids = np.random.default_rng(9).permutation(rows)
+    w = bw(330, rows, slots, d_in, d_out, 64, ids, x_std=1.0, fmt=Q8 if fmt == "int8" else gen.FMT_BF16)
+    ref = oracle.lora_layer(w)["q"]
+    dw = DeviceWorkload(w)
+    import adapter_gemv_amd as lg
+    outs = {}
+    for flag in (False, True):
+        mask = lg.module_mask(dw.ios, int8_items=flag)
+        dw.reset_y(zero=True)
+        dw.build_segments()
+        lg.apply_layer(dw.ios, rows, dw.table, slots, dw.seg, w.max_rank, dw.ws, module_mask=mask)
+        torch.cuda.synchronize()
+        outs[flag] = bf16_host(dw.y["q"])
+        check_rows(outs[flag], ref.delta, f"{fmt} delta, int8 items {flag}")
+    mask = lg.module_mask(dw.ios, int8_items=True)
+    dw.reset_y(zero=True)
+    dw.build_segments()
+    lg.layer_shrink(dw.ios, rows, dw.table, slots, dw.seg, w.max_rank, dw.ws, module_mask=mask)
+    lg.layer_expand(dw.ios, rows, dw.table, slots, dw.seg, w.max_rank, dw.ws, module_mask=mask)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_host(dw.y["q"]), outs[True])

@@ -12,7 +12,7 @@ import torch
 
 import adapter_gemv_amd as lg
 
-from .gen import Workload
+from .gen import FMT_INT8_ROWS, Workload
 
 
 def bf16_tensor(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -49,6 +49,11 @@ class DeviceWorkload:
         # zeroed: the head of a workspace must start at zero (lora_decode_layer's hand-off words)
         self.ws = torch.zeros(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
         self.ios = {m.name: lg.ModuleIO(self.x[m.x_name], self.y[m.name]) for m in w.modules}
+        # every targeted entry int8: the layer calls size their items for one-byte factors
+        cols = [m.index for m in w.modules]
+        used = w.ranks[:, cols] > 0
+        self.int8_items = bool(used.any() and (w.fmt[:, cols][used] == FMT_INT8_ROWS).all())
+        self.mask = lg.module_mask(self.ios, int8_items=self.int8_items)
         self.W = self.lin_ios = None
         if w.W is not None:  # base weights: the fused calls, and a workspace for them
             self.W, self.lin_ios = {}, {}
@@ -91,15 +96,16 @@ class DeviceWorkload:
 
     def apply_layer(self, stream=None):
         lg.apply_layer(self.ios, self.w.num_rows, self.table, self.w.num_slots, self.seg, self.w.max_rank, self.ws,
-                       stream)
+                       stream, module_mask=self.mask)
 
     def decode_layer(self, stream=None):
         """Segments and every projection through lora_decode_layer."""
         lg.decode_layer(self.ios, self.w.num_rows, self.ids, self.table, self.w.num_slots, self.seg, self.w.max_rank,
-                        self.ws, stream)
+                        self.ws, stream, module_mask=self.mask)
 
     def decode_launches(self) -> int:
-        return lg.decode_layer_launches(self.ios, self.w.num_rows, self.w.num_slots, self.seg, self.w.max_rank)
+        return lg.decode_layer_launches(self.ios, self.w.num_rows, self.w.num_slots, self.seg, self.w.max_rank,
+                                        module_mask=self.mask)
 
     def step(self, stream=None):
         """One pass of the decode path: segments, then every projection."""
