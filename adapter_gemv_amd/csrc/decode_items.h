@@ -46,8 +46,9 @@ namespace lora {
 // the chunk's sum.  int8 rows are padded to 16 bytes, so the load stays in
 // its row; where d_in ends inside it, the second x piece lies past the row
 // of x and reads zero, and the padding bytes (always finite) add nothing.
-// row_of(r) gives the original row of sorted position pos0 + r.
-template <int JW, int RG, bool Q8, typename RowOf>
+// row_of(r) gives the original row of sorted position pos0 + r.  U steps of
+// loads go out together (a step past the chunk reads zeros).
+template <int JW, int RG, bool Q8, typename RowOf, int U = 1>
 __device__ __forceinline__ void decode_shrink_rows(const LayerDesc &d, const ModuleDesc &m, const void *A, int rank,
                                                    int jw, int pos0, int nrows, int chunk, RowOf row_of) {
   constexpr int VPL = Q8 ? 16 : 8;  // k per lane and step
@@ -69,20 +70,25 @@ __device__ __forceinline__ void decode_shrink_rows(const LayerDesc &d, const Mod
   float acc[JW * RG];
 #pragma unroll
   for (int i = 0; i < JW * RG; ++i) acc[i] = 0.f;
-  for (int k = k_begin + lane * VPL; k < k_end; k += 64 * VPL) {
-    const uint32_t voff = (uint32_t)k * 2;
+  for (int k0 = k_begin + lane * VPL; k0 < k_end; k0 += U * 64 * VPL) {
+#pragma unroll
+   for (int u = 0; u < U; ++u) {
+    const int k = k0 + u * 64 * VPL;
+    const bool kin = U == 1 || k < k_end;  // a step past the chunk reads zeros
+    const uint32_t voff = kin ? (uint32_t)k * 2 : kOutOfRange;
     u32x4 xv[RG], av[JW];
 #pragma unroll
     for (int r = 0; r < RG; ++r) xv[r] = r < nrows ? buf_ld16(rx[r], voff, 0) : zero4();
     if constexpr (Q8) {
       u32x4 xw[RG];  // x[k + 8, k + 16)
 #pragma unroll
-      for (int r = 0; r < RG; ++r) xw[r] = r < nrows ? buf_ld16(rx[r], voff + 16, 0) : zero4();
+      for (int r = 0; r < RG; ++r) xw[r] = r < nrows ? buf_ld16(rx[r], kin ? voff + 16 : kOutOfRange, 0) : zero4();
       u32x4 aq[JW];
 #pragma unroll
       for (int jj = 0; jj < JW; ++jj)
-        aq[jj] = (jj < jw && j0 + jj < rank) ? buf_ld16_stream(ra, (uint32_t)k, (uint32_t)(j0 + jj) * a_row_bytes)
-                                             : zero4();
+        aq[jj] = (jj < jw && j0 + jj < rank)
+                     ? buf_ld16_stream(ra, kin ? (uint32_t)k : kOutOfRange, (uint32_t)(j0 + jj) * a_row_bytes)
+                     : zero4();
 #pragma unroll
       for (int jj = 0; jj < JW; ++jj) {
         const u32x4 lo = i8x8_to_bf16x8(u32x2{aq[jj].x, aq[jj].y});
@@ -99,6 +105,7 @@ __device__ __forceinline__ void decode_shrink_rows(const LayerDesc &d, const Mod
 #pragma unroll
         for (int r = 0; r < RG; ++r) acc[jj * RG + r] = dot8_bf16(av[jj], xv[r], acc[jj * RG + r]);
     }
+   }
   }
   reduce_scatter<JW * RG, 64>(acc);
   float *out = d.part + ((int64_t)(m.part_base + chunk) * d.num_rows + pos0) * d.rs;
@@ -143,7 +150,19 @@ __device__ __forceinline__ void decode_shrink_block(const LayerDesc &d, int blk,
   auto run = [&](auto q8) {
     constexpr bool Q8 = decltype(q8)::value;
     if (len == 1) {
-      decode_shrink_rows<JW, 1, Q8>(d, m, e.A, rank, jw, pos0, 1, chunk, [&](int r) { return d.perm[pos0 + r]; });
+      // an entry of a lower rank than the launch's runs with its own rows per
+      // wave and two steps of loads in flight (C4's shrink 46.6 -> 45.1 us;
+      // the rank-64 layer 188 -> 183 us, a change of code layout only)
+      auto row = [&](int r) { return d.perm[pos0 + r]; };
+      auto by_rank = [&](auto jwc) {
+        constexpr int JWE = decltype(jwc)::value;
+        if constexpr (JWE < JW) decode_shrink_rows<JWE, 1, Q8, decltype(row), 2>(d, m, e.A, rank, jw, pos0, 1, chunk, row);
+        else decode_shrink_rows<JW, 1, Q8>(d, m, e.A, rank, jw, pos0, 1, chunk, row);
+      };
+      if (jw <= 2) by_rank(std::integral_constant<int, 2>{});
+      else if (jw <= 4) by_rank(std::integral_constant<int, 4>{});
+      else if (jw <= 8) by_rank(std::integral_constant<int, 8>{});
+      else by_rank(std::integral_constant<int, JW>{});
     } else {
       for (int r0 = 0; r0 < len; r0 += RGM) {
         const int p = pos0 + r0;
