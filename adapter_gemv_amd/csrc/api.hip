@@ -625,7 +625,7 @@ lora_status_t linear_phase(bool do_shrink, bool do_fused, const IO *io, uint32_t
     fm.d_in = m.d_in;
     fm.d_out = m.d_out;
     fm.col = ms[i].col;
-    fm.n_tiles = (m.d_out + kFusedCols - 1) / kFusedCols;
+    fm.n_tiles = (m.d_out + fused_cols(kQ4) - 1) / fused_cols(kQ4);
     fm.block_base = (int)blocks;
     blocks += (int64_t)row_tiles * fm.n_tiles;
   }

@@ -7,22 +7,28 @@
 // next steps puts the delta into the base product's epilogue with a wide
 // accumulator, so y is written once instead of written and then updated.
 //
-// A block takes kFusedRows rows (in their original order) and kFusedCols
-// output columns of one projection, over the whole d_in:
+// A block takes kFusedRows rows (in their original order) and fused_cols
+// output columns of one projection (128 over a bf16 W, 64 over a 4-bit W),
+// over the whole d_in:
 //   * main loop: x and W stream through LDS in rounds of 64 k, two rounds in
 //     flight in registers, as in the SGMV shrink (x rows from L2, W rows from
-//     HBM once, nontemporal, 128-byte line pieces); wave w turns rows
-//     [32w, 32w+32) x the 64 columns into 2 x 4 bf16 matrix-core tiles
-//     (16x16x32, fp32 accumulate).  Loading W straight into the matrix-core
-//     operand layout (16 rows x 64 bytes per instruction) with each wave
-//     owning 16 or 32 columns measured slower, and so did one register set
-//     for both B formats in the epilogue (a branch per row around the loads
-//     makes the compiler wait for all of them);
-//   * epilogue: the base tile goes to LDS, then each wave streams the B slice
-//     (the block's 64 rows of B_a, rank values each) of one of its rows per
-//     round, one round ahead, with the row's v (from the grouped shrink);
-//     8 lanes share a B row (8 values each), a reduce-scatter leaves one
-//     output column per lane, and y is written once.
+//     HBM once, nontemporal, 128-byte line pieces); each wave turns a 64 x 64
+//     (bf16 W: waves 2 x 2 over rows and columns) or 32 x 64 (4-bit W: one
+//     row band per wave) piece into 4 x 4 or 2 x 4 bf16 matrix-core tiles
+//     (16x16x32, fp32 accumulate).  The 128-column tile halves the x bytes
+//     read from L2 per byte of W; its 2 x 2 wave grid reads 8 operand
+//     fragments from LDS per step where 4 row bands of 32 read 10.  Loading
+//     W straight into the matrix-core operand layout (16 rows x 64 bytes per
+//     instruction) with each wave owning 16 or 32 columns measured slower,
+//     and so did one register set for both B formats in the epilogue (a
+//     branch per row around the loads makes the compiler wait for all of
+//     them);
+//   * epilogue: the base tile goes to LDS, then, for each 64-column half in
+//     turn, each wave streams the B slice (the half's 64 rows of B_a, rank
+//     values each) of one of its rows per round, one round ahead, with the
+//     row's v (from the grouped shrink); 8 lanes share a B row (8 values
+//     each), a reduce-scatter leaves one output column per lane, and y is
+//     written once.
 // The table entries of the block's rows are loaded with the first rounds of
 // the main loop (one row per lane), so the epilogue starts without waiting.
 #pragma once
@@ -46,9 +52,15 @@ __device__ __forceinline__ FusedModule fused_module_of(const FusedDesc &f, int b
   return fused_desc().mod[mi];
 }
 
-constexpr int kFusedBaseStride = kFusedCols + 1;  // floats per row of the base tile in LDS (odd: no bank clash)
-static_assert(kFusedRows * kFusedBaseStride * 4 <= 2 * kShrinkBufBytes, "base tile fits the round buffers");
-constexpr int kFusedLdsBytes = kShrinkLdsBytes;  // two round buffers of x and W, later the base tile
+// LDS of a block: two round buffers of x [128 rows] and W [fused_cols rows]
+// (64 k each), later the base tile [128 rows][fused_cols + 1 floats: odd, no
+// bank clash].
+constexpr int fused_buf_bytes(bool q4) { return kShrinkXBytes + fused_cols(q4) * kShrinkRound * 2; }
+constexpr int fused_base_stride(bool q4) { return fused_cols(q4) + 1; }
+constexpr int fused_lds_bytes(bool q4) {
+  return 2 * fused_buf_bytes(q4) > kFusedRows * fused_base_stride(q4) * 4 ? 2 * fused_buf_bytes(q4)
+                                                                          : kFusedRows * fused_base_stride(q4) * 4;
+}
 
 // One epilogue row: per lane 8 pieces of the B slice (q = 0..7: B row
 // n0 + 8q + lane/8, values 8*(lane%8) .. +8; bf16 16 bytes, or int8 8 bytes
@@ -62,14 +74,22 @@ struct FusedRowLoads {
 // Q4: the base weight is 4-bit with group scales (lora_linear_layer_q4).
 template <bool Q4>
 __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t *lds) {
-  constexpr int XL = kFusedRows * 8 / 256;   // x pieces per thread per round (4)
-  constexpr int WL = kFusedCols * 8 / 256;   // bf16 W pieces per thread per round (2)
-  constexpr int RPW = kFusedRows / 4;        // epilogue rows per wave (32)
+  constexpr int NC = fused_cols(Q4);          // output columns of the block
+  // waves: WR along the rows x 4 / WR along the columns; each takes MT x 4
+  // matrix-core tiles of 16 x 16
+  constexpr int WR = NC == 128 ? 2 : 4;
+  constexpr int MT = kFusedRows / WR / 16;
+  constexpr int NTL = 4;
+  constexpr int BS = fused_base_stride(Q4);
+  constexpr int XL = kFusedRows * 8 / 256;    // x pieces per thread per round (4)
+  constexpr int WL = NC * 8 / 256;            // bf16 W pieces per thread per round
+  constexpr int RPW = kFusedRows / 4;         // epilogue rows per wave (32)
   const int t = threadIdx.x, lane = t & 63, w = wave_id();
+  const int w_row = (w % WR) * (kFusedRows / WR), w_col = (w / WR) * (NC * WR / 4);
   const FusedModule m = fused_module_of(f, blk);
   const int local = blk - m.block_base;
   const int rt = local / m.n_tiles, tile = local - rt * m.n_tiles;
-  const int row0 = rt * kFusedRows, n0 = tile * kFusedCols;
+  const int row0 = rt * kFusedRows, n0 = tile * NC;
 
   // Segments come in ascending slot order, so the slots with a segment in
   // this build are the valid ones up to the last segment's.
@@ -139,25 +159,26 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
         *(u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(i * 32 + (t >> 3), piece)) = st.wv[i];
     }
   };
-  f32x4_t acc[2][4];
+  f32x4_t acc[MT][NTL];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < NTL; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int r_in = lane & 15, g = lane >> 4;
-  auto compute = [&](const uint8_t *buf, f32x4_t (&acc)[2][4]) {
+  auto compute = [&](const uint8_t *buf, f32x4_t (&acc)[MT][NTL]) {
 #pragma unroll
     for (int ks = 0; ks < kShrinkRound / 32; ++ks) {
-      u32x4 xo[2], wo[4];
+      u32x4 xo[MT], wo[NTL];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) xo[mt] = *(const u32x4 *)(buf + shrink_lds_off(w * 32 + mt * 16 + r_in, ks * 4 + g));
+      for (int mt = 0; mt < MT; ++mt)
+        xo[mt] = *(const u32x4 *)(buf + shrink_lds_off(w_row + mt * 16 + r_in, ks * 4 + g));
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        wo[nt] = *(const u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(nt * 16 + r_in, ks * 4 + g));
+      for (int nt = 0; nt < NTL; ++nt)
+        wo[nt] = *(const u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(w_col + nt * 16 + r_in, ks * 4 + g));
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < NTL; ++nt)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xo[mt]),
                                                                 __builtin_bit_cast(bf16x8_t, wo[nt]), acc[mt][nt], 0,
                                                                 0, 0);
@@ -168,14 +189,15 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
   // output column (this lane's columns n0 + 16 nt + r_in), requested one
   // step ahead
   static_assert(2 * kShrinkRound == kQ4Group, "one group per main-loop step");
-  f32x4_t gacc[Q4 ? 2 : 1][Q4 ? 4 : 1];
+  static_assert(!Q4 || (MT == 2 && NC == 64), "4-bit blocks take 64 columns, one row band per wave");
+  f32x4_t gacc[Q4 ? MT : 1][Q4 ? 4 : 1];
   float sc_cur[4] = {0.f, 0.f, 0.f, 0.f}, sc_nxt[4] = {0.f, 0.f, 0.f, 0.f};
   const rsrc_t rs_w = make_rsrc(Q4 ? m.Ws : nullptr, Q4 ? (uint32_t)((int64_t)m.d_out * m.ldws * 4) : 0u);
   const int n_groups = Q4 ? m.d_in / kQ4Group : 0;
   auto load_scales = [&](float (&sc)[4], int grp) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const int n = n0 + nt * 16 + r_in;
+      const int n = n0 + w_col + nt * 16 + r_in;
       sc[nt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                              rs_w, n < m.d_out && grp < n_groups ?
                                                        (uint32_t)(((int64_t)n * m.ldws + grp) * 4) : kOutOfRange,
@@ -189,11 +211,11 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
   load(s1, kShrinkRound);
   const int rounds = (m.d_in + kShrinkRound - 1) / kShrinkRound;
   for (int r = 0; r < rounds; r += 2) {
-    uint8_t *b0 = lds, *b1 = lds + kShrinkBufBytes;
+    uint8_t *b0 = lds, *b1 = lds + fused_buf_bytes(Q4);
     if constexpr (Q4) {
       load_scales(sc_nxt, r / 2 + 1);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) gacc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -208,7 +230,7 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
     if constexpr (Q4) {
       compute(b1, gacc);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -225,15 +247,17 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
   // 32w + 16mt + 4*(l/16) + i, column 16nt + l%16.
   float *base = reinterpret_cast<float *>(lds);
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        base[(w * 32 + mt * 16 + g * 4 + i) * kFusedBaseStride + nt * 16 + r_in] = acc[mt][nt][i];
+        base[(w_row + mt * 16 + g * 4 + i) * BS + w_col + nt * 16 + r_in] = acc[mt][nt][i];
   __syncthreads();
 
-  // Epilogue: row rr = w + 4i of the tile in round i.
+  // Epilogue: row rr = w + 4i of the tile in round i, over each 64-column
+  // half of the block's columns in turn.
+  int nh = n0, ch = 0;  // the half's first output column, and its column in the base tile
   const int bl = lane >> 3, pc = lane & 7, j0 = pc * 8;
   const int c = 8 * pc + bl;  // this lane's output column after the reduce-scatter
   const rsrc_t ry = make_rsrc(m.y, (uint32_t)((int64_t)f.num_rows * m.ldy * 2));
@@ -277,7 +301,7 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
     const rsrc_t rb = make_rsrc(ri.ok ? vals : nullptr, ri.ok ? (uint32_t)m.d_out * row_bytes : 0u);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const int n = n0 + 8 * q + bl;
+      const int n = nh + 8 * q + bl;
       const bool lon = on && n < m.d_out;
       const uint32_t off = (uint32_t)n * row_bytes + (uint32_t)j0 * (q8 ? 1 : 2);
       L.b16[q] = buf_ld16_stream(rb, lon && !q8 ? off : kOutOfRange, 0);
@@ -308,24 +332,28 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
       }
       reduce_scatter<8, 8>(acc8);
       dl = acc8[0] * ri.scale;
-      if (ri.fmt == LORA_FORMAT_INT8_ROWS && n0 + c < m.d_out)
-        dl *= reinterpret_cast<const float *>(ri.B)[n0 + c];  // the B row's scale
+      if (ri.fmt == LORA_FORMAT_INT8_ROWS && nh + c < m.d_out)
+        dl *= reinterpret_cast<const float *>(ri.B)[nh + c];  // the B row's scale
     }
-    const float yv = base[rr * kFusedBaseStride + c] + dl;
-    buf_st_u16(ry, n0 + c < m.d_out ? (uint32_t)(((int64_t)ri.b * m.ldy + n0 + c) * 2) : kOutOfRange,
+    const float yv = base[rr * BS + ch + c] + dl;
+    buf_st_u16(ry, nh + c < m.d_out ? (uint32_t)(((int64_t)ri.b * m.ldy + nh + c) * 2) : kOutOfRange,
                f32_to_bf16(yv));
   };
-  FusedRowLoads cur, nxt;
-  RowInfo ci = row_info(0);
-  issue(ci, cur);
-  for (int i = 0; i + 1 < RPW; ++i) {  // row i+1 is requested before row i is finished
-    const RowInfo ni = row_info(i + 1);
-    issue(ni, nxt);
-    finish(ci, cur, w + 4 * i);
-    cur = nxt;
-    ci = ni;
+  for (int h = 0; h < NC / 64; ++h) {
+    nh = n0 + 64 * h;
+    ch = 64 * h;
+    FusedRowLoads cur, nxt;
+    RowInfo ci = row_info(0);
+    issue(ci, cur);
+    for (int i = 0; i + 1 < RPW; ++i) {  // row i+1 is requested before row i is finished
+      const RowInfo ni = row_info(i + 1);
+      issue(ni, nxt);
+      finish(ci, cur, w + 4 * i);
+      cur = nxt;
+      ci = ni;
+    }
+    finish(ci, cur, w + 4 * (RPW - 1));
   }
-  finish(ci, cur, w + 4 * (RPW - 1));
 }
 
 }  // namespace lora

@@ -140,10 +140,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void l
   else op_delta<CLS, false>(m, e, c, tpb, t, a, idu, od.bound_check, d.max_seg, lds);
 }
 
-// Base projection + delta (fused_items.h).
+// Base projection + delta (fused_items.h).  Two blocks per CU (their LDS
+// and registers): compiled for 2 waves per SIMD, which the 128-column bf16
+// tile's accumulators need without spilling.
 template <bool Q4>
-__global__ __launch_bounds__(256) void lora_fused_kernel(FusedDesc f) {
-  __shared__ __align__(16) uint8_t lds[kFusedLdsBytes];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void lora_fused_kernel(FusedDesc f) {
+  __shared__ __align__(16) uint8_t lds[fused_lds_bytes(Q4)];
   fused_block<Q4>(f, blockIdx.x, lds);
 }
 

@@ -98,9 +98,12 @@ struct LayerDesc {
 };
 
 // Fused base projection + delta: a block computes y for kFusedRows rows and
-// kFusedCols output columns of one projection.
+// fused_cols(q4) output columns of one projection.
 constexpr int kFusedRows = 128;
-constexpr int kFusedCols = 64;
+// Output columns of a block: 128 with a bf16 base (half the x read from L2
+// per byte of W), 64 with a 4-bit base (its group sums double the
+// accumulators).
+constexpr int fused_cols(bool q4) { return q4 ? 64 : 128; }
 
 // 4-bit base weights: inputs per scale (a group of consecutive inputs of one
 // output row); the fused kernel's two 64-k rounds per main-loop step make one.
@@ -121,7 +124,7 @@ struct FusedModule {
   int32_t d_out;
   int32_t col;         // table column
   int32_t block_base;  // first block of this module
-  int32_t n_tiles;     // column tiles of kFusedCols
+  int32_t n_tiles;     // column tiles of fused_cols(q4)
 };
 
 struct FusedDesc {
