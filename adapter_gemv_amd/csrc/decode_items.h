@@ -47,13 +47,15 @@ namespace lora {
 // its row; where d_in ends inside it, the second x piece lies past the row
 // of x and reads zero, and the padding bytes (always finite) add nothing.
 // row_of(r) gives the original row of sorted position pos0 + r.  U steps of
-// loads go out together (a step past the chunk reads zeros).
+// loads go out together (a step past the chunk reads zeros).  The rows of A
+// taken start at j_base (a pass over part of the entry's rows).
 template <int JW, int RG, bool Q8, typename RowOf, int U = 1>
 __device__ __forceinline__ void decode_shrink_rows(const LayerDesc &d, const ModuleDesc &m, const void *A, int rank,
-                                                   int jw, int pos0, int nrows, int chunk, RowOf row_of) {
+                                                   int jw, int pos0, int nrows, int chunk, RowOf row_of,
+                                                   int j_base = 0) {
   constexpr int VPL = Q8 ? 16 : 8;  // k per lane and step
   const int lane = threadIdx.x & 63;
-  const int j0 = wave_id() * jw;
+  const int j0 = j_base + wave_id() * jw;
   const int k_begin = chunk * d.kc;
   const int k_end = min(k_begin + d.kc, m.d_in);
   const uint32_t row_bytes = (uint32_t)m.d_in * 2;
@@ -131,10 +133,16 @@ __device__ __forceinline__ void decode_shrink_rows(const LayerDesc &d, const Mod
 }
 
 // Block `blk` of the decode shrink numbering (nseg: the segments built).  JW
-// = rows of A per wave at the largest rank of the launch (4*JW).
+// = rows of A per wave at the largest rank of the launch (4*JW).  An item
+// runs at its entry's own rows of A per wave (rank/4, rounded up to a power
+// of two), and a multi-row item with all its rows (at most kLongSegRows - 1)
+// against each load of A, their count rounded up to 2, 4 or 8; where rows of
+// A per wave times rows of x would pass 64 sums, the rows of A go in passes
+// of 64/RG per wave.  Two steps of loads are in flight where the registers
+// allow.
 template <int JW>
 __device__ __forceinline__ void decode_shrink_block(const LayerDesc &d, int blk, int nseg) {
-  constexpr int RGM = 4;  // rows of x per pass for multi-row segments
+  static_assert(kLongSegRows <= 8, "a decode segment's rows meet A in one pass");
   const int s = blk / d.items_per_seg;
   if (s >= nseg) return;
   const int it = blk - s * d.items_per_seg;
@@ -149,27 +157,36 @@ __device__ __forceinline__ void decode_shrink_block(const LayerDesc &d, int blk,
   const int jw = (rank + 3) >> 2;
   auto run = [&](auto q8) {
     constexpr bool Q8 = decltype(q8)::value;
-    if (len == 1) {
-      // an entry of a lower rank than the launch's runs with its own rows per
-      // wave and two steps of loads in flight (C4's shrink 46.6 -> 45.1 us;
-      // the rank-64 layer 188 -> 183 us, a change of code layout only)
-      auto row = [&](int r) { return d.perm[pos0 + r]; };
-      auto by_rank = [&](auto jwc) {
-        constexpr int JWE = decltype(jwc)::value;
-        if constexpr (JWE < JW) decode_shrink_rows<JWE, 1, Q8, decltype(row), 2>(d, m, e.A, rank, jw, pos0, 1, chunk, row);
-        else decode_shrink_rows<JW, 1, Q8>(d, m, e.A, rank, jw, pos0, 1, chunk, row);
-      };
-      if (jw <= 2) by_rank(std::integral_constant<int, 2>{});
-      else if (jw <= 4) by_rank(std::integral_constant<int, 4>{});
-      else if (jw <= 8) by_rank(std::integral_constant<int, 8>{});
-      else by_rank(std::integral_constant<int, JW>{});
-    } else {
-      for (int r0 = 0; r0 < len; r0 += RGM) {
-        const int p = pos0 + r0;
-        decode_shrink_rows<JW, RGM, Q8>(d, m, e.A, rank, jw, p, min(RGM, len - r0), chunk,
-                                        [&](int r) { return d.perm[p + r]; });
+    auto row = [&](int r) { return d.perm[pos0 + r]; };
+    auto by_shape = [&](auto jwc, auto rgc) {
+      constexpr int JWE = decltype(jwc)::value, RG = decltype(rgc)::value;
+      if constexpr (JWE <= JW) {
+        if constexpr (RG == 1) {
+          // one row: two steps in flight below the launch's rank (at rank 64
+          // the registers hold one)
+          constexpr int U = JWE < JW ? 2 : 1;
+          decode_shrink_rows<JWE, 1, Q8, decltype(row), U>(d, m, e.A, rank, jw, pos0, 1, chunk, row);
+        } else if constexpr (JWE * RG <= 64) {
+          constexpr int U = RG * (Q8 ? 2 : 1) + JWE <= 12 ? 2 : 1;
+          decode_shrink_rows<JWE, RG, Q8, decltype(row), U>(d, m, e.A, rank, jw, pos0, len, chunk, row);
+        } else {
+          constexpr int JP = 64 / RG;  // rows of A per wave and pass
+          constexpr int U = RG * (Q8 ? 2 : 1) + JP <= 12 ? 2 : 1;
+          for (int jb = 0; jb < rank; jb += 4 * JP)
+            decode_shrink_rows<JP, RG, Q8, decltype(row), U>(d, m, e.A, rank, JP, pos0, len, chunk, row, jb);
+        }
       }
-    }
+    };
+    auto by_rank = [&](auto rgc) {
+      if (jw <= 2) by_shape(std::integral_constant<int, 2>{}, rgc);
+      else if (jw <= 4) by_shape(std::integral_constant<int, 4>{}, rgc);
+      else if (jw <= 8) by_shape(std::integral_constant<int, 8>{}, rgc);
+      else by_shape(std::integral_constant<int, JW>{}, rgc);
+    };
+    if (len == 1) by_rank(std::integral_constant<int, 1>{});
+    else if (len == 2) by_rank(std::integral_constant<int, 2>{});
+    else if (len <= 4) by_rank(std::integral_constant<int, 4>{});
+    else by_rank(std::integral_constant<int, 8>{});
   };
   if (e.format == LORA_FORMAT_INT8_ROWS) run(std::true_type{});
   else run(std::false_type{});
