@@ -1,6 +1,7 @@
 // C ABI of the LoRA-delta library: argument checks, work decomposition and
 // launches.  Every check runs before the first HIP call, so a rejected call
 // touches neither the device nor the stream.
+#include <algorithm>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -606,13 +607,21 @@ lora_status_t linear_phase(bool do_shrink, bool do_fused, const IO *io, uint32_t
     if (st != LORA_OK) return st;
   }
   if (!do_fused) return LORA_OK;
-  // 3. base projection + delta
+  // 3. base projection + delta.  A block's work grows with its module's
+  // d_in, and the blocks are dispatched in order, so the modules are numbered
+  // longest first: a module of a long d_in (a down projection, 3.5x the
+  // others) numbered last would start when the others are done and run
+  // alone for most of the launch.
   FusedDesc f{};
   const int row_tiles = (num_rows + kFusedRows - 1) / kFusedRows;
+  int order[LORA_NUM_MODULES];
+  for (int i = 0; i < n; ++i) order[i] = i;
+  std::stable_sort(order, order + n, [&](int a, int b) { return la[a].d_in > la[b].d_in; });
   int64_t blocks = 0;
-  for (int i = 0; i < n; ++i) {
+  for (int j = 0; j < n; ++j) {
+    const int i = order[j];
     const LinearArgs &m = la[i];
-    FusedModule &fm = f.mod[i];
+    FusedModule &fm = f.mod[j];
     fm.x = static_cast<const uint16_t *>(m.x);
     fm.ldx = m.ldx;
     fm.W = m.W;
