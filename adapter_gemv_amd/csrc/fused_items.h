@@ -10,9 +10,9 @@
 // A block takes kFusedRows rows (in their original order) and fused_cols
 // output columns of one projection (128 over a bf16 W, 64 over a 4-bit W),
 // over the whole d_in:
-//   * main loop: x and W stream through LDS in rounds of 64 k, two rounds in
-//     flight in registers, as in the SGMV shrink (x rows from L2, W rows from
-//     HBM once, nontemporal, 128-byte line pieces); each wave turns a 64 x 64
+//   * main loop: x and W stream through LDS in rounds of 64 k, x two rounds
+//     and W three rounds ahead in registers (x rows from L2, W rows from HBM
+//     once, nontemporal, 128-byte line pieces); each wave turns a 64 x 64
 //     (bf16 W: waves 2 x 2 over rows and columns) or 32 x 64 (4-bit W: one
 //     row band per wave) piece into 4 x 4 or 2 x 4 bf16 matrix-core tiles
 //     (16x16x32, fp32 accumulate).  The 128-column tile halves the x bytes
@@ -126,16 +126,23 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
     woff[i] = n < m.d_out ? (uint32_t)((int64_t)n * w_row_bytes) : kOutOfRange;
   }
   using WRaw = typename std::conditional<Q4, u32x2, u32x4>::type;
-  struct Stage {
+  struct XStage {
     u32x4 x[XL];
+  };
+  struct WStage {
     WRaw wv[WP];
   };
-  auto load = [&](Stage &st, int k0) {  // one round; past d_in: zero, no traffic
+  auto load_x = [&](XStage &st, int k0) {  // one round; past d_in: zero, no traffic
     const int k = k0 + piece * 8;
     const bool kon = k < m.d_in;
     const uint32_t kb = (uint32_t)k * 2;
 #pragma unroll
     for (int i = 0; i < XL; ++i) st.x[i] = buf_ld16(rx, kon && xoff[i] != kOutOfRange ? xoff[i] + kb : kOutOfRange, 0);
+  };
+  auto load_w = [&](WStage &st, int k0) {
+    const int k = k0 + piece * 8;
+    const bool kon = k < m.d_in;
+    const uint32_t kb = (uint32_t)k * 2;
     if constexpr (Q4) {
       const int kq = k0 + 16 * (t & 3);
       st.wv[0] = __builtin_amdgcn_raw_buffer_load_b64(
@@ -146,17 +153,17 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
         st.wv[i] = buf_ld16_stream(rw, kon && woff[i] != kOutOfRange ? woff[i] + kb : kOutOfRange, 0);
     }
   };
-  auto store = [&](const Stage &st, uint8_t *buf) {
+  auto store = [&](const XStage &xs, const WStage &ws, uint8_t *buf) {
 #pragma unroll
-    for (int i = 0; i < XL; ++i) *(u32x4 *)(buf + shrink_lds_off(i * 32 + (t >> 3), piece)) = st.x[i];
+    for (int i = 0; i < XL; ++i) *(u32x4 *)(buf + shrink_lds_off(i * 32 + (t >> 3), piece)) = xs.x[i];
     if constexpr (Q4) {
       const int row = t >> 2, p0 = 2 * (t & 3);
-      *(u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(row, p0)) = q4x8_to_bf16x8(st.wv[0].x);
-      *(u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(row, p0 + 1)) = q4x8_to_bf16x8(st.wv[0].y);
+      *(u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(row, p0)) = q4x8_to_bf16x8(ws.wv[0].x);
+      *(u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(row, p0 + 1)) = q4x8_to_bf16x8(ws.wv[0].y);
     } else {
 #pragma unroll
       for (int i = 0; i < WL; ++i)
-        *(u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(i * 32 + (t >> 3), piece)) = st.wv[i];
+        *(u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(i * 32 + (t >> 3), piece)) = ws.wv[i];
     }
   };
   f32x4_t acc[MT][NTL];
@@ -205,41 +212,59 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
     }
   };
   if constexpr (Q4) load_scales(sc_cur, 0);
-  // Two rounds in flight; round i goes to buffer i & 1 (see the SGMV shrink).
-  Stage s0, s1;
-  load(s0, 0);
-  load(s1, kShrinkRound);
+  // x (mostly from L2) two rounds ahead, W (from HBM) three: round r goes
+  // to LDS buffer r & 1 once its loads are in, and then x of round r + 2 and
+  // W of round r + 3 are requested into the registers it leaves.
+  XStage x0, x1;
+  WStage w0, w1, w2;
+  load_x(x0, 0);
+  load_w(w0, 0);
+  load_w(w1, kShrinkRound);
+  load_x(x1, kShrinkRound);
+  load_w(w2, 2 * kShrinkRound);
   const int rounds = (m.d_in + kShrinkRound - 1) / kShrinkRound;
-  for (int r = 0; r < rounds; r += 2) {
-    uint8_t *b0 = lds, *b1 = lds + fused_buf_bytes(Q4);
-    if constexpr (Q4) {
+  uint8_t *b0 = lds, *b1 = lds + fused_buf_bytes(Q4);
+  auto step = [&](int r, auto odd, XStage &xs, WStage &ws, uint8_t *buf) {
+    constexpr bool kOdd = decltype(odd)::value;
+    if constexpr (Q4 && !kOdd) {
       load_scales(sc_nxt, r / 2 + 1);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) gacc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    store(s0, b0);
-    load(s0, (r + 2) * kShrinkRound);
-    __syncthreads();
-    if constexpr (Q4) compute(b0, gacc);
-    else compute(b0, acc);
-    store(s1, b1);
-    load(s1, (r + 3) * kShrinkRound);
+    store(xs, ws, buf);
+    load_x(xs, (r + 2) * kShrinkRound);
+    load_w(ws, (r + 3) * kShrinkRound);
     __syncthreads();
     if constexpr (Q4) {
-      compute(b1, gacc);
+      compute(buf, gacc);
+      if constexpr (kOdd) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+          for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(sc_cur[nt], gacc[mt][nt][i], acc[mt][nt][i]);
+            for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(sc_cur[nt], gacc[mt][nt][i], acc[mt][nt][i]);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) sc_cur[nt] = sc_nxt[nt];
+        for (int nt = 0; nt < 4; ++nt) sc_cur[nt] = sc_nxt[nt];
+      }
     } else {
-      compute(b1, acc);
+      compute(buf, acc);
     }
+  };
+  using Even = std::false_type;
+  using Odd = std::true_type;
+  // Six rounds per pass (one per pairing of the x and W registers); rounds
+  // past d_in read zeros and add nothing.  (An exit between the rounds of a
+  // pass makes the compiler spill.)
+  for (int r = 0; r < rounds; r += 6) {
+    step(r, Even{}, x0, w0, b0);
+    step(r + 1, Odd{}, x1, w1, b1);
+    step(r + 2, Even{}, x0, w2, b0);
+    step(r + 3, Odd{}, x1, w0, b1);
+    step(r + 4, Even{}, x0, w1, b0);
+    step(r + 5, Odd{}, x1, w2, b1);
   }
   __syncthreads();  // every wave is done with the round buffers
 
