@@ -159,17 +159,34 @@ void fill_desc(LayerDesc &d, const ModuleArgs *ms, int n, bool shrink, int num_r
 // The SGMV kernels address an activation matrix with 32-bit byte offsets.
 bool fits_u32(int64_t rows, int64_t ld) { return rows * ld * 2 <= (int64_t)0xFFFFFF00; }
 
+// A prefill batch's partials are summed once into their first chunk after
+// the shrink (fold_partials_kernel): every SGMV expand tile of a row tile
+// (d_out / 1024 of them per projection) would otherwise sum all the chunks
+// again, and the tiles of one row tile run on different XCDs, so each
+// fetches them from HBM.
+bool folds_partials(const LayerDesc &d) {
+  if (d.num_rows < kPrefillRows) return false;
+  for (int i = 0; i < d.n_active; ++i)
+    if (d.mod[i].n_chunks > 1) return true;
+  return false;
+}
+
 // Launch one phase (shrink or expand) over every module: decode items for
 // every possible segment and SGMV items for every row tile that segments of
 // at least kLongSegRows rows can produce (the kernels put the tiles the
-// build counted first and let the rest of that room exit).
+// build counted first and let the rest of that room exit).  fold: the
+// phase's partials pass from this call's shrink to its expand (not to a
+// caller's v or the fused kernel's planes), so a prefill batch folds them.
 lora_status_t launch_phase(bool shrink, const ModuleArgs *ms, int n, int num_rows, int num_slots, int max_rank,
                            int table_cols, const lora_adapter_entry_t *table, const lora_segments_t &seg, void *ws,
-                           const float *v_in, int64_t ldv, hipStream_t s) {
+                           const float *v_in, int64_t ldv, hipStream_t s, bool fold = false) {
   LayerDesc d;
   fill_desc(d, ms, n, shrink, num_rows, num_slots, max_rank, table_cols, table, seg, ws);
   d.v = v_in;
   d.ldv = ldv;
+  const bool folded = fold && v_in == nullptr && folds_partials(d);
+  if (folded && !shrink)
+    for (int i = 0; i < n; ++i) d.mod[i].n_chunks = 1;  // the sums wait in each module's first chunk
   // a call counts each bad segment and entry once: the shrink of a layer call,
   // or lora_expand on the caller's v
   d.count_errors = shrink || v_in != nullptr;
@@ -180,7 +197,9 @@ lora_status_t launch_phase(bool shrink, const ModuleArgs *ms, int n, int num_row
          (shrink ? d.items_per_seg : d.sg_items);
   if (dec + sg > 0x7fffffff) return LORA_ERR_SHAPE;
   const hipError_t e = shrink ? launch_shrink(d, (int)dec, (int)(dec + sg), s) : launch_expand(d, (int)dec, (int)(dec + sg), s);
-  return launched(e);
+  const lora_status_t st = launched(e);
+  if (st != LORA_OK || !(folded && shrink)) return st;
+  return launched(launch_fold_partials(d, s));
 }
 
 // Common checks of the layer calls; fills the module list.
@@ -230,11 +249,13 @@ lora_status_t layer_phase(bool do_shrink, bool do_expand, const lora_module_io_t
   ws = scratch;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (do_shrink) {
-    st = launch_phase(true, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
+    st = launch_phase(true, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s,
+                      true);
     if (st != LORA_OK) return st;
   }
   if (do_expand)
-    st = launch_phase(false, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
+    st = launch_phase(false, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s,
+                      true);
   return st;
 }
 
@@ -454,10 +475,11 @@ lora_status_t lora_decode_layer(const lora_module_io_t *io, uint32_t module_mask
   st = launched(launch_build_segments(row_adapter, 1, num_rows, num_slots, false, seg, seg_scratch, s));
   if (st != LORA_OK || num_rows == 0) return st;
   // the three-launch path
-  st = launch_phase(true, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, scratch, nullptr, 0, s);
+  st = launch_phase(true, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, scratch, nullptr, 0, s,
+                    true);
   if (st != LORA_OK) return st;
   return launch_phase(false, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, scratch, nullptr, 0,
-                      s);
+                      s, true);
 }
 
 int32_t lora_decode_layer_launches(const lora_module_io_t *io, uint32_t module_mask, int32_t num_rows,
@@ -504,9 +526,9 @@ lora_status_t lora_apply_layer_stacked(const lora_module_io_t *io, uint32_t modu
     st = launched(launch_build_segments(row_adapters + t, depth, num_rows, num_slots, t > 0, seg, ws, s));
     if (st != LORA_OK || num_rows == 0) return st;  // no rows: the first pass only resets the segments
     const int r = pass_max_rank ? pass_max_rank[t] : max_rank;  // the pass's launch class
-    st = launch_phase(true, ms, n, num_rows, num_slots, r, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
+    st = launch_phase(true, ms, n, num_rows, num_slots, r, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s, true);
     if (st != LORA_OK) return st;
-    st = launch_phase(false, ms, n, num_rows, num_slots, r, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
+    st = launch_phase(false, ms, n, num_rows, num_slots, r, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s, true);
     if (st != LORA_OK) return st;
   }
   return LORA_OK;
@@ -752,7 +774,8 @@ extern "C" lora_status_t lora_apply_layer_noalloc(const lora_module_io_t *io, ui
   st = scratch_address(&ws);
   if (st != LORA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = launch_phase(true, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
+  st = launch_phase(true, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s, true);
   if (st != LORA_OK) return st;
-  return launch_phase(false, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s);
+  return launch_phase(false, ms, n, num_rows, num_slots, max_rank, LORA_NUM_MODULES, table, seg, ws, nullptr, 0, s,
+                      true);
 }

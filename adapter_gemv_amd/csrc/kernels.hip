@@ -102,6 +102,31 @@ __global__ __launch_bounds__(256) void shrink_reduce_kernel(LayerDesc d) {
   if ((unsigned)b < (unsigned)d.num_rows) v_out[(int64_t)b * d.ldv + j] = sum;
 }
 
+// Sum the k-chunk partials of every row in a segment into its first chunk,
+// for module blockIdx.y.  A prefill call runs this between its shrink and
+// its expand, whose SGMV tiles (one per 1024 columns of a row tile) then
+// read one chunk each instead of summing them all again.  A thread owns 4
+// columns of one row: it reads them in every chunk and writes the sum over
+// the first, so no two threads touch the same words.  Columns past an
+// entry's rank are summed like the others and never read.
+__global__ __launch_bounds__(256) void fold_partials_kernel(LayerDesc d) {
+  const int nseg = min(*d.num_segments, d.max_seg);
+  if (nseg <= 0) return;
+  const int nvalid = min(d.seg_offsets[nseg], d.num_rows);
+  const int quads = d.rs / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int p = (int)(idx / quads);
+  if (p >= nvalid) return;
+  const int jq = (int)(idx - (int64_t)p * quads) * 4;
+  const ModuleDesc m = kernel_desc().mod[blockIdx.y];
+  if (m.n_chunks < 2) return;
+  const int64_t chunk_stride = (int64_t)d.num_rows * d.rs;
+  float *first = d.part + ((int64_t)m.part_base * d.num_rows + p) * d.rs + jq;
+  f32x4_t sum = *(const f32x4_t *)first;
+  for (int c = 1; c < m.n_chunks; ++c) sum += *(const f32x4_t *)(first + c * chunk_stride);
+  *(f32x4_t *)first = sum;
+}
+
 // One-launch decode (onepass_items.h): block 0 writes the segments; blocks
 // 1.. are (item, row), item-major over row_slots (a multiple of 8) rows, so
 // the blocks of one row share an XCD when blocks are dealt to the XCDs in
@@ -186,6 +211,13 @@ hipError_t launch_shrink_reduce(const LayerDesc &d, hipStream_t stream) {
   const int64_t total = (int64_t)d.num_rows * d.max_rank;
   if (total <= 0) return hipSuccess;
   shrink_reduce_kernel<<<dim3((unsigned)((total + 255) / 256), (unsigned)d.n_active), 256, 0, stream>>>(d);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold_partials(const LayerDesc &d, hipStream_t stream) {
+  const int64_t total = (int64_t)d.num_rows * (d.rs / 4);
+  if (total <= 0) return hipSuccess;
+  fold_partials_kernel<<<dim3((unsigned)((total + 255) / 256), (unsigned)d.n_active), 256, 0, stream>>>(d);
   return hipGetLastError();
 }
 

@@ -185,6 +185,8 @@ size_t partials_ws_bytes(int num_rows, int max_rank, int64_t sum_d_in);
 hipError_t launch_build_segments(const int32_t *ids, int stride, int n, int num_slots, bool add_status,
                                  const lora_segments_t &seg, void *ws, hipStream_t stream);
 hipError_t launch_shrink_reduce(const LayerDesc &d, hipStream_t stream);
+// Sum each row's k-chunk partials into its first chunk, for every module.
+hipError_t launch_fold_partials(const LayerDesc &d, hipStream_t stream);
 // One launch per phase: blocks [0, decode_blocks) take decode items, the
 // rest SGMV row tiles.
 hipError_t launch_shrink(const LayerDesc &d, int decode_blocks, int grid, hipStream_t stream);

@@ -310,6 +310,28 @@ def test_long_segments_with_short_and_base_rows():
         check_workload(w, oracle_all(w), runner)
 
 
+@pytest.mark.parametrize("runner", sorted(RUNNERS))
+def test_prefill_folded_partials_mixed_chunks(runner):
+    # A prefill-sized batch over projections of 3, 1 and 4 k-chunks (d_in
+    # 4104, 2048, 8192 at the 2048-input chunks of a prefill call): the layer
+    # calls sum each row's partials into its first chunk between the shrink
+    # and the expand, and the one-chunk projection is left as it is.  Ranks
+    # differ per projection and slot (some 0), with long, short and base rows.
+    lens = [900, 1, 3, 640, 1, 7, 12, 520, 2, 1]
+    ids = np.concatenate([np.repeat(np.arange(len(lens)), lens), -np.ones(30, int)])
+    ids = np.random.default_rng(11).permutation(ids).astype(np.int32)
+    shapes = {"q": (4104, 1032), "k": (2048, 520), "o": (8192, 1024)}
+    rng = np.random.default_rng(12)
+    ranks = np.zeros((len(lens), gen.N_MOD), np.int32)
+    for n in shapes:
+        ranks[:, gen.MODULE_INDEX[n]] = rng.choice([0, 8, 16, 40, 64], size=len(lens), p=[0.1, 0.2, 0.2, 0.2, 0.3])
+    w = gen.build_workload("fold_mixed", 400, ids.size, len(lens), shapes, ids, ranks,
+                           x_of={n: "x_" + n for n in shapes}, x_std=1.0)
+    assert w.num_rows >= 2048
+    note(f"folded partials runner={runner} rows={w.num_rows}")
+    check_workload(w, oracle_all(w), runner)
+
+
 def test_prefill_phases_expand_twice():
     # A prefill-sized batch (at least 2048 rows, ragged k-chunks): the layer
     # expand only reads the shrink's k-chunk partials, so a second expand
