@@ -21,7 +21,7 @@ BIG = 1 << 40
 def declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lora_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(lora_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol():

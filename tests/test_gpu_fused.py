@@ -61,6 +61,11 @@ SHAPES = [
     (128, 128, 4096, 1024, 64, "distinct"),
     (129, 40, 1024, 4104, (8, 16, 24), "random"),
     (200, 9, 3080, 520, (64, 1, 40), "random"),
+    # long input ranges (128 or more rounds of 64 inputs; 8200: a ragged last
+    # round), one and three row tiles
+    (64, 64, 8200, 520, (16, 64, 8), "distinct"),
+    (130, 20, 12288, 264, (8, 32, 64), "random"),
+    (257, 30, 8192, 136, (64, 0, 16), "random"),
 ]
 
 
@@ -158,3 +163,55 @@ def test_fused_max_rank_not_a_multiple_of_eight(max_rank):
     w = gen.add_base_weights(bw(440 + max_rank, rows, slots, 1024, 528, None, ids, ranks=ranks, x_std=1.0,
                                 max_rank=max_rank, fmt=fmt))
     check_fused(w)
+
+
+def test_fused_repeated_calls_same_bits():
+    # calls after the first on the same workspace give the same bits, whole or
+    # in two parts, and a second fused part after one shrink part too
+    rng = np.random.default_rng(441)
+    rows, slots = 140, 24
+    ids = rng.integers(-1, slots, size=rows)
+    ranks = np.zeros((slots, 7), np.int32)
+    ranks[:, 0] = rng.choice([0, 8, 32, 64], size=slots)
+    w = gen.add_base_weights(bw(441, rows, slots, 8200, 520, None, ids, ranks=ranks, x_std=1.0, max_rank=64))
+    run = FusedRun(w)
+    first = run.run()["q"]
+    assert np.isfinite(first).all()
+    for _ in range(2):
+        assert np.array_equal(run.run()["q"], first)
+    assert np.array_equal(run.run(phases=True)["q"], first)
+    dw = run.dw
+    args = (dw.lin_ios, w.num_rows, dw.ids, dw.table, w.num_slots, dw.seg, w.max_rank, dw.ws)
+    dw.y["q"].fill_(float("nan"))
+    lg.linear_expand(*args)  # the v planes of the shrink above
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_host(dw.y["q"]), first)
+
+
+def test_fused_long_one_hot_bit_exact():
+    """The one-hot case over 9000 inputs (141 rounds, a ragged last one):
+    every sum has one nonzero term, so y is exact."""
+    rows, slots, d_in, d_out, rank = 130, 20, 9000, 520, 16
+    rng = np.random.default_rng(17)
+    kw = rng.integers(0, d_in, size=d_out)
+    ka = rng.choice(d_in, slots, replace=False)
+    na = rng.choice(d_out, slots, replace=False)
+
+    def fill(w):
+        for a in range(slots):
+            A, B = w.A(a, 0), w.B(a, 0)
+            A[:] = 0
+            B[:] = 0
+            A[0, ka[a]] = 0x3F80
+            B[na[a], 0] = 0x3F80
+    ids = rng.integers(-1, slots, size=rows)
+    w = bw(18, rows, slots, d_in, d_out, rank, ids, ab_fill=fill, x_std=1.0)
+    w.W = {"q": np.zeros((d_out, d_in), np.uint16)}
+    w.W["q"][np.arange(d_out), kw] = 0x3F80
+    x = bf16_to_f32(w.x["x"])
+    want = x[:, kw].copy()
+    r = np.arange(rows)
+    on = ids >= 0
+    want[r[on], na[ids[on]]] += x[r[on], ka[ids[on]]]
+    want = bf16_to_f32(gen.bf16_bits(want)).astype(np.float64)
+    assert np.array_equal(FusedRun(w).run()["q"], want)

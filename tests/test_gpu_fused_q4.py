@@ -58,6 +58,8 @@ SHAPES = [
     (129, 40, 1024, 4104, (8, 16, 24), "random"),    # base-only and out-of-range ids in the batch
     (200, 9, 3072, 520, (64, 1, 40), "random"),
     (16, 4, 128, 8, 8, "random"),                    # one group, one column tile
+    (96, 30, 8320, 264, (8, 64, 0, 32), "random"),   # 65 groups of inputs
+    (140, 140, 12288, 136, 64, "distinct"),          # 96 groups, two row tiles
 ]
 
 
@@ -164,3 +166,15 @@ def test_q4_full_layer_sampled_rows():
     rows[0] = 0  # a base-only row (ids[::16] = -1)
     note(f"q4 fused full layer: rows {list(rows)}")
     check_q4(w, rows=rows, bound_segments=True)
+
+
+def test_q4_repeated_calls_same_bits():
+    # later calls on the same workspace give the same bits
+    ids = np.random.default_rng(14).integers(-1, 20, size=100)
+    w = gen.add_base_weights_q4(bw(531, 100, 20, 8320, 264, 32, ids, x_std=1.0))
+    first, dw = run(w)
+    assert np.isfinite(first["q"]).all()
+    again, _ = run(w, dw=dw)
+    assert np.array_equal(again["q"], first["q"])
+    phases, _ = run(w, dw=dw, phases=True)
+    assert np.array_equal(phases["q"], first["q"])
