@@ -46,7 +46,6 @@ class DeviceWorkload:
         self.seg = lg.Segments(w.num_rows + ws_extra_rows, device, max_segments=bound)
         sum_d_in = sum(m.d_in for m in w.modules)
         self.ws_bytes = lg.workspace_bytes(w.num_rows + ws_extra_rows, w.num_slots, w.max_rank, sum_d_in)
-        # zeroed: the head of a workspace must start at zero (lora_decode_layer's hand-off words)
         self.ws = torch.zeros(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
         self.ios = {m.name: lg.ModuleIO(self.x[m.x_name], self.y[m.name]) for m in w.modules}
         # every targeted entry int8: the layer calls size their items for one-byte factors
