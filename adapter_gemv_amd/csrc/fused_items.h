@@ -8,16 +8,15 @@
 // accumulator, so y is written once instead of written and then updated.
 //
 // A block takes kFusedRows rows (in their original order) and fused_cols
-// output columns of one projection (128 over a bf16 W, 64 over a 4-bit W),
-// over the whole d_in:
+// (128) output columns of one projection, over the whole d_in:
 //   * main loop: x and W stream through LDS in rounds of 64 k, x two rounds
-//     and W three rounds ahead in registers (x rows from L2, W rows from HBM
-//     once, nontemporal, 128-byte line pieces); each wave turns a 64 x 64
-//     (bf16 W: waves 2 x 2 over rows and columns) or 32 x 64 (4-bit W: one
-//     row band per wave) piece into 4 x 4 or 2 x 4 bf16 matrix-core tiles
-//     (16x16x32, fp32 accumulate).  The 128-column tile halves the x bytes
-//     read from L2 per byte of W; its 2 x 2 wave grid reads 8 operand
-//     fragments from LDS per step where 4 row bands of 32 read 10.  Loading
+//     and W three (4-bit W: two) rounds ahead in registers (x rows from L2,
+//     W rows from HBM once, nontemporal, 128-byte line pieces); the waves
+//     form a 2 x 2 grid over rows and columns, and each turns its 64 x 64
+//     piece into 4 x 4 bf16 matrix-core tiles (16x16x32, fp32 accumulate).
+//     The 128-column tile halves the x bytes read from L2 per byte of W; its
+//     2 x 2 wave grid reads 8 operand fragments from LDS per step where 4
+//     row bands of 32 read 10.  Loading
 //     W straight into the matrix-core operand layout (16 rows x 64 bytes per
 //     instruction) with each wave owning 16 or 32 columns measured slower,
 //     and so did one register set for both B formats in the epilogue (a
@@ -96,13 +95,22 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
   const int nseg = min(uniform(*f.num_segments), f.max_seg);
   const int last_slot = nseg > 0 ? uniform(f.seg_adapter[nseg - 1]) : -1;
   // Table entries of this wave's epilogue rows w + 4i, one per lane (i < 32).
-  lora_adapter_entry_t my_e{};
-  bool my_valid = false;
+  // (what the epilogue needs of it: B, rank, scale, format; rank 0 when the
+  // row gets no delta: base only, a slot past the build, a malformed entry)
+  const void *my_B = nullptr;
+  int my_rank = 0, my_fmt = 0;
+  float my_scale = 0.f;
   if (lane < RPW) {
     const int b = row0 + w + 4 * lane;
     const int a = b < f.num_rows ? f.ids[b] : -1;
-    my_valid = (unsigned)a < (unsigned)f.num_slots && a <= last_slot;
-    if (my_valid) my_e = f.table[(int64_t)a * f.table_cols + m.col];
+    if ((unsigned)a < (unsigned)f.num_slots && a <= last_slot) {
+      const lora_adapter_entry_t e = f.table[(int64_t)a * f.table_cols + m.col];
+      const bool ok = entry_ok(e, f.max_rank);  // a malformed entry: counted by the shrink
+      my_B = e.B;
+      my_rank = ok ? e.rank : 0;
+      my_fmt = e.format;
+      my_scale = e.scale;
+    }
   }
 
   const int piece = t & 7;
@@ -114,18 +122,18 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
     xoff[i] = r < f.num_rows ? (uint32_t)((int64_t)r * m.ldx * 2) : kOutOfRange;
   }
   // W of a round: bf16, WL pieces of 8 values per thread (rows 32i + t/8);
-  // 4-bit, one 8-byte piece of 16 values per thread (row t/4, values
-  // 16 (t%4) .. +16 of the round), widened to bf16 on the way into LDS
+  // 4-bit, one 16-byte piece of 32 values per thread (row t/2, values
+  // 32 (t%2) .. +32 of the round), widened to bf16 on the way into LDS
   const int64_t w_row_bytes = Q4 ? m.ldw : m.ldw * 2;
   const rsrc_t rw = make_rsrc(m.W, (uint32_t)((int64_t)m.d_out * w_row_bytes));
   constexpr int WP = Q4 ? 1 : WL;
   uint32_t woff[WP];
 #pragma unroll
   for (int i = 0; i < WP; ++i) {
-    const int n = n0 + (Q4 ? (t >> 2) : i * 32 + (t >> 3));
+    const int n = n0 + (Q4 ? (t >> 1) : i * 32 + (t >> 3));
     woff[i] = n < m.d_out ? (uint32_t)((int64_t)n * w_row_bytes) : kOutOfRange;
   }
-  using WRaw = typename std::conditional<Q4, u32x2, u32x4>::type;
+  using WRaw = u32x4;
   struct XStage {
     u32x4 x[XL];
   };
@@ -144,8 +152,8 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
     const bool kon = k < m.d_in;
     const uint32_t kb = (uint32_t)k * 2;
     if constexpr (Q4) {
-      const int kq = k0 + 16 * (t & 3);
-      st.wv[0] = __builtin_amdgcn_raw_buffer_load_b64(
+      const int kq = k0 + 32 * (t & 1);
+      st.wv[0] = __builtin_amdgcn_raw_buffer_load_b128(
           rw, kq < m.d_in && woff[0] != kOutOfRange ? woff[0] + (uint32_t)kq / 2 : kOutOfRange, 0, kNonTemporal);
     } else {
 #pragma unroll
@@ -157,9 +165,11 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
 #pragma unroll
     for (int i = 0; i < XL; ++i) *(u32x4 *)(buf + shrink_lds_off(i * 32 + (t >> 3), piece)) = xs.x[i];
     if constexpr (Q4) {
-      const int row = t >> 2, p0 = 2 * (t & 3);
+      const int row = t >> 1, p0 = 4 * (t & 1);
       *(u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(row, p0)) = q4x8_to_bf16x8(ws.wv[0].x);
       *(u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(row, p0 + 1)) = q4x8_to_bf16x8(ws.wv[0].y);
+      *(u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(row, p0 + 2)) = q4x8_to_bf16x8(ws.wv[0].z);
+      *(u32x4 *)(buf + kShrinkXBytes + shrink_lds_off(row, p0 + 3)) = q4x8_to_bf16x8(ws.wv[0].w);
     } else {
 #pragma unroll
       for (int i = 0; i < WL; ++i)
@@ -189,6 +199,7 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xo[mt]),
                                                                 __builtin_bit_cast(bf16x8_t, wo[nt]), acc[mt][nt], 0,
                                                                 0, 0);
+      if constexpr (Q4) __builtin_amdgcn_sched_barrier(0);  // one k-step's operands live at a time
     }
   };
   // 4-bit: the two rounds of a main-loop step are one group of kQ4Group
@@ -196,7 +207,7 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
   // output column (this lane's columns n0 + 16 nt + r_in), requested one
   // step ahead
   static_assert(2 * kShrinkRound == kQ4Group, "one group per main-loop step");
-  static_assert(!Q4 || (MT == 2 && NC == 64), "4-bit blocks take 64 columns, one row band per wave");
+
   f32x4_t gacc[Q4 ? MT : 1][Q4 ? 4 : 1];
   float sc_cur[4] = {0.f, 0.f, 0.f, 0.f}, sc_nxt[4] = {0.f, 0.f, 0.f, 0.f};
   const rsrc_t rs_w = make_rsrc(Q4 ? m.Ws : nullptr, Q4 ? (uint32_t)((int64_t)m.d_out * m.ldws * 4) : 0u);
@@ -221,7 +232,7 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
   load_w(w0, 0);
   load_w(w1, kShrinkRound);
   load_x(x1, kShrinkRound);
-  load_w(w2, 2 * kShrinkRound);
+  if constexpr (!Q4) load_w(w2, 2 * kShrinkRound);  // 4-bit W: two rounds ahead (its registers are few, its rounds short)
   const int rounds = (m.d_in + kShrinkRound - 1) / kShrinkRound;
   uint8_t *b0 = lds, *b1 = lds + fused_buf_bytes(Q4);
   auto step = [&](int r, auto odd, XStage &xs, WStage &ws, uint8_t *buf) {
@@ -235,7 +246,7 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
     }
     store(xs, ws, buf);
     load_x(xs, (r + 2) * kShrinkRound);
-    load_w(ws, (r + 3) * kShrinkRound);
+    load_w(ws, (r + (Q4 ? 2 : 3)) * kShrinkRound);
     __syncthreads();
     if constexpr (Q4) {
       compute(buf, gacc);
@@ -261,10 +272,10 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
   for (int r = 0; r < rounds; r += 6) {
     step(r, Even{}, x0, w0, b0);
     step(r + 1, Odd{}, x1, w1, b1);
-    step(r + 2, Even{}, x0, w2, b0);
-    step(r + 3, Odd{}, x1, w0, b1);
-    step(r + 4, Even{}, x0, w1, b0);
-    step(r + 5, Odd{}, x1, w2, b1);
+    step(r + 2, Even{}, x0, Q4 ? w0 : w2, b0);
+    step(r + 3, Odd{}, x1, Q4 ? w1 : w0, b1);
+    step(r + 4, Even{}, x0, Q4 ? w0 : w1, b0);
+    step(r + 5, Odd{}, x1, Q4 ? w1 : w2, b1);
   }
   __syncthreads();  // every wave is done with the round buffers
 
@@ -296,26 +307,17 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
   auto row_info = [&](int i) {  // uniform: the entry held by lane i
     RowInfo ri;
     ri.b = row0 + w + 4 * i;
-    const bool valid = __builtin_amdgcn_readlane((int)my_valid, i) != 0;
-    lora_adapter_entry_t e;
-    e.A = (const void *)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
-                                         (int)(uint32_t)(uintptr_t)my_e.A, i)) |
-                                    ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
-                                         (int)(uint32_t)((uintptr_t)my_e.A >> 32), i)
-                                     << 32));
-    e.B = (const void *)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
-                                         (int)(uint32_t)(uintptr_t)my_e.B, i)) |
-                                    ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
-                                         (int)(uint32_t)((uintptr_t)my_e.B >> 32), i)
-                                     << 32));
-    e.rank = __builtin_amdgcn_readlane(my_e.rank, i);
-    e.scale = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_e.scale), i));
-    e.format = __builtin_amdgcn_readlane(my_e.format, i);
-    ri.ok = valid && ri.b < f.num_rows && entry_ok(e, f.max_rank);  // a malformed entry: counted by the shrink
-    ri.rank = e.rank;
-    ri.fmt = e.format;
-    ri.scale = e.scale;
-    ri.B = static_cast<const uint8_t *>(e.B);
+    const int rank = __builtin_amdgcn_readlane(my_rank, i);
+    const void *B = (const void *)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                                                   (int)(uint32_t)(uintptr_t)my_B, i)) |
+                                              ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                                                   (int)(uint32_t)((uintptr_t)my_B >> 32), i)
+                                               << 32));
+    ri.ok = rank > 0 && ri.b < f.num_rows;
+    ri.rank = rank;
+    ri.fmt = __builtin_amdgcn_readlane(my_fmt, i);
+    ri.scale = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_scale), i));
+    ri.B = static_cast<const uint8_t *>(B);
     return ri;
   };
   auto issue = [&](const RowInfo &ri, FusedRowLoads &L) {

@@ -100,10 +100,10 @@ struct LayerDesc {
 // Fused base projection + delta: a block computes y for kFusedRows rows and
 // fused_cols(q4) output columns of one projection.
 constexpr int kFusedRows = 128;
-// Output columns of a block: 128 with a bf16 base (half the x read from L2
-// per byte of W), 64 with a 4-bit base (its group sums double the
-// accumulators).
-constexpr int fused_cols(bool q4) { return q4 ? 64 : 128; }
+// Output columns of a block, with either base: 128 (against 64, half the x
+// read from L2 per byte of W; the 4-bit kernel holds its group sums beside
+// the accumulators at the cost of a few spilled registers).
+constexpr int fused_cols(bool) { return 128; }
 
 // 4-bit base weights: inputs per scale (a group of consecutive inputs of one
 // output row); the fused kernel's two 64-k rounds per main-loop step make one.
