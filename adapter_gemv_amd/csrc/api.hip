@@ -380,10 +380,16 @@ namespace {
 // same 268 MB with 256 rows.  Batches of at most kOnePassMaxRows rows, ranks
 // up to 32.  False for any other batch.
 constexpr double kOnePassRepeatBytes = 320.0 * (1 << 20);
-// The grid keeps this many blocks as tiles per block grow (measured: 128
-// rows x 8192 at rank 16 takes 17.1 us with one tile per block (513
-// blocks), 17.2 with two, 20.7 with four).
-constexpr int64_t kOnePassMinBlocks = 512;
+// Tiles per block grow while the blocks that work (one per row group and
+// item) stay at least this many and the widest projection keeps at least
+// two blocks per row group: every block of a group reads its A, so fewer
+// blocks read A fewer times, until too few blocks share a row's tiles.
+// Measured (graph-timed, a distinct adapter per row, 8192 x 8192): rank 32
+// at 128 rows 39.5 us with 4 blocks per row, 32.0 with 2; rank 16 at 128
+// rows 19.6 with 4, 19.1 with 2, 23.6 with 1 (bench); 256 rows of rank 16 at
+// 4096 x 4096 14.9 with 2, 15.7 with 1; 128 rows over 32 adapters at rank 16
+// 20.7 with 4 (128 working blocks), 24.7 with 2.
+constexpr int64_t kOnePassMinWorking = 256;
 
 bool onepass_plan(const ModuleArgs *ms, int n, int num_rows, const int32_t *ids, int num_slots, int max_rank,
                   const lora_adapter_entry_t *table, const lora_segments_t &seg, OnePassDesc *od, int *grid) {
@@ -395,15 +401,24 @@ bool onepass_plan(const ModuleArgs *ms, int n, int num_rows, const int32_t *ids,
   const bool bound_check = max_seg < (num_rows < num_slots ? num_rows : num_slots);
   if (bound_check && num_slots > kOnePassMaxSlots) return false;
   const double passes = max_seg + (num_rows - max_seg + 3) / 4;
-  // tiles per block: doubled while the grid keeps kOnePassMinBlocks blocks
-  // (each block reads its segment's A once for all its tiles)
+  // tiles per block (each block reads its segment's A once for all its tiles)
   auto items = [&](int tpb) {
     int64_t it = 0;
     for (int i = 0; i < n; ++i) it += ((ms[i].d_out + nt - 1) / nt + tpb - 1) / tpb;
     return it;
   };
+  auto widest = [&](int tpb) {  // items of the projection with the most tiles
+    int64_t w = 0;
+    for (int i = 0; i < n; ++i) {
+      const int64_t it = ((ms[i].d_out + nt - 1) / nt + tpb - 1) / tpb;
+      w = it > w ? it : w;
+    }
+    return w;
+  };
   int tpb = 1;
-  while (tpb < 64 && items(2 * tpb) < items(tpb) && items(2 * tpb) * num_rows >= kOnePassMinBlocks) tpb *= 2;
+  while (tpb < 64 && items(2 * tpb) < items(tpb) && widest(2 * tpb) >= 2 &&
+         items(2 * tpb) * passes >= kOnePassMinWorking)
+    tpb *= 2;
   double repeat = 0;
   for (int i = 0; i < n; ++i)
     repeat += (double)(((ms[i].d_out + nt - 1) / nt + tpb - 1) / tpb) * ms[i].d_in * (8 * lpr) * 2 * passes;
