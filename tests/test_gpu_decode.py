@@ -357,12 +357,15 @@ def test_prefill_phases_expand_twice():
     check_rows(bf16_host(dw.y["q"]), ref["q"].delta, "prefill phases delta")
 
 
+@pytest.mark.parametrize("d_out", [2 * 2048 + 8, 3 * 512 + 8, 5 * 512 + 24])
 @pytest.mark.parametrize("fmt", ["bf16", "int8", "mixed"])
-def test_entry_lane_width_in_rank64_launch(fmt):
+def test_entry_lane_width_in_rank64_launch(fmt, d_out):
     # One row per adapter, entries of many ranks in one launch of rank class
     # 64: each expand item runs at the lane width of its own entry's rank
     # (1, 2, 4 or 8 lanes per output row, fewer load passes at width 1), over
-    # whole and ragged n-tiles (d_out = 2 * 2048 + 8).
+    # whole and ragged n-tiles.  17 segments take 512-output tiles (the
+    # smallest), narrower than a low-rank entry's sub-tile, so most of such an
+    # item's load passes fall past its tile and read zero.
     ranks_ = np.array([1, 3, 8, 9, 13, 16, 17, 24, 32, 33, 40, 57, 64, 8, 16, 32, 64], np.int32)
     slots = ranks_.size
     ids = np.random.default_rng(11).permutation(slots).astype(np.int32)
@@ -375,7 +378,7 @@ def test_entry_lane_width_in_rank64_launch(fmt):
     else:
         code = np.where(np.arange(slots)[:, None] % 2 == 0, gen.FMT_INT8_ROWS, gen.FMT_BF16) * np.ones((1, 7), int)
         code = code.astype(np.int32)
-    w = bw(400, slots, slots, 2056, 2 * 2048 + 8, None, ids, ranks=ranks, x_std=1.0, max_rank=64, fmt=code)
+    w = bw(400, slots, slots, 2056, d_out, None, ids, ranks=ranks, x_std=1.0, max_rank=64, fmt=code)
     assert w.max_rank == 64
     for runner in ("layer", "split"):
         check_workload(w, oracle_all(w), runner)
