@@ -10,7 +10,7 @@
 // A block takes kFusedRows rows (in their original order) and fused_cols
 // (128) output columns of one projection, over the whole d_in:
 //   * main loop: x and W stream through LDS in rounds of 64 k, x two rounds
-//     and W three (4-bit W: two) rounds ahead in registers (x rows from L2,
+//     and W four (4-bit W: two) rounds ahead in registers (x rows from L2,
 //     W rows from HBM once, nontemporal, 128-byte line pieces); the waves
 //     form a 2 x 2 grid over rows and columns, and each turns its 64 x 64
 //     piece into 4 x 4 bf16 matrix-core tiles (16x16x32, fp32 accumulate).
@@ -223,16 +223,19 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
     }
   };
   if constexpr (Q4) load_scales(sc_cur, 0);
-  // x (mostly from L2) two rounds ahead, W (from HBM) three: round r goes
+  // x (mostly from L2) two rounds ahead, W (from HBM) four: round r goes
   // to LDS buffer r & 1 once its loads are in, and then x of round r + 2 and
-  // W of round r + 3 are requested into the registers it leaves.
+  // W of round r + 4 are requested into the registers it leaves.
   XStage x0, x1;
-  WStage w0, w1, w2;
+  WStage w0, w1, w2, w3;
   load_x(x0, 0);
   load_w(w0, 0);
   load_w(w1, kShrinkRound);
   load_x(x1, kShrinkRound);
-  if constexpr (!Q4) load_w(w2, 2 * kShrinkRound);  // 4-bit W: two rounds ahead (its registers are few, its rounds short)
+  if constexpr (!Q4) {  // 4-bit W: two rounds ahead (its registers are few, its rounds short)
+    load_w(w2, 2 * kShrinkRound);
+    load_w(w3, 3 * kShrinkRound);
+  }
   const int rounds = (m.d_in + kShrinkRound - 1) / kShrinkRound;
   uint8_t *b0 = lds, *b1 = lds + fused_buf_bytes(Q4);
   auto step = [&](int r, auto odd, XStage &xs, WStage &ws, uint8_t *buf) {
@@ -246,7 +249,7 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
     }
     store(xs, ws, buf);
     load_x(xs, (r + 2) * kShrinkRound);
-    load_w(ws, (r + (Q4 ? 2 : 3)) * kShrinkRound);
+    load_w(ws, (r + (Q4 ? 2 : 4)) * kShrinkRound);
     __syncthreads();
     if constexpr (Q4) {
       compute(buf, gacc);
@@ -266,16 +269,16 @@ __device__ __forceinline__ void fused_block(const FusedDesc &f, int blk, uint8_t
   };
   using Even = std::false_type;
   using Odd = std::true_type;
-  // Six rounds per pass (one per pairing of the x and W registers); rounds
+  // Four rounds per pass (one per pairing of the x and W registers); rounds
   // past d_in read zeros and add nothing.  (An exit between the rounds of a
-  // pass makes the compiler spill.)
-  for (int r = 0; r < rounds; r += 6) {
+  // pass makes the compiler spill.  The 4-bit kernel, whose W registers
+  // alternate, runs the same four-round pass: in the six-round pass that W
+  // three rounds ahead needed, it spilled 17 registers.)
+  for (int r = 0; r < rounds; r += 4) {
     step(r, Even{}, x0, w0, b0);
     step(r + 1, Odd{}, x1, w1, b1);
     step(r + 2, Even{}, x0, Q4 ? w0 : w2, b0);
-    step(r + 3, Odd{}, x1, Q4 ? w1 : w0, b1);
-    step(r + 4, Even{}, x0, Q4 ? w0 : w1, b0);
-    step(r + 5, Odd{}, x1, Q4 ? w1 : w2, b1);
+    step(r + 3, Odd{}, x1, Q4 ? w1 : w3, b1);
   }
   __syncthreads();  // every wave is done with the round buffers
 
