@@ -61,6 +61,10 @@ SHAPES = [
     (128, 128, 4096, 1024, 64, "distinct"),
     (129, 40, 1024, 4104, (8, 16, 24), "random"),
     (200, 9, 3080, 520, (64, 1, 40), "random"),
+    # short input ranges: fewer rounds of 64 inputs than a pass of the main
+    # loop (72: one whole round and a ragged one; 264: five, the last ragged)
+    (5, 5, 72, 136, 8, "distinct"),
+    (33, 10, 264, 264, (16, 64), "random"),
     # long input ranges (128 or more rounds of 64 inputs; 8200: a ragged last
     # round), one and three row tiles
     (64, 64, 8200, 520, (16, 64, 8), "distinct"),
