@@ -90,7 +90,13 @@ def run_phases(dw):
     lg.layer_expand(dw.ios, w.num_rows, dw.table, w.num_slots, dw.seg, w.max_rank, dw.ws)
 
 
-RUNNERS = {"split": run_split, "layer": run_layer, "phases": run_phases}
+def run_decode(dw):
+    """lora_decode_layer: the segments and every projection, in one launch
+    where the batch fits it, else in the three launches."""
+    dw.decode_layer()
+
+
+RUNNERS = {"split": run_split, "layer": run_layer, "phases": run_phases, "decode": run_decode}
 
 
 def check_workload(w, ref, runner="layer", check_v=True, rows=None):

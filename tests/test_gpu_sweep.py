@@ -25,6 +25,7 @@ if not torch.cuda.is_available():  # pragma: no cover
     pytest.skip("no GPU", allow_module_level=True)
 
 from tests.test_gpu_decode import check_workload  # noqa: E402
+from workloads.device import DeviceWorkload  # noqa: E402
 
 RANK_CHOICES = np.array([0, 1, 3, 8, 13, 16, 24, 32, 40, 57, 64])
 
@@ -66,6 +67,21 @@ def test_random_layer_case(seed):
     note(f"sweep seed {seed}: {w.num_rows} rows, {w.num_slots} slots, "
          f"{[(m.name, m.d_in, m.d_out) for m in w.modules]}, max_rank {w.max_rank}, runner {runner}")
     check_workload(w, oracle.lora_layer(w), runner)
+
+
+@pytest.mark.parametrize("int8", [False, True])
+@pytest.mark.parametrize("seed", range(14))
+def test_random_decode_layer_case(seed, int8):
+    # the same batches through lora_decode_layer: one launch where the batch
+    # fits it (at most 256 rows, launch rank class at most 32), the three
+    # launches otherwise; both kinds occur among the seeds
+    w = random_case(seed if not int8 else 300 + seed, int8=int8)
+    dw = DeviceWorkload(w)
+    launches = dw.decode_launches()
+    note(f"sweep decode seed {seed} int8 {int8}: {w.num_rows} rows, {w.num_slots} slots, "
+         f"{[(m.name, m.d_in, m.d_out) for m in w.modules]}, max_rank {w.max_rank}, launches {launches}")
+    assert launches in (1, 3)
+    check_workload(w, oracle.lora_layer(w), "decode")
 
 
 @pytest.mark.parametrize("seed", range(2))
