@@ -87,16 +87,17 @@ lora_status_t launched(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_E
 
 // Shrink k-chunk.  Prefill-sized batches: 2 * kKChunkMin (fewer partials to
 // write and sum).  Decode batches: about 128 KiB of A per item at the
-// launch's rank class (1024 k at rank 64, longer below; twice the k when the
-// caller states int8 factors, LORA_MASK_INT8_ITEMS), halved while the batch
-// would give fewer than 512 items, never below kKChunkMin (the workspace is
-// sized for that chunk).  Measured on the 70B layer at rank 64 with int8
-// factors: shrink 137 -> 109 us with 2048 k instead of 1024 (and bf16
-// factors 186 -> 196 us: the hint is the caller's).
+// launch's rank class (1024 k at rank 64, longer below; four times the k,
+// at most 4 * kKChunkMin, when the caller states int8 factors,
+// LORA_MASK_INT8_ITEMS), halved while the batch would give fewer than 512
+// items, never below kKChunkMin (the workspace is sized for that chunk).
+// Measured on the 70B layer at rank 64 with int8 factors: shrink 137 -> 109
+// us with 2048 k instead of 1024, and 106 -> 102 us with 4096 (and bf16
+// factors 186 -> 196 us at 2048: the hint is the caller's).
 int pick_kc(int num_rows, int max_rank, int64_t max_seg, const ModuleArgs *ms, int n) {
   if (num_rows >= kPrefillRows) return 2 * kKChunkMin;
   const int cls = max_rank <= 8 ? 8 : max_rank <= 16 ? 16 : max_rank <= 32 ? 32 : 64;
-  int kc = kKChunkMin * (64 / cls) * (n > 0 && ms[0].int8_items ? 2 : 1);
+  int kc = kKChunkMin * (64 / cls) * (n > 0 && ms[0].int8_items ? 4 : 1);
   if (kc > 4 * kKChunkMin) kc = 4 * kKChunkMin;
   while (kc > kKChunkMin) {
     int64_t items = 0;

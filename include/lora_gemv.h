@@ -83,8 +83,8 @@ extern "C" {
  * lora_apply_layer_noalloc, lora_apply_layer_stacked, lora_linear_layer and
  * its parts and their _q4 forms) accept in module_mask beside the module
  * bits: the caller's table entries are int8 (LORA_FORMAT_INT8_ROWS), so the
- * shrink's work items take twice the k of a bf16 item (as many bytes per
- * item).  Results are the same within the tolerance with or without it and
+ * shrink's work items take more k than a bf16 item (four times, up to 4096
+ * inputs: at least as many bytes per item).  Results are the same within the tolerance with or without it and
  * for entries of either format; pass the same flag to both parts of a split
  * call.  Source: "m07 -- Multi-Adapter (LoRA) Serving", "9. Bottlenecks and
  * Evolution", item 3 (int8 adapters halve the bytes). */
